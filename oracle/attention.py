@@ -1,0 +1,235 @@
+"""Plain, slow, fp64 reference for paged decode attention and its split-KV algebra.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+reaches this module.
+
+What it computes, and where the pages fix it
+--------------------------------------------
+* Decode attention for one new token per request: every query head h attends,
+  with a dense softmax, over the keys of its KV group at the visible positions.
+  The paged layout only changes *where* a row lives: logical position j of
+  request r is slot j % page_size of physical page table[r][j // page_size]
+  (TensorFold PR #1619, body: "page p is rows [256p, 256(p+1))"; the table maps a
+  stream's logical pages to leased pool pages).
+* GQA: eight query heads share one KV head (gem design note, "Fixed production
+  shape").  Reading taken: head h uses KV head h // (Hq / Hkv), the consecutive
+  grouping.
+* Rows: the split row is K | V; the folded row keeps only the rotated K columns
+  and all of V, and the unrotated part of the score is taken against V with the
+  norm weight folded into the query (pegainfer PR #1055, Description).
+* Windowed decode (sliding layers): the resident pages may hold one page more
+  than the window and those older keys are masked (pegainfer PR #1057,
+  Description).  Reading taken: position j is visible iff L - W <= j < L.
+* Split-KV: each key chunk yields an online-softmax partial (running max M, sum
+  S, unnormalised numerator O); partials merge with the exact rescaling identity
+  M = max(Ma, Mb), S = Sa e^(Ma-M) + Sb e^(Mb-M), O likewise, then O / S; empty
+  partitions are valid states, and invalid finite states fail closed (gem design
+  note, opening status paragraph and "Candidate ownership and storage").  The
+  merge runs in two levels: groups of consecutive chunk partials first, then the
+  group states (pegainfer PR #1055, Description).
+
+All arithmetic is float64.  bf16 inputs widen exactly; fp32 queries widen
+exactly.  Library primitives used as steps: numpy's matmul, exp, max and sum.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Sequence
+
+import numpy as np
+
+__all__ = [
+    "InvalidState", "State", "bf16_bits_to_f64", "visible_range", "row_view", "gather_rows",
+    "keys_values", "dense_attention", "decode_attention", "partial_state", "empty_state",
+    "merge", "finalize", "split_kv_attention", "paged_partials", "validate",
+]
+
+
+class InvalidState(ValueError):
+    """A split-KV state that cannot arise from any set of finite keys."""
+
+
+# --------------------------------------------------------------------------------------
+# data access
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the upper half of an IEEE binary32, so widening is exact."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def visible_range(L: int, window: int) -> tuple[int, int]:
+    """Positions [lo, L) that a decode token at context length L attends to."""
+    if L < 1:
+        raise ValueError("a decode step needs at least one key")
+    lo = max(0, L - window) if window > 0 else 0
+    return lo, L
+
+
+def row_view(wl) -> np.ndarray:
+    """The pool seen as rows[page][kv_head][slot][col] through the layout strides."""
+    itemsize = wl.pool.dtype.itemsize
+    return np.lib.stride_tricks.as_strided(
+        wl.pool,
+        shape=(wl.num_pages, wl.num_kv_heads, wl.page_size, wl.row_cols),
+        strides=(wl.page_stride * itemsize, wl.head_stride * itemsize,
+                 wl.row_stride * itemsize, itemsize),
+        writeable=False)
+
+
+def gather_rows(wl, r: int, g: int, positions: np.ndarray) -> np.ndarray:
+    """bf16 bits of the stored rows of KV head g at logical positions of request r."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = wl.table[r][positions // wl.page_size].astype(np.int64)
+    if positions.size and (pages.min() < 0 or pages.max() >= wl.num_pages):
+        raise IndexError("page table points outside the pool")
+    slots = positions % wl.page_size
+    return row_view(wl)[pages, g, slots]
+
+
+def keys_values(wl, rows_f64: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Split a stored row into the vectors the score and the output use.
+
+    split : k = row[k_off : k_off+D],  v = row[v_off : v_off+D]
+    folded: the score is q'[0:rot].row[k_off : k_off+rot] + q'[rot:D].v[rot:D],
+            so the effective key is (row[k_off : k_off+rot], v[rot:D]).
+    """
+    D = wl.head_dim
+    V = rows_f64[:, wl.v_offset:wl.v_offset + D]
+    if wl.fmt == "split":
+        K = rows_f64[:, wl.k_offset:wl.k_offset + D]
+    else:
+        rot = wl.rot_cols
+        K = np.concatenate([rows_f64[:, wl.k_offset:wl.k_offset + rot], V[:, rot:]], axis=1)
+    return K, V
+
+
+# --------------------------------------------------------------------------------------
+# dense definition
+
+def dense_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * q K^T) V for query rows q[H][D] over keys K[n][D], values V[n][Dv].
+
+    Materialise every score, subtract the row maximum, exponentiate, normalise.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    s = scale * (q @ K.T)                      # [H][n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e @ V) / z
+
+
+def decode_attention(wl) -> np.ndarray:
+    """fp64 output [B][Hq][D] of one decode step over the paged pool."""
+    G = wl.num_q_heads // wl.num_kv_heads
+    out = np.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=np.float64)
+    for r in range(wl.batch):
+        lo, L = visible_range(int(wl.seq_lens[r]), wl.window)
+        pos = np.arange(lo, L)
+        for g in range(wl.num_kv_heads):
+            K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
+            heads = slice(g * G, (g + 1) * G)
+            out[r, heads] = dense_attention(wl.q[r, heads], K, V, wl.scale)
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# split-KV algebra
+
+@dataclasses.dataclass
+class State:
+    """Online-softmax state of a set of keys for one query head (natural-log units).
+
+    m = max score, l = sum of e^(s - m), acc = sum of e^(s - m) v.
+    The empty set is (-inf, 0, 0).
+    """
+    m: float
+    l: float
+    acc: np.ndarray
+
+
+def empty_state(dv: int) -> State:
+    return State(-math.inf, 0.0, np.zeros(dv, dtype=np.float64))
+
+
+def validate(st: State) -> None:
+    """Fail closed on states no finite key set produces."""
+    if math.isnan(st.m) or st.m == math.inf:
+        raise InvalidState("maximum is NaN or +inf")
+    if not np.all(np.isfinite(st.acc)) or not math.isfinite(st.l):
+        raise InvalidState("non-finite sum or numerator")
+    if st.m == -math.inf:
+        if st.l != 0.0 or np.any(st.acc != 0.0):
+            raise InvalidState("empty state with a non-zero sum or numerator")
+    elif st.l < 1.0:
+        # the maximal key contributes e^0 = 1 to a non-empty state's sum
+        raise InvalidState("non-empty state with sum below one")
+
+
+def partial_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> State:
+    """State of one query vector q[D] over the keys K[n][D] / values V[n][Dv]."""
+    if K.shape[0] == 0:
+        return empty_state(V.shape[1])
+    s = scale * (K @ np.asarray(q, dtype=np.float64))
+    m = float(s.max())
+    e = np.exp(s - m)
+    return State(m, float(e.sum()), e @ V)
+
+
+def merge(a: State, b: State) -> State:
+    """Exact rescaling merge of two states; an empty side leaves the other unchanged."""
+    validate(a)
+    validate(b)
+    M = max(a.m, b.m)
+    if M == -math.inf:
+        return empty_state(a.acc.shape[0])
+    alpha = 0.0 if a.m == -math.inf else math.exp(a.m - M)
+    beta = 0.0 if b.m == -math.inf else math.exp(b.m - M)
+    return State(M, alpha * a.l + beta * b.l, alpha * a.acc + beta * b.acc)
+
+
+def finalize(st: State) -> np.ndarray:
+    validate(st)
+    if st.l == 0.0:
+        raise InvalidState("finalize of an empty state (no keys)")
+    return st.acc / st.l
+
+
+def fold(states: Sequence[State]) -> State:
+    """Left-to-right merge of consecutive states."""
+    acc = states[0]
+    validate(acc)
+    for st in states[1:]:
+        acc = merge(acc, st)
+    return acc
+
+
+def split_kv_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                       cuts: Sequence[int], group: int) -> np.ndarray:
+    """Attention of q[D] through chunk partials merged in two levels.
+
+    ``cuts`` are chunk boundaries 0 = c0 <= c1 <= ... <= cn = n (equal cuts give
+    empty chunks); level one folds each run of ``group`` consecutive chunk
+    states, level two folds the group states, then O / S.
+    """
+    parts = [partial_state(q, K[a:b], V[a:b], scale) for a, b in zip(cuts[:-1], cuts[1:])]
+    groups = [fold(parts[i:i + group]) for i in range(0, len(parts), group)]
+    return finalize(fold(groups))
+
+
+def paged_partials(wl, r: int, g: int, ranges: Sequence[tuple[int, int]]) -> list[list[State]]:
+    """Per-chunk states for the G query heads of KV head g of request r.
+
+    ``ranges`` are position intervals [a, b); positions outside the visible
+    range are dropped.  Returns states[h_in_group][chunk].
+    """
+    G = wl.num_q_heads // wl.num_kv_heads
+    lo, L = visible_range(int(wl.seq_lens[r]), wl.window)
+    out = [[] for _ in range(G)]
+    for a, b in ranges:
+        pos = np.arange(max(a, lo), min(b, L))
+        K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
+        for i in range(G):
+            out[i].append(partial_state(wl.q[r, g * G + i], K, V, wl.scale))
+    return out

@@ -1,0 +1,270 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only *builds data*: query vectors, bf16 K/V rows scattered into a
+paged pool through a shuffled page table, and the per-request lengths.  It holds
+none of the attention arithmetic, so both the fp64 oracle (``oracle/``) and the
+GPU path can consume the same bits without sharing any of the method's code.
+
+Shapes and distributions follow the workloads on the pages:
+
+* global layers of Gemma 4 31B: 32 query heads, 4 KV heads (eight query heads
+  per KV head), head dim 512, pages of 256 positions, one decode token
+  (pegainfer PR #1055, Description and Verification; TensorFold PR #1619, body);
+* the split row is K[0:512] | V[0:512] (1024 bf16 columns); the folded row is
+  the 128 rotated K columns followed by all of V (640 columns), with K's norm
+  weight folded into the query at prep time (pegainfer PR #1055, Description);
+* sliding layers: head dim 256, window 1024, pages of 64 (pegainfer PR #1057,
+  Description).
+
+q, K and V are N(0, 1); q stays fp32, K/V are rounded to bf16 with
+round-to-nearest-even.  Random numbers come from a seeded torch CPU generator
+(Mersenne Twister stream, deterministic for a given seed on any host).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+SPLIT = "split"
+FOLDED = "folded"
+
+HEAD_MAJOR = "head_major"    # pool[page][kv_head][slot][cols]
+TOKEN_MAJOR = "token_major"  # pool[page][slot][kv_head][cols]
+
+# bf16 bit patterns used to make unused slots hostile.
+BF16_QNAN = 0x7FC0
+BF16_BIG = 0x7149          # about 1e30
+PADS = {"nan": BF16_QNAN, "big": BF16_BIG, "zero": 0x0000}
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode step's inputs.  All arrays live on the host."""
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    fmt: str                 # SPLIT or FOLDED
+    rot_cols: int            # folded: stored rotated K columns (128); split: 0
+    page_size: int
+    max_pages: int           # page-table row length
+    window: int              # 0 = whole context
+    scale: float
+    layout: str
+    num_pages: int
+    row_cols: int            # bf16 columns per stored row
+    page_stride: int         # elements between pages
+    head_stride: int         # elements between KV heads inside a page
+    row_stride: int          # elements between consecutive slots
+    k_offset: int            # column where the K part starts
+    v_offset: int            # column where V starts
+    q: np.ndarray            # float32 [B][Hq][D]  (folded: the folded query)
+    pool: np.ndarray         # uint16 bf16 bits, flat, num_pages * page_stride
+    table: np.ndarray        # int32 [B][max_pages], -1 where no page
+    seq_lens: np.ndarray     # int32 [B]
+    fold_w: Optional[np.ndarray] = None   # float32 [D - rot_cols] (folded pair only)
+    q_unfolded: Optional[np.ndarray] = None
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def visible(self, r: int) -> tuple[int, int]:
+        """[lo, hi) of the key positions request r attends to (data layout helper)."""
+        L = int(self.seq_lens[r])
+        lo = max(0, L - self.window) if self.window > 0 else 0
+        return lo, L
+
+    def kv_bytes(self) -> int:
+        """Bytes of K/V rows a decode step must stream (visible keys only)."""
+        n = sum(self.visible(r)[1] - self.visible(r)[0] for r in range(self.batch))
+        return n * self.num_kv_heads * self.row_cols * 2
+
+
+def _gen(seed: int) -> torch.Generator:
+    return torch.Generator().manual_seed(int(seed))
+
+
+def _normal_bf16(gen: torch.Generator, shape) -> np.ndarray:
+    """N(0,1) fp32 rounded to bf16 (RNE), returned as uint16 bit patterns."""
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (RNE) and return the bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _strides(layout: str, num_kv_heads: int, page_size: int, row_cols: int):
+    if layout == HEAD_MAJOR:
+        row_stride = row_cols
+        head_stride = page_size * row_cols
+    elif layout == TOKEN_MAJOR:
+        head_stride = row_cols
+        row_stride = num_kv_heads * row_cols
+    else:
+        raise ValueError(layout)
+    page_stride = num_kv_heads * page_size * row_cols
+    return page_stride, head_stride, row_stride
+
+
+def resident_pages(L: int, page_size: int, window: int, extra_page: bool) -> tuple[int, int]:
+    """Logical pages [p0, p1) a request keeps resident.
+
+    Whole context: every page up to the one holding position L-1.  Windowed:
+    the pages overlapping [L-window, L), plus, when ``extra_page`` is set and
+    one exists, the page before them (the resident pages may hold up to one
+    page more than the window; pegainfer PR #1057, Description).
+    """
+    p1 = (L + page_size - 1) // page_size
+    if window <= 0:
+        return 0, p1
+    lo = max(0, L - window)
+    p0 = lo // page_size
+    if extra_page and p0 > 0:
+        p0 -= 1
+    return p0, p1
+
+
+def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: int,
+                  head_dim: int, page_size: int, window: int = 0, fmt: str = SPLIT,
+                  rot_cols: int = 128, seed: int = 0, table_seed: Optional[int] = None,
+                  layout: str = HEAD_MAJOR, spare_pages: int = 4, pad: str = "nan",
+                  max_pages: Optional[int] = None, extra_page: bool = True,
+                  scale: Optional[float] = None) -> Workload:
+    """Build a decode-step workload.
+
+    Data is drawn per (request, logical page) in ascending order from ``seed``;
+    physical placement comes from a permutation drawn from ``table_seed``
+    (default ``seed + 1000``), so two workloads that differ only in
+    ``table_seed`` hold the same logical rows at different physical pages.
+    Slots outside a request's visible keys and unused pages hold ``pad``.
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    D = head_dim
+    if fmt == SPLIT:
+        row_cols, k_off, v_off, rot = 2 * D, 0, D, 0
+    elif fmt == FOLDED:
+        row_cols, k_off, v_off, rot = rot_cols + D, 0, rot_cols, rot_cols
+    else:
+        raise ValueError(fmt)
+    if max_pages is None:
+        max_pages = max((L + page_size - 1) // page_size for L in seq_lens)
+    spans = [resident_pages(L, page_size, window, extra_page) for L in seq_lens]
+    needed = sum(p1 - p0 for p0, p1 in spans)
+    num_pages = needed + spare_pages
+    page_stride, head_stride, row_stride = _strides(layout, num_kv_heads, page_size, row_cols)
+
+    gen = _gen(seed)
+    tgen = _gen(seed + 1000 if table_seed is None else table_seed)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    q = torch.randn(B, num_q_heads, D, generator=gen, dtype=torch.float32).numpy()
+    fold_w = None
+    q_unfolded = None
+    if fmt == FOLDED:
+        fold_w = (torch.rand(D - rot, generator=gen, dtype=torch.float32) + 0.5).numpy()
+        q_unfolded = q.copy()
+        q = q.copy()
+        q[:, :, rot:] = (q_unfolded[:, :, rot:] * fold_w).astype(np.float32)
+
+    padv = np.uint16(PADS[pad])
+    pool = np.full(num_pages * page_stride, padv, dtype=np.uint16)
+    perm = torch.randperm(num_pages, generator=tgen).numpy().astype(np.int32)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    pool_pages = pool.reshape(num_pages, page_stride)
+
+    k = 0
+    for r, L in enumerate(seq_lens):
+        p0, p1 = spans[r]
+        lo = max(0, L - window) if window > 0 else 0
+        for j in range(p0, p1):
+            pid = int(perm[k]); k += 1
+            table[r, j] = pid
+            block = _normal_bf16(gen, (num_kv_heads, page_size, row_cols))
+            # positions of this page that are outside the visible range get the pad
+            pos = j * page_size + np.arange(page_size)
+            dead = (pos >= L) | (pos < lo)
+            block[:, dead, :] = padv
+            _store_page(pool_pages[pid], block, layout, num_kv_heads, page_size, row_cols)
+
+    return Workload(batch=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                    head_dim=D, fmt=fmt, rot_cols=rot, page_size=page_size,
+                    max_pages=max_pages, window=window, scale=scale, layout=layout,
+                    num_pages=num_pages, row_cols=row_cols, page_stride=page_stride,
+                    head_stride=head_stride, row_stride=row_stride, k_offset=k_off,
+                    v_offset=v_off, q=q, pool=pool, table=table,
+                    seq_lens=np.asarray(seq_lens, dtype=np.int32), fold_w=fold_w,
+                    q_unfolded=q_unfolded)
+
+
+def _store_page(dst: np.ndarray, block: np.ndarray, layout: str, hkv: int, ps: int, cols: int):
+    if layout == HEAD_MAJOR:
+        dst[:] = block.reshape(-1)
+    else:
+        dst[:] = block.transpose(1, 0, 2).reshape(-1)
+
+
+def split_pair_of_folded(wl: Workload) -> Workload:
+    """The split-row pool that a folded pool stands for.
+
+    Row = [Krot | bf16(w * V[rot:]) | V]: the unrotated K columns are what the
+    norm weight makes of V's columns, so the score against the folded row with
+    the folded query equals the score against this row with the unfolded
+    query, up to the bf16 rounding of w * V (pegainfer PR #1055, Description).
+    """
+    if wl.fmt != FOLDED:
+        raise ValueError("need a folded workload")
+    D, rot = wl.head_dim, wl.rot_cols
+    cols = 2 * D
+    page_stride, head_stride, row_stride = _strides(wl.layout, wl.num_kv_heads, wl.page_size, cols)
+    pool = np.empty(wl.num_pages * page_stride, dtype=np.uint16)
+    src = wl.pool.reshape(wl.num_pages, -1)
+    dst = pool.reshape(wl.num_pages, -1)
+    for p in range(wl.num_pages):
+        if wl.layout == HEAD_MAJOR:
+            rows = src[p].reshape(wl.num_kv_heads, wl.page_size, wl.row_cols)
+        else:
+            rows = src[p].reshape(wl.page_size, wl.num_kv_heads, wl.row_cols).transpose(1, 0, 2)
+        krot = rows[:, :, :rot]
+        v = rows[:, :, rot:]
+        vf = (v.astype(np.uint32) << 16).view(np.float32)
+        kfold = f32_to_bf16_bits((vf[:, :, rot:] * wl.fold_w).astype(np.float32))
+        out = np.concatenate([krot, kfold, v], axis=2)
+        _store_page(dst[p], out, wl.layout, wl.num_kv_heads, wl.page_size, cols)
+    return dataclasses.replace(wl, fmt=SPLIT, rot_cols=0, row_cols=cols, page_stride=page_stride,
+                               head_stride=head_stride, row_stride=row_stride, k_offset=0,
+                               v_offset=D, q=wl.q_unfolded.copy(), pool=pool)
+
+
+# ---- the workloads the pages measure -------------------------------------------------
+
+GLOBAL = dict(num_q_heads=32, num_kv_heads=4, head_dim=512, page_size=256)
+SLIDING = dict(num_q_heads=32, num_kv_heads=16, head_dim=256, page_size=64, window=1024)
+
+
+def tiny_ref(seed: int = 0, **kw) -> Workload:
+    """1 token of decode over a 1024-token context, split rows, 4 pages drawn
+    from a pool of 8 (the other 4 hold the pad), shuffled page table."""
+    return make_workload([1024], **GLOBAL, seed=seed, **kw)
+
+
+def global_decode(L: int, seed: int = 1, fmt: str = SPLIT, **kw) -> Workload:
+    """Global-layer decode at context L (10,602 / 40,002 / 81,653 / 163,336)."""
+    kw.setdefault("spare_pages", 1)
+    return make_workload([L], **GLOBAL, fmt=fmt, seed=seed, **kw)
+
+
+def sliding_batch(seed: int = 4, batch: int = 16, max_len: int = 4096, **kw) -> Workload:
+    """16 ragged requests, lengths drawn uniformly from 1..4096, window 1024."""
+    g = _gen(seed + 77)
+    lens = (torch.randint(1, max_len + 1, (batch,), generator=g)).tolist()
+    kw.setdefault("max_pages", max_len // SLIDING["page_size"])
+    return make_workload(lens, **SLIDING, seed=seed, **kw)

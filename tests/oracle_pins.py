@@ -1,0 +1,355 @@
+"""Checks that pin the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+brute-force computation, a closed form, an invariant or a figure printed on the
+pages.  ``test_oracle.py`` runs them as tests, and also runs them against
+deliberately broken copies of the oracle (on the CPU) to show that each planted
+mistake is caught by at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+import numpy as np
+
+import oracle
+import synth
+from tests.golden.read import load as load_golden
+
+
+# ---------------------------------------------------------------------------- helpers
+
+def _bf16_to_float(bits: int) -> float:
+    """Independent bf16 decode: the 16 bits are the top half of a big-endian binary32."""
+    return struct.unpack(">f", struct.pack(">I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def brute_force_decode(wl) -> np.ndarray:
+    """Pure-Python decode attention: explicit flat indexing, exp without max shift, fsum.
+
+    Element (page p, KV head g, slot s, column c) sits at flat index
+    p*page_stride + g*head_stride + s*row_stride + c.  Scores are kept small by the
+    callers, so exp(s) / sum exp(s) is evaluated literally.
+    """
+    D, G = wl.head_dim, wl.num_q_heads // wl.num_kv_heads
+    out = np.zeros((wl.batch, wl.num_q_heads, D))
+    pool = wl.pool
+    for r in range(wl.batch):
+        L = int(wl.seq_lens[r])
+        lo = L - wl.window if (wl.window and L > wl.window) else 0
+        for g in range(wl.num_kv_heads):
+            keys, vals = [], []
+            for j in range(lo, L):
+                p = int(wl.table[r][j // wl.page_size])
+                base = p * wl.page_stride + g * wl.head_stride + (j % wl.page_size) * wl.row_stride
+                row = [_bf16_to_float(pool[base + c]) for c in range(wl.row_cols)]
+                v = row[wl.v_offset:wl.v_offset + D]
+                if wl.fmt == "split":
+                    k = row[wl.k_offset:wl.k_offset + D]
+                else:
+                    k = row[wl.k_offset:wl.k_offset + wl.rot_cols] + v[wl.rot_cols:]
+                keys.append(k)
+                vals.append(v)
+            for h in range(g * G, (g + 1) * G):
+                qh = [float(x) for x in wl.q[r, h]]
+                w = [math.exp(wl.scale * math.fsum(qh[d] * k[d] for d in range(D))) for k in keys]
+                Z = math.fsum(w)
+                out[r, h] = [math.fsum(w[j] * vals[j][d] for j in range(len(w))) / Z for d in range(D)]
+    return out
+
+
+def _assert_close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    assert err <= tol * scale, f"{what}: max|diff| = {err:.3e} > {tol:.1e} x {scale:.3g}"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------- pins
+
+BRUTE_CASES = [
+    # (seq_lens, Hq, Hkv, D, page_size, window, fmt, layout)
+    ([1, 5, 16], 4, 2, 17, 4, 0, "split", synth.HEAD_MAJOR),
+    ([3, 16], 6, 3, 1, 8, 0, "split", synth.TOKEN_MAJOR),
+    ([16, 7], 16, 2, 512, 4, 0, "split", synth.HEAD_MAJOR),
+    ([14, 9, 1], 8, 1, 512, 4, 0, "folded", synth.TOKEN_MAJOR),
+    ([16, 11, 4, 2], 4, 4, 17, 4, 5, "split", synth.HEAD_MAJOR),
+]
+
+
+def pin_brute_force():
+    """Dense fp64 oracle == literal pure-Python softmax on tiny paged inputs."""
+    for i, (lens, hq, hkv, D, ps, W, fmt, layout) in enumerate(BRUTE_CASES):
+        wl = synth.make_workload(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=ps,
+                                 window=W, fmt=fmt, rot_cols=128, seed=10 + i, layout=layout,
+                                 spare_pages=3, pad="big")
+        _assert_close(oracle.decode_attention(wl), brute_force_decode(wl), 1e-13, f"brute case {i}")
+
+
+def pin_single_key():
+    """L = 1: softmax of one score is exactly 1, so o = v_0 bit for bit."""
+    for fmt in ("split", "folded"):
+        wl = synth.make_workload([1], num_q_heads=8, num_kv_heads=1, head_dim=512, page_size=256,
+                                 fmt=fmt, seed=3)
+        v0 = oracle.bf16_bits_to_f64(oracle.gather_rows(wl, 0, 0, np.array([0])))[0]
+        v0 = v0[wl.v_offset:wl.v_offset + 512]
+        o = oracle.decode_attention(wl)
+        for h in range(8):
+            assert np.array_equal(o[0, h], v0), "L=1 output is not v_0"
+
+
+def pin_uniform_scores():
+    """q = 0 (all scores equal) or identical keys: o is the plain mean of V."""
+    wl = synth.make_workload([37], num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=16, seed=4)
+    wl.q[:] = 0.0
+    pos = np.arange(37)
+    o = oracle.decode_attention(wl)
+    for g in range(2):
+        V = oracle.bf16_bits_to_f64(oracle.gather_rows(wl, 0, g, pos))[:, 64:128]
+        for h in (2 * g, 2 * g + 1):
+            _assert_close(o[0, h], V.mean(axis=0), 1e-14, "q=0 mean")
+    # identical keys, arbitrary q
+    D = 32
+    K = np.tile(_rng(5).standard_normal(D), (9, 1))
+    V = _rng(6).standard_normal((9, D))
+    q = _rng(7).standard_normal((3, D))
+    _assert_close(oracle.dense_attention(q, K, V, 0.3), np.tile(V.mean(axis=0), (3, 1)), 1e-14,
+                  "identical keys mean")
+
+
+def pin_two_keys():
+    """Two keys: o = sigma(s1 - s2) v1 + sigma(s2 - s1) v2."""
+    rng = _rng(8)
+    for _ in range(20):
+        D = int(rng.integers(1, 40))
+        K = rng.standard_normal((2, D)) * 3
+        V = rng.standard_normal((2, D))
+        q = rng.standard_normal((1, D))
+        scale = float(rng.uniform(0.1, 2))
+        s1, s2 = scale * float(q[0] @ K[0]), scale * float(q[0] @ K[1])
+        w1 = 1.0 / (1.0 + math.exp(s2 - s1))
+        expect = w1 * V[0] + (1.0 - w1) * V[1]
+        _assert_close(oracle.dense_attention(q, K, V, scale)[0], expect, 1e-14, "two keys")
+
+
+def pin_needle():
+    """One key scoring 40 above every other: o = v_needle to within L e^-40."""
+    rng = _rng(9)
+    n, D = 300, 48
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((n, D)) * 0.01
+    K[123] = q / np.dot(q, q) * 45.0          # score 45 against at most ~1 for the rest
+    V = rng.standard_normal((n, D))
+    o = oracle.dense_attention(q[None], K, V, 1.0)[0]
+    _assert_close(o, V[123], n * math.exp(-40.0), "needle")
+
+
+def pin_gqa_grouping():
+    """Eight query heads per KV head, consecutive: head h reads KV head h // G.
+
+    Every V row of KV head g is the constant g + 1, so o[h] = h // G + 1 (to rounding).
+    """
+    wl = synth.make_workload([40], num_q_heads=32, num_kv_heads=4, head_dim=16, page_size=8,
+                             seed=11)
+    rows = wl.pool.reshape(wl.num_pages, 4, 8, 32)
+    for g in range(4):
+        rows[:, g, :, 16:] = synth.f32_to_bf16_bits(np.float32(g + 1))
+    o = oracle.decode_attention(wl)
+    for h in range(32):
+        assert np.max(np.abs(o[0, h] - (h // 8 + 1))) < 1e-13, f"head {h} did not read KV head {h // 8}"
+
+
+def pin_linearity_and_order():
+    """o is linear in V, invariant to reordering the keys, and to (q, scale) -> (cq, scale/c)."""
+    rng = _rng(12)
+    n, D = 50, 24
+    q = rng.standard_normal((3, D))
+    K = rng.standard_normal((n, D))
+    V1 = rng.standard_normal((n, D))
+    V2 = rng.standard_normal((n, D))
+    f = oracle.dense_attention
+    _assert_close(f(q, K, V1 + 2 * V2, 0.4), f(q, K, V1, 0.4) + 2 * f(q, K, V2, 0.4), 1e-13, "linear")
+    p = rng.permutation(n)
+    _assert_close(f(q, K[p], V1[p], 0.4), f(q, K, V1, 0.4), 1e-13, "key order")
+    _assert_close(f(4 * q, K, V1, 0.1), f(q, K, V1, 0.4), 1e-13, "scale")
+
+
+def _split_cuts(n, ways):
+    """Equal-as-possible cut points; more ways than tokens gives empty partitions."""
+    return [(i * n) // ways for i in range(ways + 1)]
+
+
+def pin_partition_invariance():
+    """Split-KV partials merged in two levels == dense, for 1/2/3/4/7/16-way splits of the
+    13 x 17 fixture (16-way has empty partitions), random cuts at D=512, L=1024."""
+    fx = load_golden("partition_fixture.txt")
+    n, D = fx["tokens"], fx["dims"]
+    rng = _rng(13)
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    dense = oracle.dense_attention(q[None], K, V, 0.5)[0]
+    for ways in fx["ways"]:
+        cuts = _split_cuts(n, ways)
+        if ways > n:
+            assert any(a == b for a, b in zip(cuts[:-1], cuts[1:])), "no empty partition"
+        for group in (1, 2, 3, ways):
+            got = oracle.split_kv_attention(q, K, V, 0.5, cuts, group)
+            _assert_close(got, dense, 1e-13, f"{ways}-way, group {group}")
+    n, D = 1024, 512
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    dense = oracle.dense_attention(q[None], K, V, 1 / math.sqrt(D))[0]
+    for _ in range(5):
+        inner = np.sort(rng.integers(0, n + 1, size=int(rng.integers(1, 40))))
+        cuts = [0] + inner.tolist() + [n]
+        got = oracle.split_kv_attention(q, K, V, 1 / math.sqrt(D), cuts, int(rng.integers(1, 9)))
+        _assert_close(got, dense, 1e-13, "random cuts")
+
+
+def pin_empty_merge_identity():
+    """merge(a, empty) and merge(empty, a) are a bit for bit (alpha = e^0 = 1, beta = 0)."""
+    rng = _rng(14)
+    D = 33
+    a = oracle.partial_state(rng.standard_normal(D), rng.standard_normal((7, D)),
+                             rng.standard_normal((7, D)), 0.7)
+    e = oracle.empty_state(D)
+    for m in (oracle.merge(a, e), oracle.merge(e, a)):
+        assert m.m == a.m and m.l == a.l and np.array_equal(m.acc, a.acc), "empty merge changed a"
+    ee = oracle.merge(e, e)
+    assert ee.m == -math.inf and ee.l == 0.0 and not np.any(ee.acc)
+
+
+def pin_merge_identity_values():
+    """merge(partial(A), partial(B)) == partial(A u B) for the state itself, not just O/S."""
+    rng = _rng(15)
+    D = 20
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((30, D)) * 2
+    V = rng.standard_normal((30, D))
+    whole = oracle.partial_state(q, K, V, 0.9)
+    m = oracle.merge(oracle.partial_state(q, K[:11], V[:11], 0.9),
+                     oracle.partial_state(q, K[11:], V[11:], 0.9))
+    assert m.m == whole.m
+    _assert_close(m.l, whole.l, 1e-14, "merged S")
+    _assert_close(m.acc, whole.acc, 1e-14, "merged O")
+
+
+def pin_gem_audit_bounds(lengths=None):
+    """At gem's audit lengths with P = 32, DV = 512, the split path stays inside the bounds
+    the page prints against direct softmax (upper bounds: fp64 should be far below)."""
+    gold = load_golden("gem_online_merge_audit.txt")
+    P, D = gold["partitions"], gold["value_dim"]
+    rng = _rng(16)
+    for n in (lengths or gold["lengths"]):
+        K = rng.standard_normal((n, D)).astype(np.float32).astype(np.float64)
+        V = rng.standard_normal((n, D)).astype(np.float32).astype(np.float64)
+        q = rng.standard_normal(D).astype(np.float32).astype(np.float64)
+        dense = oracle.dense_attention(q[None], K, V, 1 / math.sqrt(D))[0]
+        got = oracle.split_kv_attention(q, K, V, 1 / math.sqrt(D), _split_cuts(n, P), 8)
+        err = got - dense
+        nmse = float(np.sum(err ** 2) / np.sum(dense ** 2))
+        corr = float(np.corrcoef(got, dense)[0, 1])
+        assert np.all(np.isfinite(got))
+        assert float(np.max(np.abs(err))) < gold["max_abs_max"], f"max|diff| at {n}"
+        assert nmse <= gold["nmse_max"], f"NMSE at {n}"
+        assert corr >= gold["corr_min"], f"corr at {n}"
+        # repeat determinism
+        again = oracle.split_kv_attention(q, K, V, 1 / math.sqrt(D), _split_cuts(n, P), 8)
+        assert np.array_equal(got, again)
+
+
+def pin_window():
+    """Windowed decode == dense attention over the sliced in-window keys, for L around W;
+    the pad in masked slots (older keys of resident pages) does not change a bit."""
+    W = 64
+    for L in (1, W - 1, W, W + 1, W + 16, W + 64, 3 * W + 5):
+        outs = {}
+        for pad in ("nan", "big", "zero"):
+            wl = synth.make_workload([L], num_q_heads=4, num_kv_heads=2, head_dim=32, page_size=16,
+                                     window=W, seed=17, pad=pad)
+            outs[pad] = oracle.decode_attention(wl)
+        assert np.array_equal(outs["nan"], outs["big"]) and np.array_equal(outs["nan"], outs["zero"])
+        lo = max(0, L - W)
+        for g in range(2):
+            rows = oracle.bf16_bits_to_f64(oracle.gather_rows(wl, 0, g, np.arange(lo, L)))
+            K, V = rows[:, :32], rows[:, 32:]
+            assert K.shape[0] == min(L, W)
+            ref = oracle.dense_attention(wl.q[0, 2 * g:2 * g + 2], K, V, wl.scale)
+            _assert_close(outs["zero"][0, 2 * g:2 * g + 2], ref, 1e-15, f"window L={L}")
+
+
+def pin_permutation_invariance():
+    """Any page-table permutation (data moved with it) and either pool layout: same bits."""
+    base = synth.make_workload([300, 77], num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+                               seed=18, table_seed=1)
+    ref = oracle.decode_attention(base)
+    for ts, layout in ((2, synth.HEAD_MAJOR), (3, synth.TOKEN_MAJOR), (1, synth.TOKEN_MAJOR)):
+        wl = synth.make_workload([300, 77], num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=32,
+                                 seed=18, table_seed=ts, layout=layout)
+        if ts != 1:
+            assert not np.array_equal(wl.table, base.table)
+        assert np.array_equal(oracle.decode_attention(wl), ref), f"table seed {ts} {layout}"
+
+
+def pin_folded_equals_split():
+    """Folded row + folded query == split row with K[rot:] = w * V[rot:] (fp64, unrounded)."""
+    wl = synth.make_workload([700], num_q_heads=8, num_kv_heads=1, head_dim=512, page_size=256,
+                             fmt="folded", seed=19)
+    # fold w into q in fp64 here, so the identity is exact (the fp32 fold rounds by 2^-24)
+    q64 = wl.q_unfolded.astype(np.float64)
+    q64[:, :, 128:] *= wl.fold_w.astype(np.float64)
+    wl.q = q64
+    o_fold = oracle.decode_attention(wl)
+    rows = oracle.bf16_bits_to_f64(oracle.gather_rows(wl, 0, 0, np.arange(700)))
+    krot, V = rows[:, :128], rows[:, 128:640]
+    K = np.concatenate([krot, V[:, 128:] * wl.fold_w.astype(np.float64)], axis=1)
+    o_split = oracle.dense_attention(wl.q_unfolded[0], K, V, wl.scale)
+    _assert_close(o_fold[0], o_split, 1e-12, "folded vs split")
+
+
+def pin_fail_closed():
+    """States no finite key set can produce are refused, as is finalize of no keys."""
+    D = 4
+    good = oracle.State(0.5, 2.0, np.ones(D))
+    bad = [
+        oracle.State(math.nan, 1.0, np.zeros(D)),
+        oracle.State(math.inf, 1.0, np.zeros(D)),
+        oracle.State(-math.inf, 1.0, np.zeros(D)),
+        oracle.State(-math.inf, 0.0, np.ones(D)),
+        oracle.State(0.0, 0.5, np.zeros(D)),
+        oracle.State(0.0, 2.0, np.array([1.0, math.nan, 0.0, 0.0])),
+        oracle.State(0.0, math.inf, np.zeros(D)),
+    ]
+    for st in bad:
+        for args in ((st, good), (good, st)):
+            try:
+                oracle.merge(*args)
+            except oracle.InvalidState:
+                continue
+            raise AssertionError(f"merge accepted invalid state {st}")
+        try:
+            oracle.finalize(st)
+        except oracle.InvalidState:
+            pass
+        else:
+            raise AssertionError(f"finalize accepted invalid state {st}")
+    try:
+        oracle.finalize(oracle.empty_state(D))
+    except oracle.InvalidState:
+        pass
+    else:
+        raise AssertionError("finalize of the empty state returned")
+
+
+ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, pin_needle,
+            pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
+            pin_empty_merge_identity, pin_merge_identity_values, pin_window,
+            pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed]

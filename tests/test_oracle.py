@@ -1,0 +1,131 @@
+"""The fp64 oracle against brute force, closed forms, invariants and the pages' figures,
+plus planted mistakes (in copies of the oracle, on the CPU) that the pins must catch."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as OA
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_gem_audit_bounds_short():
+    P.pin_gem_audit_bounds(lengths=[8191, 8192, 8193])
+
+
+def test_gem_audit_bounds_long():
+    P.pin_gem_audit_bounds(lengths=[65536, 131072])
+
+
+# ---------------------------------------------------------------------- planted mistakes
+
+def _kv_swapped(wl, rows):
+    K, V = _orig_keys_values(wl, rows)
+    return V, K
+
+
+def _gqa_modulo(wl):
+    G = wl.num_q_heads // wl.num_kv_heads
+    out = np.empty((wl.batch, wl.num_q_heads, wl.head_dim))
+    for r in range(wl.batch):
+        lo, L = OA.visible_range(int(wl.seq_lens[r]), wl.window)
+        for h in range(wl.num_q_heads):
+            g = h % wl.num_kv_heads
+            K, V = OA.keys_values(wl, OA.bf16_bits_to_f64(OA.gather_rows(wl, r, g, np.arange(lo, L))))
+            out[r, h] = OA.dense_attention(wl.q[r, h][None], K, V, wl.scale)[0]
+    return out
+
+
+def _no_scale(q, K, V, scale):
+    return _orig_dense(q, K, V, 1.0)
+
+
+def _window_off_by_one(L, window):
+    lo, hi = _orig_visible(L, window)
+    return (lo + 1 if window > 0 and lo > 0 else lo), hi
+
+
+def _folded_wrong_cols(wl, rows):
+    K, V = _orig_keys_values(wl, rows)
+    if wl.fmt == "folded":
+        K = rows[:, :wl.head_dim]
+    return K, V
+
+
+def _merge_no_rescale(a, b):
+    OA.validate(a)
+    OA.validate(b)
+    M = max(a.m, b.m)
+    if M == -math.inf:
+        return OA.empty_state(a.acc.shape[0])
+    alpha = 0.0 if a.m == -math.inf else math.exp(a.m - M)
+    beta = 0.0 if b.m == -math.inf else math.exp(b.m - M)
+    return OA.State(M, alpha * a.l + beta * b.l, a.acc + b.acc)
+
+
+def _merge_swapped_weights(a, b):
+    OA.validate(a)
+    OA.validate(b)
+    M = max(a.m, b.m)
+    if M == -math.inf:
+        return OA.empty_state(a.acc.shape[0])
+    alpha = 0.0 if a.m == -math.inf else math.exp(a.m - M)
+    beta = 0.0 if b.m == -math.inf else math.exp(b.m - M)
+    return OA.State(M, beta * a.l + alpha * b.l, beta * a.acc + alpha * b.acc)
+
+
+def _gather_slot_page_swapped(wl, r, g, positions):
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = wl.table[r][(positions % wl.page_size) % wl.table.shape[1]].astype(np.int64)
+    pages = np.clip(pages, 0, wl.num_pages - 1)
+    return OA.row_view(wl)[pages, g, positions // wl.page_size % wl.page_size]
+
+
+def _dense_max_wrong_axis(q, K, V, scale):
+    q = np.asarray(q, dtype=np.float64)
+    s = scale * (q @ K.T)
+    m = s.max(axis=0, keepdims=True)
+    e = np.exp(s - m)
+    return (e @ V) / e.sum(axis=1, keepdims=True).max()
+
+
+def _validate_lenient(st):
+    return None
+
+
+_orig_keys_values = OA.keys_values
+_orig_dense = OA.dense_attention
+_orig_visible = OA.visible_range
+
+MUTANTS = {
+    "k_v_swapped": ("keys_values", _kv_swapped),
+    "gqa_modulo": ("decode_attention", _gqa_modulo),
+    "scale_dropped": ("dense_attention", _no_scale),
+    "window_off_by_one": ("visible_range", _window_off_by_one),
+    "folded_wrong_columns": ("keys_values", _folded_wrong_cols),
+    "merge_without_rescale": ("merge", _merge_no_rescale),
+    "merge_weights_swapped": ("merge", _merge_swapped_weights),
+    "gather_slot_page_swapped": ("gather_rows", _gather_slot_page_swapped),
+    "softmax_max_wrong_axis": ("dense_attention", _dense_max_wrong_axis),
+    "no_fail_closed": ("validate", _validate_lenient),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
