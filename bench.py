@@ -1,0 +1,304 @@
+"""Benchmark: one decode step of paged split-KV attention on one MI355X.
+
+A step is the whole hot path for one global-layer decode token: attn_decode_split
+(page-table gather, K/V streaming, scores, online softmax, PV, partial write)
+followed by attn_decode_merge (level-1 and level-2 merge, O / S), at 163,336
+tokens of context, 32 query / 4 KV heads, head dim 512, split 1024-column rows
+in pages of 256 with a shuffled page table.  Inputs are synthetic N(0, 1) data
+already resident in HBM when timing starts.
+
+Prints one JSON line.  `value` is effective GB/s: K/V row bytes the step must
+read divided by the step time.  `roofline` reports the partial kernel's own
+algorithmic bytes over its average duration (HIP events on its stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/step + effective HBM GB/s (% peak) at 163K ctx, hd512"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_global163k_split.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--context", type=int, default=163336)
+    ap.add_argument("--fmt", choices=["split", "folded"], default="split")
+    ap.add_argument("--num-chunks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference kernel for counters)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("attn_decode.hip", "plan.cpp", "plan_internal.h"):
+        with open(os.path.join(ROOT, "paged_split_kv_02_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(launch_bytes: int):
+    """HBM bytes per partial-kernel launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Resident:
+    """A workload's buffers on the GPU and its plan."""
+
+    def __init__(self, wl, num_chunks=0):
+        import numpy as np
+        import torch
+        import paged_split_kv_02_amd as K
+        dev = torch.device("cuda:0")
+        self.wl = wl
+        self.K = K
+        self.plan = K.attn_decode_plan(K.make_desc(**wl.desc_fields(num_chunks)), wl.seq_lens)
+        self.q = torch.from_numpy(np.ascontiguousarray(wl.q, dtype=np.float32)).to(dev)
+        self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(dev)
+        self.table = torch.from_numpy(wl.table).to(dev)
+        self.lens = torch.from_numpy(wl.seq_lens).to(dev)
+        self.ws = torch.empty(int(self.plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.float32,
+                               device=dev)
+
+    def split(self):
+        self.K.attn_decode_split(self.plan, self.q, self.pool, self.table, self.lens, self.ws)
+
+    def merge(self):
+        self.K.attn_decode_merge(self.plan, self.ws, self.out)
+
+    def kernel_bytes(self) -> int:
+        """Algorithmic bytes of one partial-kernel launch: K/V rows read, q, page-table
+        entries, and the chunk states written."""
+        wl, p = self.wl, self.plan
+        pages = sum(-(-int(L) // wl.page_size) for L in wl.seq_lens)
+        states = wl.batch * wl.num_q_heads * p.num_chunks
+        return (wl.kv_bytes() + wl.q.size * 4 + pages * 4 + states * (wl.head_dim + 2) * 4)
+
+
+def time_steps(res, steps, warmup, flush=None):
+    """Time `steps` decode steps (split + merge).
+
+    Without ``flush``: region A brackets all steps with one pair of events (the
+    step time); region B repeats the steps with events around each partial-kernel
+    launch (its duration, for the roofline).  With ``flush`` (inputs that fit the
+    256 MB infinity cache): every step is preceded by an untimed 1 GiB write and
+    timed on its own.
+    """
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        res.split()
+        res.merge()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    if flush is None:
+        first, last = E(), E()
+        t0 = time.perf_counter()
+        first.record(stream)
+        for _ in range(steps):
+            res.split()
+            res.merge()
+        last.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = first.elapsed_time(last)
+        ev = [(E(), E()) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            res.split()
+            b.record(stream)
+            res.merge()
+        torch.cuda.synchronize()
+        split_ms = [a.elapsed_time(b) for a, b in ev]
+        return dict(total_ms=total_ms, wall_s=wall, split_ms=split_ms,
+                    step_ms=[total_ms / steps] * steps)
+    step_ms, split_ms = [], []
+    for _ in range(steps):
+        flush()
+        a, b, c = E(), E(), E()
+        a.record(stream)
+        res.split()
+        b.record(stream)
+        res.merge()
+        c.record(stream)
+        torch.cuda.synchronize()
+        step_ms.append(a.elapsed_time(c))
+        split_ms.append(a.elapsed_time(b))
+    return dict(total_ms=sum(step_ms), wall_s=None, split_ms=split_ms, step_ms=step_ms)
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """Time the fp64 oracle on the host over the same step, repeated until the budget
+    is spent (KV heads one after another, at least one); GB/s of K/V rows consumed."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    G = wl.num_q_heads // wl.num_kv_heads
+    done_heads = 0
+    total_heads = wl.batch * wl.num_kv_heads
+    t0 = time.perf_counter()
+    while True:
+        for r in range(wl.batch):
+            lo, L = oracle.visible_range(int(wl.seq_lens[r]), wl.window)
+            pos = np.arange(lo, L)
+            for g in range(wl.num_kv_heads):
+                Kx, Vx = oracle.keys_values(
+                    wl, oracle.bf16_bits_to_f64(oracle.gather_rows(wl, r, g, pos)))
+                oracle.dense_attention(wl.q[r, g * G:(g + 1) * G], Kx, Vx, wl.scale)
+                done_heads += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    bytes_done = wl.kv_bytes() * done_heads / total_heads
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(bytes_done / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done_heads} KV-head passes ({done_heads / total_heads:.2f} steps) of the "
+                      f"same {wl.seq_lens[0]}-token step, fp64 numpy oracle, {dt:.1f} s wall",
+            "seconds": round(dt, 2),
+            "us_per_step_equiv": round(dt / done_heads * total_heads * 1e6, 1),
+            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
+              "(the decode step shards across GPUs without this process).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_split_kv_02_amd  # noqa: F401  (raises if the HIP library is missing)
+
+    t_gen = time.perf_counter()
+    wl = synth.global_decode(args.context, seed=2, fmt=args.fmt)
+    print(f"# generated {args.context}-token {args.fmt} workload in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    res = Resident(wl, args.num_chunks)
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del a, b
+
+    t = time_steps(res, args.steps, args.warmup)
+    ms_per_step = t["total_ms"] / args.steps
+    kv = wl.kv_bytes()
+    gbs = kv / (ms_per_step * 1e-3) / 1e9
+    split_avg_ms = sum(t["split_ms"]) / len(t["split_ms"])
+    kb = res.kernel_bytes()
+    achieved = kb / (split_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(kb)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_median": round(median(t["step_ms"]) * 1e3, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"global-decode-{args.context}-{args.fmt}", "context": args.context,
+                   "batch": 1, "q_heads": 32, "kv_heads": 4, "head_dim": 512, "page_size": 256,
+                   "row_cols": wl.row_cols, "num_chunks": res.plan.num_chunks,
+                   "chunk_len": res.plan.chunk_len, "merge_group": res.plan.merge_group,
+                   "kv_bytes": kv, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "split_partial_kernel",
+                     "kernel_us": round(split_avg_ms * 1e3, 2), "algorithmic_bytes": kb},
+        "merge_us": round((ms_per_step - split_avg_ms) * 1e3, 2),
+    }
+    print(f"# step {ms_per_step * 1e3:.1f} us, partial kernel {split_avg_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    del res
+
+    if not args.no_variants:
+        variants = {}
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+
+        def flush():
+            flush_buf.zero_()  # 1 GiB of writes evicts the 256 MB infinity cache
+        for name, maker, n_steps in (
+                ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
+                ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20)):
+            vwl = maker()
+            vres = Resident(vwl)
+            vt = time_steps(vres, n_steps, 3, flush=flush)
+            vms = median(vt["step_ms"])
+            vsplit = median(vt["split_ms"])
+            variants[name] = {"us_per_step": round(vms * 1e3, 2),
+                              "partial_kernel_us": round(vsplit * 1e3, 2),
+                              "kv_bytes": vwl.kv_bytes(),
+                              "effective_gbs": round(vwl.kv_bytes() / (vms * 1e-3) / 1e9, 1),
+                              "partial_kernel_gbs": round(vres.kernel_bytes() / (vsplit * 1e-3) / 1e9, 1),
+                              "num_chunks": vres.plan.num_chunks, "timing": "median, cache flushed"}
+            print(f"# {name}: {vms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+            del vres
+        line["variants"] = variants
+        del flush_buf
+
+    if not args.no_cpu_baseline:
+        print("# timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

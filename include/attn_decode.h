@@ -1,0 +1,182 @@
+/*
+ * attn_decode.h -- C ABI of the paged split-KV decode-attention library (gfx950).
+ *
+ * One decode step of one attention layer: every query head of every request
+ * attends, with an exact softmax, over its KV head's keys stored in a paged pool.
+ * The keys are cut into chunks; each chunk yields an online-softmax partial
+ * (running max M, sum S, unnormalised numerator O) and the partials are merged
+ * with the exact rescaling identity in two levels (pegainfer PR #1055,
+ * "Description": a split-KV decode kernel with a partial over key chunks and a
+ * merge in two levels; gem "Parked D512 fused split-KV decode design", section
+ * "Candidate ownership and storage": M = max(Ma, Mb), S = Sa e^(Ma-M) + Sb e^(Mb-M),
+ * the numerator likewise, then O / S).
+ *
+ * Three calls make a step:
+ *   attn_decode_plan   host only: validates the shape and the request lengths,
+ *                      chooses the chunking and lays out the workspace.
+ *   attn_decode_split  enqueues the partial kernel on a HIP stream.
+ *   attn_decode_merge  enqueues the merge (level 1, level 2, O / S) on a stream.
+ *
+ * Ownership: the caller owns every buffer (query, pool, page table, lengths,
+ * workspace, output).  The library allocates nothing, keeps no mutable global
+ * state and is reentrant.  Launches are asynchronous; buffers must stay alive
+ * until the stream has run them.  A plan is plain old data and may be copied.
+ *
+ * Errors: every check runs before any launch, so a refused call enqueues
+ * nothing.  Kernels write only the plan's workspace extent and `out`.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID_ARG = -1,  /* null pointer, non-positive size, inconsistent layout */
+  ATTN_E_UNSUPPORTED = -2,  /* shape with no kernel: see attn_decode_desc */
+  ATTN_E_PAST_PAGES = -3,   /* a length needs more pages than a table row holds */
+  ATTN_E_OVERFLOW = -4,     /* a size computation would overflow 64 bits / grid limits */
+  ATTN_E_WORKSPACE = -5,    /* workspace smaller than the plan needs, or misaligned */
+  ATTN_E_PLAN = -6,         /* plan not produced by attn_decode_plan (bad magic) */
+  ATTN_E_LAUNCH = -7        /* the HIP runtime refused a launch */
+};
+
+/* Row formats of the pool, fixed for the pool's life (pegainfer PR #1055,
+ * "Description": the page format is an axis of the layout). */
+enum {
+  ATTN_KV_SPLIT = 0,   /* row = K[0:D] at k_offset, V[0:D] at v_offset (1024 cols at D=512) */
+  ATTN_KV_FOLDED = 1   /* row = rotated K[0:rot] at k_offset, V[0:D] at v_offset; the
+                          unrotated part of the score is q'[rot:D] . V[rot:D], with K's norm
+                          weight already folded into q' by the caller (640 cols at D=512) */
+};
+
+/*
+ * Shape and layout of one layer's paged pool and decode batch.
+ *
+ * Supported shapes (others give ATTN_E_UNSUPPORTED):
+ *   head_dim 512, 8 query heads per KV head, SPLIT, or FOLDED with rot_cols 128
+ *   head_dim 256, 2 query heads per KV head, SPLIT (sliding layers, any window)
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Element (page p, KV head g, slot s, column c) of the pool is the bf16 at
+ *   pool[p * page_stride + g * head_stride + s * row_stride + c]
+ * All strides and offsets count bf16 elements and must be multiples of 8
+ * (16-byte loads); every row of a page must lie inside its page_stride.
+ * Logical key position j of request r lives in slot j % page_size of page
+ * page_table[r * max_pages_per_seq + j / page_size] (TensorFold PR #1619, body).
+ *
+ * window > 0 makes a request of length L attend to positions [L - window, L)
+ * only; older keys in resident pages are masked (pegainfer PR #1057,
+ * "Description").  Page-table entries wholly before that range are never read.
+ */
+typedef struct attn_decode_desc {
+  int32_t batch;              /* requests, one query token each */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;           /* D: 512 or 256 */
+  int32_t format;             /* ATTN_KV_SPLIT or ATTN_KV_FOLDED */
+  int32_t rot_cols;           /* FOLDED: stored rotated K columns (128); SPLIT: 0 */
+  int32_t page_size;          /* positions per page, a multiple of 16 */
+  int32_t max_pages_per_seq;  /* length of one page-table row */
+  int32_t window;             /* 0 = whole context */
+  int32_t num_chunks;         /* key chunks per (request, KV head); 0 = choose automatically */
+  int32_t merge_group;        /* chunk partials per level-1 group; 0 = choose automatically,
+                                 else at least ceil(chunks / 8) (at most 8 groups) */
+  float scale;                /* score = scale * q . k (1/sqrt(D) in the workloads) */
+  int64_t num_pages;          /* pages in the pool; table entries outside [0, num_pages) poison */
+  int64_t page_stride;        /* elements between pages */
+  int64_t head_stride;        /* elements between KV heads inside a page */
+  int64_t row_stride;         /* elements between consecutive slots */
+  int64_t k_offset;           /* column of K[0] (split) or of the rotated K[0] (folded) */
+  int64_t v_offset;           /* column of V[0] */
+} attn_decode_desc;
+
+/*
+ * A validated plan (host-only POD).  Chunk c of request r covers key positions
+ *   [start_r + c * chunk_len, start_r + (c + 1) * chunk_len)  intersected with [lo_r, L_r)
+ * where lo_r = max(0, L_r - window) (0 without a window) and
+ * start_r = lo_r rounded down to a multiple of `tile`.  A chunk with no visible key
+ * yields the empty partial (-inf, 0, 0).
+ *
+ * Workspace layout (byte offsets from the workspace base, each region 256-byte
+ * aligned, all float32, partition-major and contiguous in the output dimension;
+ * gem design note, "Candidate ownership and storage"):
+ *   part_m [B][Hq][num_chunks]        running maxima, natural-log units
+ *   part_l [B][Hq][num_chunks]        denominators S
+ *   part_o [B][Hq][num_chunks][D]     numerators O (unnormalised)
+ * The merge's level-1 group states live in on-chip memory and need no workspace.
+ */
+typedef struct attn_decode_plan_t {
+  uint64_t magic;
+  attn_decode_desc desc;
+  int32_t group_size;    /* query heads per KV head */
+  int32_t tile;          /* keys per tile; chunk starts are multiples of it */
+  int32_t chunk_len;     /* keys per chunk, a multiple of tile */
+  int32_t num_chunks;    /* chunks per (request, KV head) */
+  int32_t merge_group;   /* chunk partials folded per level-1 group */
+  int32_t num_groups;    /* level-1 states per (request, query head), at most 8 */
+  int32_t max_span;      /* max over requests of L_r - start_r */
+  int32_t reserved;
+  uint64_t off_part_m, off_part_l, off_part_o;
+  uint64_t workspace_bytes; /* bytes attn_decode_split / attn_decode_merge need */
+} attn_decode_plan_t;
+
+/*
+ * Validate `desc` and the host copy of the request lengths seq_lens_host[batch]
+ * and fill `plan`.  No device call is made.
+ * Refusals: null pointers or non-positive sizes (ATTN_E_INVALID_ARG); a shape
+ * outside the supported list (ATTN_E_UNSUPPORTED); a stride or offset not a
+ * multiple of 8, or rows overrunning their page (ATTN_E_INVALID_ARG); a length
+ * below 1 (ATTN_E_INVALID_ARG); a length above max_pages_per_seq * page_size
+ * (ATTN_E_PAST_PAGES, TensorFold PR #1619, body: rows past a slot's pages are
+ * refused); a merge_group below ceil(chunks / 8) (ATTN_E_UNSUPPORTED); any size
+ * product that overflows, or a grid beyond the launch limits (ATTN_E_OVERFLOW;
+ * gem design note, "Candidate ownership and storage": all scratch products are
+ * overflow-checked).
+ */
+int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
+                     attn_decode_plan_t* plan);
+
+/*
+ * Enqueue the partial kernel: one online-softmax state per (request, query
+ * head, chunk) into the workspace's part_* regions.
+ *   q          device, float32 [batch][num_q_heads][head_dim] (FOLDED: the folded q')
+ *   kv_pool    device, bf16 pool laid out as described for attn_decode_desc
+ *   page_table device, int32 [batch][max_pages_per_seq]
+ *   seq_lens   device, int32 [batch]; must equal the lengths given to the plan.  A
+ *              device length or page id the plan cannot serve is not read past:
+ *              the affected request's partials become NaN.
+ *   workspace  device, >= plan->workspace_bytes, 256-byte aligned
+ *   stream     hipStream_t (NULL = the default stream)
+ * Returns ATTN_E_PLAN on a bad plan, ATTN_E_WORKSPACE on a short or misaligned
+ * workspace, ATTN_E_INVALID_ARG on null pointers, ATTN_E_LAUNCH if HIP refuses.
+ */
+int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                      const int32_t* page_table, const int32_t* seq_lens, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Enqueue the two-level merge as one kernel: level 1 folds each run of
+ * merge_group consecutive chunk states into a group state (out of place: the
+ * chunk states are only read); level 2 folds the group states in ascending
+ * order and writes O / S.
+ *   out   device, float32 [batch][num_q_heads][head_dim]; nothing else is written.
+ * Same error behaviour as attn_decode_split.
+ */
+int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace, size_t workspace_bytes,
+                      float* out, void* stream);
+
+/* Static, NUL-terminated text for a status code. */
+const char* attn_decode_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

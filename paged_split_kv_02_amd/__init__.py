@@ -1,0 +1,143 @@
+"""Paged split-KV decode attention for MI355X (gfx950).
+
+A thin ctypes binding of the C ABI in include/attn_decode.h: the same four
+calls, argument marshalling only.  Every step of the computation runs in the
+HIP library; if it is missing or cannot be loaded, importing this package
+raises.  Device buffers are passed as torch tensors (their data_ptr) or as raw
+integer addresses; ``stream`` defaults to torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+__all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_plan",
+           "attn_decode_split", "attn_decode_merge", "attn_decode_status_string", "make_desc",
+           "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "STATUS", "LIB_PATH", "SYMBOLS"]
+
+ATTN_KV_SPLIT = 0
+ATTN_KV_FOLDED = 1
+STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
+          "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
+          "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
+SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_merge",
+           "attn_decode_status_string")
+LIB_PATH = _build.LIB
+
+
+class AttnDecodeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("format", ctypes.c_int32), ("rot_cols", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("merge_group", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_pages", ctypes.c_int64), ("page_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+                ("k_offset", ctypes.c_int64), ("v_offset", ctypes.c_int64)]
+
+
+class AttnDecodePlan(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint64), ("desc", AttnDecodeDesc),
+                ("group_size", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("merge_group", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("max_span", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("off_part_m", ctypes.c_uint64), ("off_part_l", ctypes.c_uint64),
+                ("off_part_o", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+class AttnDecodeError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call}: {attn_decode_status_string(status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.attn_decode_plan.argtypes = [ctypes.POINTER(AttnDecodeDesc), P, ctypes.POINTER(AttnDecodePlan)]
+    lib.attn_decode_plan.restype = ctypes.c_int
+    lib.attn_decode_split.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P, P, ctypes.c_size_t, P]
+    lib.attn_decode_split.restype = ctypes.c_int
+    lib.attn_decode_merge.argtypes = [ctypes.POINTER(AttnDecodePlan), P, ctypes.c_size_t, P, P]
+    lib.attn_decode_merge.restype = ctypes.c_int
+    lib.attn_decode_status_string.argtypes = [ctypes.c_int]
+    lib.attn_decode_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(x) -> int:
+    """Device/host address of a torch tensor, numpy array or raw integer."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    if hasattr(x, "ctypes"):
+        return int(x.ctypes.data)
+    raise TypeError(f"cannot take the address of {type(x).__name__}")
+
+
+def _nbytes(x) -> int:
+    if hasattr(x, "untyped_storage"):
+        return int(x.numel() * x.element_size())
+    return int(x.nbytes)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
+def make_desc(**fields) -> AttnDecodeDesc:
+    """An attn_decode_desc from keyword fields (missing integer fields are 0)."""
+    d = AttnDecodeDesc()
+    for k, v in fields.items():
+        setattr(d, k, v)
+    return d
+
+
+def attn_decode_status_string(status: int) -> str:
+    return _lib.attn_decode_status_string(int(status)).decode()
+
+
+def attn_decode_plan(desc: AttnDecodeDesc, seq_lens_host) -> AttnDecodePlan:
+    """Validate and plan; ``seq_lens_host`` is a host int32 array (numpy) of length batch."""
+    import numpy as np
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    plan = AttnDecodePlan()
+    rc = _lib.attn_decode_plan(ctypes.byref(desc), lens.ctypes.data, ctypes.byref(plan))
+    if rc != 0:
+        raise AttnDecodeError("attn_decode_plan", rc)
+    return plan
+
+
+def attn_decode_split(plan: AttnDecodePlan, q, kv_pool, page_table, seq_lens, workspace,
+                      workspace_bytes=None, stream=None) -> None:
+    nbytes = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    rc = _lib.attn_decode_split(ctypes.byref(plan), _ptr(q), _ptr(kv_pool), _ptr(page_table),
+                                _ptr(seq_lens), _ptr(workspace), nbytes, _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_decode_split", rc)
+
+
+def attn_decode_merge(plan: AttnDecodePlan, workspace, out, workspace_bytes=None,
+                      stream=None) -> None:
+    nbytes = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    rc = _lib.attn_decode_merge(ctypes.byref(plan), _ptr(workspace), nbytes, _ptr(out),
+                                _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_decode_merge", rc)

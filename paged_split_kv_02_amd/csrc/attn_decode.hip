@@ -1,0 +1,482 @@
+// Paged split-KV decode attention for gfx950 (MI355X): partial and merge kernels
+// and the C-ABI entry points that launch them.
+//
+// Partial kernel (one wave = one key chunk of one (request, KV head)):
+//   * the G query heads of a KV head share every K/V byte the wave streams; each
+//     row is fetched from HBM once (gem design note, "Candidate ownership and
+//     storage": stage each K row once for the eight query heads);
+//   * the page id is resolved once per 16-key tile, never per key (TensorFold
+//     PR #1619, review thread: per-tile lookup instead of per-key);
+//   * QK^T and PV run on MFMA.  The 16 output columns of a 16x16 MFMA hold the G
+//     heads twice: a high and a low bf16 part of the fp32 query (and of the fp32
+//     probabilities), so the products keep ~16 mantissa bits while the inputs
+//     stay bf16, and no column is padding when G = 8;
+//   * online softmax in base 2 with scale*log2(e) folded into the query; the
+//     stored maxima are converted back to natural-log units;
+//   * masked keys (past L, before the window, padding slots of the last page)
+//     are excluded by select, and their V rows are zeroed before PV, so NaN or
+//     huge padding never reaches the sums.
+// Merge (one launch): level 1 folds runs of consecutive chunk states into group
+// states held in LDS, out of place; level 2 folds the group states in order and
+// divides (pegainfer PR #1055, "Description": merge in two levels; gem design note,
+// "Candidate ownership and storage" for the identity).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "plan_internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+struct SplitArgs {
+  const float* q;
+  const uint16_t* pool;
+  const int32_t* table;
+  const int32_t* seq_lens;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
+  int32_t num_q_heads, page_size, max_pages, window, chunk_len, num_chunks;
+  float qscale;  // scale * log2(e)
+};
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Streaming 16-byte load that does not keep the line in the caches.
+__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Per-wave LDS tile: the 16 stored rows of one key tile, padded by 16 bytes per
+// row.  Staging writes (one row, 16 consecutive 16-byte pieces per 16-lane pass)
+// and the QK reads (16 rows, one column per pass) both fall in distinct banks.
+template <int COLS>
+struct alignas(16) RowTile {
+  static constexpr int kPitch = COLS + 8;  // elements
+  uint16_t v[kTile * kPitch];
+};
+
+template <int D, int G, bool FOLDED>
+__global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
+  constexpr int KSTEPS = D / 32;    // 16x16x32 MFMA steps over the key dimension
+  constexpr int VGROUPS = D / 128;  // 128-dim slabs of V per tile
+  constexpr int ROT = FOLDED ? 128 : 0;
+  // Columns staged per row: split K | V (2D), folded rotated K | V (ROT + D).
+  constexpr int COLS = FOLDED ? ROT + D : 2 * D;
+  constexpr int SLABS = COLS / 128;  // 256-byte pieces per row
+  constexpr int P = RowTile<COLS>::kPitch;
+  // Staged-tile columns of the K part and of V.
+  constexpr int TK = 0;
+  constexpr int TV = FOLDED ? ROT : D;
+  static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
+  __shared__ RowTile<COLS> tiles[kWavesPerBlock];
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;   // MFMA row/column index inside a 16-block
+  const int qg = lane >> 4;  // lane group: selects k sub-range / output rows
+  const int wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x * kWavesPerBlock + wave;
+  const int g = blockIdx.y;
+  const int r = blockIdx.z;
+  if (chunk >= a.num_chunks) return;
+  uint16_t* tile = tiles[wave].v;
+
+  const int L = a.seq_lens[r];
+  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int start = lo & ~(kTile - 1);
+  const int64_t cap = int64_t(a.max_pages) * a.page_size;
+  bool poison = L < 1 || int64_t(L) > cap ||
+                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
+  const int c0 = start + chunk * a.chunk_len;
+  const int c1 = min(c0 + a.chunk_len, L);
+
+  // Query operand: column c holds head (c % G), high part for c < G, low part for
+  // G <= c < 2G, zero beyond.  Dims of k-step j for lane group qg: 32j + 8qg + [0, 8).
+  const int part = c / G;
+  const int hq = g * G + (c % G);
+  bf16x8 qop[KSTEPS];
+  {
+    const float* qrow = a.q + (int64_t(r) * a.num_q_heads + hq) * D;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      bf16x8 v;
+      if (part < 2) {
+        const floatx4 x0 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg);
+        const floatx4 x1 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * a.qscale;
+          const __bf16 h = (__bf16)x;
+          v[e] = part == 0 ? h : (__bf16)(x - (float)h);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qop[j] = v;
+    }
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  floatx4 acc[VGROUPS][8];
+#pragma unroll
+  for (int b = 0; b < VGROUPS; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (!poison && c0 < c1) {
+    const int32_t* trow = a.table + int64_t(r) * a.max_pages;
+    const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
+    u32x4 stage[4][SLABS];
+
+    // Resolve the tile's page once; false if the table entry is outside the pool.
+    auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
+      const int32_t pid = trow[tok0 / a.page_size];
+      if (pid < 0 || int64_t(pid) >= a.num_pages) return false;
+      *base = head_base + int64_t(pid) * a.page_stride + int64_t(tok0 % a.page_size) * a.row_stride;
+      return true;
+    };
+    // Column of staged piece sb (128 elements each) in the stored row.
+    auto src_col = [&](int sb) -> int64_t {
+      if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
+      return sb < VGROUPS ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VGROUPS);
+    };
+    // Lane (c, qg) fetches rows 4qg + e, 16 bytes at 128 sb + 8c: every instruction
+    // reads four whole 256-byte row pieces, so each line is requested once.
+    auto load_tile = [&](const uint16_t* base) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t* row = base + int64_t(4 * qg + e) * a.row_stride + 8 * c;
+#pragma unroll
+        for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col(sb));
+      }
+    };
+
+    int tok0 = c0;
+    const uint16_t* base;
+    if (!tile_base(tok0, &base)) {
+      poison = true;
+    } else {
+      load_tile(base);
+      for (;;) {
+        const int next = tok0 + kTile;
+        bool has_next = next < c1;
+        const uint16_t* nbase = nullptr;
+        if (has_next && !tile_base(next, &nbase)) {
+          poison = true;
+          has_next = false;
+        }
+        // Stage the tile (V rows of masked keys zeroed, so padding cannot leak
+        // through 0 * NaN), then start fetching the next one.
+        const bool partial_tile = tok0 < lo || tok0 + kTile > L;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = tok0 + 4 * qg + e;
+          const bool dead = partial_tile && (t < lo || t >= L);
+#pragma unroll
+          for (int sb = 0; sb < SLABS; ++sb) {
+            u32x4 w = stage[e][sb];
+            if (dead && 128 * sb >= TV) w = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = w;
+          }
+        }
+        if (has_next) load_tile(nbase);
+
+        // Scores of 16 keys x 16 columns (hi/lo parts of the G heads).  Key dim kd
+        // sits at staged column kd (split / rotated part) or TV + kd (folded, kd >= ROT).
+        floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j) {
+          const int kd = 32 * j + 8 * qg;
+          const int col = (FOLDED && kd >= ROT) ? TV + kd : TK + kd;
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(tile + c * P + col);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[j], s, 0,
+                                                      0, 0);
+        }
+
+        // Online softmax over this tile (base 2); lane holds keys tok0 + 4qg + i.
+        float sc[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float full = s[i] + shfl_xor(s[i], G);
+          const int t = tok0 + 4 * qg + i;
+          sc[i] = (t >= lo && t < L) ? full : -INFINITY;
+          mx = fmaxf(mx, sc[i]);
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        float alpha = 1.0f;
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (m_new != -INFINITY) {
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+        }
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m_run = m_new;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int b = 0; b < VGROUPS; ++b)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
+        }
+        bf16x4 pop;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 h = (__bf16)p[i];
+          const __bf16 l = (__bf16)(p[i] - (float)h);
+          pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
+        }
+
+        // PV: lane row c of slab b, step jj <-> dim 128b + 8c + jj; keys 4qg + [0, 4).
+#pragma unroll
+        for (int b = 0; b < VGROUPS; ++b) {
+          u32x4 w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = *reinterpret_cast<const u32x4*>(tile + (4 * qg + e) * P + TV + 128 * b + 8 * c);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const u32x2 even = {perm(w[1][u], w[0][u], 0x05040100u), perm(w[3][u], w[2][u], 0x05040100u)};
+            const u32x2 odd = {perm(w[1][u], w[0][u], 0x07060302u), perm(w[3][u], w[2][u], 0x07060302u)};
+            acc[b][2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(bf16x4, even), pop, acc[b][2 * u], 0, 0, 0);
+            acc[b][2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(bf16x4, odd), pop, acc[b][2 * u + 1], 0, 0, 0);
+          }
+        }
+        if (!has_next) break;
+        tok0 = next;
+      }
+    }
+  }
+
+  // Chunk state: sum l over the lane groups, add the low columns onto the high ones.
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+#pragma unroll
+  for (int b = 0; b < VGROUPS; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][jj][i] += shfl_xor(acc[b][jj][i], G);
+
+  if (c < G) {
+    const int64_t st = (int64_t(r) * a.num_q_heads + hq) * a.num_chunks + chunk;
+    const float qnan = __builtin_nanf("");
+    if (qg == 0) {
+      a.part_m[st] = poison ? qnan : (m_run == -INFINITY ? -INFINITY : m_run * kLn2);
+      a.part_l[st] = poison ? qnan : l_run;
+    }
+    float* o = a.part_o + st * D;
+#pragma unroll
+    for (int b = 0; b < VGROUPS; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        floatx4 w0 = {acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+        floatx4 w1 = {acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
+        if (poison) w0 = w1 = floatx4{qnan, qnan, qnan, qnan};
+        float* dst = o + 128 * b + 32 * qg + 8 * i;
+        *reinterpret_cast<floatx4*>(dst) = w0;
+        *reinterpret_cast<floatx4*>(dst + 4) = w1;
+      }
+  }
+}
+
+struct MergeArgs {
+  const float* part_m;
+  const float* part_l;
+  const float* part_o;
+  float* out;
+  int32_t n;      // chunk states per (request, head)
+  int32_t group;  // consecutive chunk states folded by one level-1 group
+};
+
+// Fold states [k0, k1) of one (request, head) over 4 dims: the maximum first, then
+// every state weighted by e^(m_k - M) (0 for an empty state) in ascending k.
+// Returns false if a maximum is NaN (a poisoned chunk).
+__device__ __forceinline__ bool fold_states(const float* m, const float* l, const float* o,
+                                            int64_t stride, int k0, int k1, float& M, float& S,
+                                            floatx4& O) {
+  M = -INFINITY;
+  bool nan = false;
+  for (int k = k0; k < k1; ++k) {
+    const float x = m[k];
+    nan |= x != x;
+    M = fmaxf(M, x);
+  }
+  S = 0.0f;
+  O = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (nan || M == -INFINITY) return !nan;
+  int k = k0;
+  for (; k + 4 <= k1; k += 4) {  // four independent loads in flight
+    floatx4 v[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = *reinterpret_cast<const floatx4*>(o + int64_t(k + u) * stride);
+      const float x = m[k + u];
+      w[u] = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      S += w[u] * l[k + u];
+      O += w[u] * v[u];
+    }
+  }
+  for (; k < k1; ++k) {
+    const float x = m[k];
+    const float w = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
+    S += w * l[k];
+    O += w * *reinterpret_cast<const floatx4*>(o + int64_t(k) * stride);
+  }
+  return true;
+}
+
+// One workgroup per (128-dim slab, request*head).  Level 1: thread group gi (32
+// threads, 4 dims each) folds chunk states [gi*group, (gi+1)*group) into a group
+// state kept in LDS (out of place: chunk states are only read).  Level 2: group 0
+// folds the group states in ascending order and writes O / S.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  __shared__ float sm[kMergeGroups], sl[kMergeGroups];
+  __shared__ floatx4 so[kMergeGroups][32];
+  const int t = threadIdx.x;
+  const int gi = t >> 5;
+  const int d4 = t & 31;
+  const int64_t bh = blockIdx.y;
+  const int dim = blockIdx.x * 128 + 4 * d4;
+  const float qnan = __builtin_nanf("");
+
+  float M, S;
+  floatx4 O;
+  const int k0 = gi * a.group;
+  const int k1 = min(k0 + a.group, a.n);
+  if (!fold_states(a.part_m + bh * a.n, a.part_l + bh * a.n, a.part_o + bh * a.n * D + dim, D, k0,
+                   k1, M, S, O)) {
+    M = S = qnan;
+    O = floatx4{qnan, qnan, qnan, qnan};
+  }
+  if (d4 == 0) {
+    sm[gi] = M;
+    sl[gi] = S;
+  }
+  so[gi][d4] = O;
+  __syncthreads();
+  if (gi == 0) {
+    float M2, S2;
+    floatx4 O2;
+    if (!fold_states(sm, sl, reinterpret_cast<const float*>(&so[0][d4]), 32 * 4, 0, kMergeGroups,
+                     M2, S2, O2)) {
+      S2 = qnan;
+      O2 = floatx4{qnan, qnan, qnan, qnan};
+    }
+    *reinterpret_cast<floatx4*>(a.out + bh * D + dim) = O2 / S2;
+  }
+}
+
+template <int D, int G, bool FOLDED>
+void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
+                     args);
+}
+
+template <int D>
+void launch_merge(const attn_decode_plan_t& p, char* ws, float* out, hipStream_t s) {
+  const int64_t bh = int64_t(p.desc.batch) * p.desc.num_q_heads;
+  MergeArgs m{reinterpret_cast<const float*>(ws + p.off_part_m),
+              reinterpret_cast<const float*>(ws + p.off_part_l),
+              reinterpret_cast<const float*>(ws + p.off_part_o), out, p.num_chunks, p.merge_group};
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(D / 128, bh), dim3(256), 0, s, m);
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  using namespace attn;
+  int rc = check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (!q || !kv_pool || !page_table || !seq_lens) return ATTN_E_INVALID_ARG;
+  rc = check_workspace(plan, workspace, workspace_bytes);
+  if (rc != ATTN_OK) return rc;
+  const attn_decode_desc& d = plan->desc;
+  if (!shape_supported(d)) return ATTN_E_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  SplitArgs args;
+  args.q = q;
+  args.pool = static_cast<const uint16_t*>(kv_pool);
+  args.table = page_table;
+  args.seq_lens = seq_lens;
+  args.part_m = reinterpret_cast<float*>(ws + plan->off_part_m);
+  args.part_l = reinterpret_cast<float*>(ws + plan->off_part_l);
+  args.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
+  args.page_stride = d.page_stride;
+  args.head_stride = d.head_stride;
+  args.row_stride = d.row_stride;
+  args.k_offset = d.k_offset;
+  args.v_offset = d.v_offset;
+  args.num_pages = d.num_pages;
+  args.num_q_heads = d.num_q_heads;
+  args.page_size = d.page_size;
+  args.max_pages = d.max_pages_per_seq;
+  args.window = d.window;
+  args.chunk_len = plan->chunk_len;
+  args.num_chunks = plan->num_chunks;
+  args.qscale = d.scale * kLog2e;
+
+  const dim3 grid((plan->num_chunks + kWavesPerBlock - 1) / kWavesPerBlock, d.num_kv_heads, d.batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
+    launch_split<512, 8, false>(args, grid, s);
+  else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
+    launch_split<512, 8, true>(args, grid, s);
+  else
+    launch_split<256, 2, false>(args, grid, s);
+  return launch_status();
+}
+
+extern "C" int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+  using namespace attn;
+  int rc = check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (!out) return ATTN_E_INVALID_ARG;
+  rc = check_workspace(plan, workspace, workspace_bytes);
+  if (rc != ATTN_OK) return rc;
+  if (!shape_supported(plan->desc)) return ATTN_E_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (plan->desc.head_dim == 512)
+    launch_merge<512>(*plan, static_cast<char*>(workspace), out, s);
+  else
+    launch_merge<256>(*plan, static_cast<char*>(workspace), out, s);
+  return launch_status();
+}

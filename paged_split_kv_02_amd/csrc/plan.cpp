@@ -1,0 +1,188 @@
+// Host-side planning for paged split-KV decode attention: validation, chunking
+// and the workspace layout.  No device call is made here, so the plan can be
+// built (and tested) on a machine without a GPU.
+#include "plan_internal.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+bool align_up(uint64_t v, uint64_t* out) {
+  uint64_t t;
+  if (!add_ok(v, kAlign - 1, &t)) return false;
+  *out = t / kAlign * kAlign;
+  return true;
+}
+
+// Place a float32 region of `count` elements at *cursor (aligned), advance the cursor.
+bool place(uint64_t* cursor, uint64_t count, uint64_t* offset) {
+  uint64_t bytes, start, end;
+  if (!mul_ok(count, 4, &bytes)) return false;
+  if (!align_up(*cursor, &start)) return false;
+  if (!add_ok(start, bytes, &end)) return false;
+  *offset = start;
+  *cursor = end;
+  return true;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+namespace attn {
+
+bool shape_supported(const attn_decode_desc& d) {
+  const int g = d.num_q_heads / d.num_kv_heads;
+  if (d.head_dim == 512 && g == 8) {
+    if (d.format == ATTN_KV_SPLIT) return d.rot_cols == 0;
+    if (d.format == ATTN_KV_FOLDED) return d.rot_cols == 128;
+    return false;
+  }
+  if (d.head_dim == 256 && g == 2) return d.format == ATTN_KV_SPLIT && d.rot_cols == 0;
+  return false;
+}
+
+// Last column (exclusive) a row read touches.
+int64_t row_extent(const attn_decode_desc& d) {
+  int64_t k_end = d.k_offset + (d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim);
+  int64_t v_end = d.v_offset + d.head_dim;
+  return k_end > v_end ? k_end : v_end;
+}
+
+int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan) {
+  if (!desc || !lens || !plan) return ATTN_E_INVALID_ARG;
+  const attn_decode_desc& d = *desc;
+  if (d.batch < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.head_dim < 1 ||
+      d.page_size < 1 || d.max_pages_per_seq < 1 || d.window < 0 || d.num_chunks < 0 ||
+      d.merge_group < 0 || d.num_pages < 1)
+    return ATTN_E_INVALID_ARG;
+  if (d.num_q_heads % d.num_kv_heads != 0) return ATTN_E_UNSUPPORTED;
+  if (d.format != ATTN_KV_SPLIT && d.format != ATTN_KV_FOLDED) return ATTN_E_INVALID_ARG;
+  if (!shape_supported(d)) return ATTN_E_UNSUPPORTED;
+  if (!std::isfinite(d.scale)) return ATTN_E_INVALID_ARG;
+  if (d.page_size % kTile != 0) return ATTN_E_UNSUPPORTED;
+
+  // Layout: 16-byte aligned rows and columns, non-negative strides, rows inside their page.
+  const int64_t v[] = {d.page_stride, d.head_stride, d.row_stride, d.k_offset, d.v_offset};
+  for (int64_t x : v)
+    if (x < 0 || x % 8 != 0) return ATTN_E_INVALID_ARG;
+  {
+    uint64_t a, b, c, e;
+    if (!mul_ok(uint64_t(d.num_kv_heads - 1), uint64_t(d.head_stride), &a) ||
+        !mul_ok(uint64_t(d.page_size - 1), uint64_t(d.row_stride), &b) || !add_ok(a, b, &c) ||
+        !add_ok(c, uint64_t(row_extent(d)), &e))
+      return ATTN_E_OVERFLOW;
+    if (e > uint64_t(d.page_stride)) return ATTN_E_INVALID_ARG;
+    uint64_t pool_elems;
+    if (!mul_ok(uint64_t(d.num_pages), uint64_t(d.page_stride), &pool_elems) ||
+        pool_elems > (uint64_t(1) << 62))
+      return ATTN_E_OVERFLOW;
+  }
+
+  // Lengths: 1 <= L <= pages in a table row * page size.
+  const int64_t cap = int64_t(d.max_pages_per_seq) * d.page_size;
+  int64_t max_span = 0;
+  for (int r = 0; r < d.batch; ++r) {
+    const int64_t L = lens[r];
+    if (L < 1) return ATTN_E_INVALID_ARG;
+    if (L > cap) return ATTN_E_PAST_PAGES;
+    const int64_t lo = d.window > 0 && L > d.window ? L - d.window : 0;
+    const int64_t start = lo / kTile * kTile;
+    if (L - start > max_span) max_span = L - start;
+  }
+  if (max_span > INT32_MAX) return ATTN_E_OVERFLOW;
+
+  // Chunking: enough waves to give every SIMD of the chip one chunk, never a
+  // chunk shorter than a tile; an explicit count is honoured (trailing chunks
+  // may then be empty).
+  const int64_t tiles = ceil_div(max_span, kTile);
+  int64_t n = d.num_chunks;
+  if (n == 0) {
+    const int64_t units = int64_t(d.batch) * d.num_kv_heads;
+    n = ceil_div(kTargetWaves, units);
+    if (n > tiles) n = tiles;
+    if (n < 1) n = 1;
+  }
+  if (n > (int64_t(1) << 24)) return ATTN_E_OVERFLOW;
+  const int64_t chunk_tiles = ceil_div(tiles, n);
+  const int64_t chunk_len = chunk_tiles * kTile;
+  if (d.num_chunks == 0) n = ceil_div(max_span, chunk_len);
+
+  // Level-1 groups: at most kMergeGroups per (request, head), so the merge's second
+  // level fits one workgroup.
+  const int64_t gm_min = ceil_div(n, kMergeGroups);
+  int64_t gm = d.merge_group == 0 ? gm_min : d.merge_group;
+  if (gm < gm_min) return ATTN_E_UNSUPPORTED;
+  if (gm > n) gm = n;
+  const int64_t ng = ceil_div(n, gm);
+
+  // Grid limits: blocks along x carry chunk quads, y the KV heads, z the requests.
+  if (ceil_div(n, kWavesPerBlock) > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535 ||
+      d.num_q_heads > 65535)
+    return ATTN_E_OVERFLOW;
+
+  attn_decode_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  p.magic = kPlanMagic;
+  p.desc = d;
+  p.group_size = d.num_q_heads / d.num_kv_heads;
+  p.tile = kTile;
+  p.chunk_len = int32_t(chunk_len);
+  p.num_chunks = int32_t(n);
+  p.merge_group = int32_t(gm);
+  p.num_groups = int32_t(ng);
+  p.max_span = int32_t(max_span);
+
+  uint64_t bh, states, elems;
+  if (!mul_ok(uint64_t(d.batch), uint64_t(d.num_q_heads), &bh) ||
+      !mul_ok(bh, uint64_t(n), &states) || !mul_ok(states, uint64_t(d.head_dim), &elems))
+    return ATTN_E_OVERFLOW;
+  if (bh > 65535) return ATTN_E_OVERFLOW;  // merge grid rows
+  uint64_t cur = 0;
+  if (!place(&cur, states, &p.off_part_m) || !place(&cur, states, &p.off_part_l) ||
+      !place(&cur, elems, &p.off_part_o) || !align_up(cur, &p.workspace_bytes))
+    return ATTN_E_OVERFLOW;
+
+  *plan = p;
+  return ATTN_OK;
+}
+
+int check_plan(const attn_decode_plan_t* plan) {
+  if (!plan) return ATTN_E_INVALID_ARG;
+  if (plan->magic != kPlanMagic) return ATTN_E_PLAN;
+  return ATTN_OK;
+}
+
+int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes) {
+  if (!ws) return ATTN_E_INVALID_ARG;
+  if (bytes < plan->workspace_bytes) return ATTN_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return ATTN_E_WORKSPACE;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
+extern "C" int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
+                                attn_decode_plan_t* plan) {
+  return attn::make_plan(desc, seq_lens_host, plan);
+}
+
+extern "C" const char* attn_decode_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_INVALID_ARG: return "invalid argument";
+    case ATTN_E_UNSUPPORTED: return "unsupported shape";
+    case ATTN_E_PAST_PAGES: return "length past the pages of a table row";
+    case ATTN_E_OVERFLOW: return "size overflow";
+    case ATTN_E_WORKSPACE: return "workspace too small or misaligned";
+    case ATTN_E_PLAN: return "not a plan made by attn_decode_plan";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}

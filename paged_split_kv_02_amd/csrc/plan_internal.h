@@ -1,0 +1,22 @@
+// Internal constants and helpers shared by the host plan and the launchers.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/attn_decode.h"
+
+namespace attn {
+
+constexpr uint64_t kPlanMagic = 0x5041474544534b56ull;  // "PAGEDSKV"
+constexpr int kTile = 16;            // keys per tile = rows of one 16x16 MFMA block
+constexpr int kWavesPerBlock = 4;    // one chunk per wave, four waves per workgroup
+constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
+constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
+
+bool shape_supported(const attn_decode_desc& d);
+int64_t row_extent(const attn_decode_desc& d);
+int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan);
+int check_plan(const attn_decode_plan_t* plan);
+int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
+
+}  // namespace attn

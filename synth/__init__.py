@@ -79,6 +79,17 @@ class Workload:
         lo = max(0, L - self.window) if self.window > 0 else 0
         return lo, L
 
+    def desc_fields(self, num_chunks: int = 0, merge_group: int = 0) -> dict:
+        """The pool/batch description as plain fields (names of the C descriptor)."""
+        return dict(batch=self.batch, num_q_heads=self.num_q_heads,
+                    num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
+                    format=0 if self.fmt == SPLIT else 1, rot_cols=self.rot_cols,
+                    page_size=self.page_size, max_pages_per_seq=self.max_pages,
+                    window=self.window, num_chunks=num_chunks, merge_group=merge_group,
+                    scale=self.scale, num_pages=self.num_pages, page_stride=self.page_stride,
+                    head_stride=self.head_stride, row_stride=self.row_stride,
+                    k_offset=self.k_offset, v_offset=self.v_offset)
+
     def kv_bytes(self) -> int:
         """Bytes of K/V rows a decode step must stream (visible keys only)."""
         n = sum(self.visible(r)[1] - self.visible(r)[0] for r in range(self.batch))

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar (the decode gate of pegainfer PR #1055, Verification, taken against fp64):
+max |GPU - oracle| <= 2e-3 for bf16 KV; plus NMSE <= 1e-4 and correlation
+>= 0.9999 (gem design note, "Fail-closed evidence"), and a relative bar of
+1e-3 x max|o| that still bites at 163K context, where |o| is only ~4e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_harness import Device, compare, fnv1a, note
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+REL = 1e-3
+
+
+def check(got, ref, what):
+    st = compare(got, ref)
+    note(f"  {what}: max|d|={st['max_abs']:.3e} max|o|={st['max_ref']:.3e} "
+         f"nmse={st['nmse']:.3e} corr={st['corr']:.9f}")
+    assert st["finite"], what
+    assert st["max_abs"] <= TOL, (what, st)
+    assert st["max_abs"] <= REL * st["max_ref"], (what, st)
+    assert st["nmse"] <= 1e-4 and st["corr"] >= 0.9999, (what, st)
+    return st
+
+
+def run_case(wl, what, **kw):
+    note(f"[gpu] {what}")
+    dev = Device(wl, **kw)
+    got = dev.run()
+    assert dev.guards_intact(), f"{what}: wrote outside out / workspace"
+    return dev, got
+
+
+def test_tiny_ref_eight_chunks():
+    wl = synth.tiny_ref(seed=0)
+    dev, got = run_case(wl, "tiny ref L=1024 n=8", num_chunks=8)
+    assert dev.plan.num_chunks == 8 and dev.plan.chunk_len == 128
+    check(got, oracle.decode_attention(wl), "tiny")
+
+
+def test_partials_match_oracle_per_chunk():
+    wl = synth.make_workload([1000, 333], **synth.GLOBAL, seed=5, spare_pages=2)
+    dev, got = run_case(wl, "partials L=1000,333 n=9", num_chunks=9, merge_group=4)
+    m, l, o = dev.partials()
+    G = wl.group_size
+    for r in range(wl.batch):
+        ranges = dev.chunk_ranges(r)
+        for g in range(wl.num_kv_heads):
+            states = oracle.paged_partials(wl, r, g, ranges)
+            for i in range(G):
+                h = g * G + i
+                for c, st in enumerate(states[i]):
+                    if st.m == -math.inf:
+                        assert m[r, h, c] == -np.inf and l[r, h, c] == 0 and not np.any(o[r, h, c]), (r, h, c)
+                        continue
+                    assert abs(m[r, h, c] - st.m) <= 1e-5 * max(1.0, abs(st.m)), (r, h, c, m[r, h, c], st.m)
+                    assert abs(l[r, h, c] - st.l) <= 1e-5 * st.l, (r, h, c)
+                    d = np.max(np.abs(o[r, h, c] / l[r, h, c] - st.acc / st.l))
+                    assert d <= 1e-4, (r, h, c, d)
+    check(got, oracle.decode_attention(wl), "partials case")
+
+
+def test_repeat_runs_bit_identical():
+    wl = synth.global_decode(10602, seed=1)
+    note("[gpu] repeat x10 L=10602")
+    dev = Device(wl)
+    prints = set()
+    for _ in range(10):
+        dev.step()
+        torch.cuda.synchronize()
+        prints.add(fnv1a(dev.result()))
+    assert len(prints) == 1, prints
+
+
+def test_page_permutation_and_layout_bit_identical():
+    outs = []
+    for ts, layout in ((1, synth.HEAD_MAJOR), (2, synth.HEAD_MAJOR), (3, synth.TOKEN_MAJOR)):
+        wl = synth.make_workload([2000, 777], **synth.GLOBAL, seed=6, table_seed=ts, layout=layout)
+        _, got = run_case(wl, f"permutation table_seed={ts} {layout}")
+        outs.append(got)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_single_token_is_v0_exactly(fmt):
+    wl = synth.make_workload([1, 1], **synth.GLOBAL, seed=7, fmt=fmt)
+    _, got = run_case(wl, f"L=1 {fmt}")
+    for r in range(2):
+        for g in range(4):
+            v0 = oracle.gather_rows(wl, r, g, np.array([0]))[0][wl.v_offset:wl.v_offset + 512]
+            v0 = (v0.astype(np.uint32) << 16).view(np.float32)
+            for h in range(8 * g, 8 * g + 8):
+                assert np.array_equal(got[r, h].view(np.uint32), v0.view(np.uint32)), (r, h)
+
+
+@pytest.mark.parametrize("L,n", [(100, 16), (17, 4), (1024, 64), (300, 3)])
+def test_empty_and_ragged_partitions(L, n):
+    wl = synth.make_workload([L], **synth.GLOBAL, seed=8, pad="big")
+    dev, got = run_case(wl, f"empty partitions L={L} n={n}", num_chunks=n)
+    check(got, oracle.decode_attention(wl), f"L={L} n={n}")
+
+
+@pytest.mark.parametrize("pad", ["nan", "big"])
+def test_hostile_padding(pad):
+    """Slots past L in the last page, spare pages: NaN or 1e30 must not leak."""
+    wl = synth.make_workload([1000, 257, 16], **synth.GLOBAL, seed=9, pad=pad, spare_pages=3)
+    _, got = run_case(wl, f"hostile padding {pad}")
+    check(got, oracle.decode_attention(wl), f"pad {pad}")
+
+
+@pytest.mark.parametrize("L", [10602, 40002])
+def test_global_lengths_auto_chunks(L):
+    wl = synth.global_decode(L, seed=1)
+    _, got = run_case(wl, f"global split L={L} auto")
+    check(got, oracle.decode_attention(wl), f"L={L}")
+
+
+@pytest.mark.parametrize("n", [16, 32, 64])
+def test_global_10602_chunk_counts(n):
+    wl = synth.global_decode(10602, seed=1)
+    _, got = run_case(wl, f"global split L=10602 n={n}", num_chunks=n)
+    check(got, oracle.decode_attention(wl), f"n={n}")
+
+
+def test_folded_matches_oracle():
+    wl = synth.global_decode(10602, seed=3, fmt="folded")
+    _, got = run_case(wl, "folded L=10602")
+    check(got, oracle.decode_attention(wl), "folded")
+
+
+def test_folded_equals_split_with_power_of_two_weights():
+    """With w in {1/2, 1, 2}, K[128:] = w V[128:] is exact in bf16 and q' = q w is exact in
+    fp32, so the folded and split rows give the same MFMA products: identical bits."""
+    wl = synth.make_workload([3000], **synth.GLOBAL, seed=10, fmt="folded")
+    rng = np.random.default_rng(10)
+    wl.fold_w = rng.choice(np.array([0.5, 1.0, 2.0], dtype=np.float32), size=384)
+    wl.q = wl.q_unfolded.copy()
+    wl.q[:, :, 128:] = wl.q_unfolded[:, :, 128:] * wl.fold_w
+    split = synth.split_pair_of_folded(wl)
+    _, got_f = run_case(wl, "folded pow2 w")
+    _, got_s = run_case(split, "split pair pow2 w")
+    assert np.array_equal(got_f.view(np.uint32), got_s.view(np.uint32))
+    check(got_f, oracle.decode_attention(wl), "folded pow2")
+
+
+def test_needle():
+    wl = synth.make_workload([5000], **synth.GLOBAL, seed=11)
+    # key 3210 of KV head 1 aligned with query head 9: a peaked softmax for that head
+    q = wl.q[0, 9].astype(np.float64)
+    k = q / np.linalg.norm(q) * 60.0
+    pos = 3210
+    rows = oracle.row_view(wl)
+    page = wl.table[0][pos // 256]
+    flat = (page * wl.page_stride + 1 * wl.head_stride + (pos % 256) * wl.row_stride)
+    wl.pool[flat:flat + 512] = synth.f32_to_bf16_bits(k.astype(np.float32))
+    del rows
+    _, got = run_case(wl, "needle")
+    ref = oracle.decode_attention(wl)
+    check(got, ref, "needle")
+    vneedle = oracle.bf16_bits_to_f64(wl.pool[flat + 512:flat + 1024])
+    assert np.max(np.abs(got[0, 9] - vneedle)) < 1e-2
+
+
+@pytest.mark.parametrize("L", [1, 528, 1023, 1024, 1025, 1040, 1088, 4096])
+def test_window_lengths(L):
+    """hd256 sliding decode at residencies around the window (pegainfer PR #1057,
+    Verification: 1040 / 1024 / 528 / 1)."""
+    wl = synth.make_workload([L], **synth.SLIDING, seed=12, pad="nan", max_pages=64)
+    _, got = run_case(wl, f"window L={L}")
+    check(got, oracle.decode_attention(wl), f"window L={L}")
+
+
+def test_sliding_ragged_batch():
+    wl = synth.sliding_batch(seed=4, pad="nan")
+    _, got = run_case(wl, f"sliding batch lens={wl.seq_lens.tolist()}")
+    check(got, oracle.decode_attention(wl), "sliding batch")
+
+
+def test_bad_page_id_poisons_only_its_request():
+    """A table entry outside the pool is not read: that request's output is NaN, the
+    others are unaffected (forced from the host; every kernel exits normally)."""
+    wl = synth.make_workload([600, 600], **synth.GLOBAL, seed=13)
+    wl.table[1][1] = wl.num_pages + 100
+    _, got = run_case(wl, "bad page id")
+    assert np.all(np.isnan(got[1]))
+    wl.table[1][1] = wl.table[0][1]  # any valid page: request 0 is independent of it
+    check(got[:1], oracle.decode_attention(wl)[:1], "healthy request")
+
+
+def test_device_length_past_plan_poisons():
+    wl = synth.make_workload([600, 300], **synth.GLOBAL, seed=14)
+    note("[gpu] device length past the plan")
+    dev = Device(wl, seq_lens_dev=[600, 5000])
+    got = dev.run()
+    assert dev.guards_intact()
+    assert np.all(np.isnan(got[1]))
+    check(got[:1], oracle.decode_attention(wl)[:1], "request 0")

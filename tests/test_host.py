@@ -1,0 +1,226 @@
+"""Host-side checks of the C-ABI library (no GPU needed): exported symbols, struct
+layout against the header, plan refusals, chunking and the workspace contract."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_split_kv_02_amd as K
+from tests.golden.read import load as load_golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_decode_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(K.SYMBOLS), names
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(attn_decode_\w+)$", out, re.M))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = [f for f, _ in K.AttnDecodeDesc._fields_]
+    pfields = [f for f, _ in K.AttnDecodePlan._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
+           'printf("%zu %zu\\n", sizeof(attn_decode_desc), sizeof(attn_decode_plan_t));']
+    src += [f'printf("%zu\\n", offsetof(attn_decode_desc, {f}));' for f in fields]
+    src += [f'printf("%zu\\n", offsetof(attn_decode_plan_t, {f}));' for f in pfields]
+    src += ["return 0;}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(c)], check=True)
+    vals = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    assert int(vals[0]) == ctypes.sizeof(K.AttnDecodeDesc)
+    assert int(vals[1]) == ctypes.sizeof(K.AttnDecodePlan)
+    offs = [int(v) for v in vals[2:]]
+    assert offs[:len(fields)] == [getattr(K.AttnDecodeDesc, f).offset for f in fields]
+    assert offs[len(fields):] == [getattr(K.AttnDecodePlan, f).offset for f in pfields]
+
+
+def global_desc(L=1024, **kw):
+    ps, hkv, cols = 256, 4, 1024
+    pages = (L + ps - 1) // ps
+    f = dict(batch=1, num_q_heads=32, num_kv_heads=hkv, head_dim=512, format=0, rot_cols=0,
+             page_size=ps, max_pages_per_seq=pages, window=0, num_chunks=0, merge_group=0,
+             scale=1 / math.sqrt(512), num_pages=pages + 4, page_stride=hkv * ps * cols,
+             head_stride=ps * cols, row_stride=cols, k_offset=0, v_offset=512)
+    f.update(kw)
+    return f
+
+
+def plan_status(lens, **fields):
+    d = K.make_desc(**fields)
+    p = K.AttnDecodePlan()
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    return K._lib.attn_decode_plan(ctypes.byref(d), lens.ctypes.data, ctypes.byref(p)), p
+
+
+S = K.STATUS
+
+
+@pytest.mark.parametrize("lens,fields,status", [
+    ([1024], dict(batch=0), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(num_kv_heads=5), "ATTN_E_UNSUPPORTED"),
+    ([1024], dict(num_kv_heads=8), "ATTN_E_UNSUPPORTED"),          # GQA 4 at D=512
+    ([1024], dict(head_dim=128), "ATTN_E_UNSUPPORTED"),
+    ([1024], dict(format=1, rot_cols=64, v_offset=64), "ATTN_E_UNSUPPORTED"),
+    ([1024], dict(format=2), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(page_size=8, max_pages_per_seq=128), "ATTN_E_UNSUPPORTED"),
+    ([1024], dict(row_stride=1020), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(v_offset=516), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(page_stride=4 * 256 * 1024 - 8), "ATTN_E_INVALID_ARG"),  # last row overruns the page
+    ([1024], dict(scale=float("nan")), "ATTN_E_INVALID_ARG"),
+    ([0], dict(), "ATTN_E_INVALID_ARG"),
+    ([-3], dict(), "ATTN_E_INVALID_ARG"),
+    ([1025], dict(), "ATTN_E_PAST_PAGES"),
+    ([1024], dict(num_pages=1 << 62), "ATTN_E_OVERFLOW"),
+    ([1024], dict(num_chunks=-1), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(window=-1), "ATTN_E_INVALID_ARG"),
+])
+def test_plan_refusals(lens, fields, status):
+    f = global_desc()
+    f.update(fields)
+    rc, _ = plan_status(lens, **f)
+    assert rc == S[status], (rc, K.attn_decode_status_string(rc))
+
+
+def test_plan_accepts_exact_capacity_and_refuses_one_past():
+    rc, _ = plan_status([1024], **global_desc(1024))
+    assert rc == 0
+    rc, _ = plan_status([1025], **global_desc(1024))
+    assert rc == S["ATTN_E_PAST_PAGES"]
+
+
+def test_null_pointers_refused():
+    d = K.make_desc(**global_desc())
+    p = K.AttnDecodePlan()
+    lens = np.array([1024], dtype=np.int32)
+    assert K._lib.attn_decode_plan(None, lens.ctypes.data, ctypes.byref(p)) == S["ATTN_E_INVALID_ARG"]
+    assert K._lib.attn_decode_plan(ctypes.byref(d), None, ctypes.byref(p)) == S["ATTN_E_INVALID_ARG"]
+    assert K._lib.attn_decode_plan(ctypes.byref(d), lens.ctypes.data, None) == S["ATTN_E_INVALID_ARG"]
+
+
+def test_workspace_matches_gem_scratch_contract():
+    """At P = 32, Hq = 32, D = 512 the workspace is the byte contract the gem design
+    note prints: 4,096 + 4,096 + 2,097,152 = 2,105,344 bytes."""
+    gold = load_golden("gem_scratch_contract.txt")
+    rc, p = plan_status([8192], **global_desc(8192, num_chunks=gold["partitions"]))
+    assert rc == 0
+    assert p.num_chunks == gold["partitions"]
+    assert p.off_part_m == 0
+    assert p.off_part_l - p.off_part_m == gold["maxima_bytes"]
+    assert p.off_part_o - p.off_part_l == gold["denominators_bytes"]
+    assert p.workspace_bytes - p.off_part_o == gold["numerators_bytes"]
+    assert p.workspace_bytes == gold["total_bytes"]
+
+
+def test_size_limits_fail_closed():
+    """A pool whose element count passes 2^62, or a merge grid past 65535 rows, is refused."""
+    rc, _ = plan_status([1024], **global_desc(1024, num_pages=1 << 62))
+    assert rc == S["ATTN_E_OVERFLOW"]
+    hkv = 8191
+    f = global_desc(1024, batch=9, num_q_heads=8 * hkv, num_kv_heads=hkv,
+                    page_stride=hkv * 256 * 1024, num_pages=8)
+    rc, _ = plan_status([1024] * 9, **f)
+    assert rc == S["ATTN_E_OVERFLOW"], rc       # 9 x 65528 merge rows
+    f["batch"] = 1
+    rc, p = plan_status([1024], **f)
+    assert rc == 0 and p.workspace_bytes > 0
+
+
+def test_merge_group_bounds():
+    rc, p = plan_status([8192], **global_desc(8192, num_chunks=64, merge_group=8))
+    assert rc == 0 and p.num_groups == 8
+    rc, _ = plan_status([8192], **global_desc(8192, num_chunks=64, merge_group=7))
+    assert rc == S["ATTN_E_UNSUPPORTED"]
+    rc, p = plan_status([8192], **global_desc(8192, num_chunks=64))
+    assert rc == 0 and p.merge_group == 8 and p.num_groups == 8
+    rc, p = plan_status([8192], **global_desc(8192, num_chunks=5))
+    assert rc == 0 and p.merge_group == 1 and p.num_groups == 5
+
+
+def chunk_ranges(p, L):
+    lo = max(0, L - p.desc.window) if p.desc.window > 0 else 0
+    start = lo // p.tile * p.tile
+    out = []
+    for c in range(p.num_chunks):
+        a = start + c * p.chunk_len
+        out.append((max(a, lo), min(a + p.chunk_len, L)))
+    return lo, out
+
+
+@pytest.mark.parametrize("lens,fields,expect", [
+    ([1024], dict(num_chunks=8), dict(num_chunks=8, chunk_len=128)),
+    ([163336], dict(), dict(num_chunks=256, chunk_len=640)),
+    ([10602], dict(), dict(num_chunks=221, chunk_len=48)),
+    ([100], dict(num_chunks=16), dict(num_chunks=16, chunk_len=16)),
+])
+def test_chunking(lens, fields, expect):
+    L = lens[0]
+    f = global_desc(L, **fields)
+    rc, p = plan_status(lens, **f)
+    assert rc == 0
+    for k, v in expect.items():
+        assert getattr(p, k) == v, (k, getattr(p, k))
+    assert p.chunk_len % p.tile == 0 and p.tile == 16
+    lo, ranges = chunk_ranges(p, L)
+    covered = [x for a, b in ranges for x in range(a, b)]
+    assert covered == list(range(lo, L)), "chunks must tile [lo, L) in order"
+    assert p.num_groups == -(-p.num_chunks // p.merge_group)
+
+
+def test_sliding_chunking_covers_every_window():
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, 4097, size=16)
+    f = dict(batch=16, num_q_heads=32, num_kv_heads=16, head_dim=256, format=0, rot_cols=0,
+             page_size=64, max_pages_per_seq=64, window=1024, num_chunks=0, merge_group=0,
+             scale=1 / 16, num_pages=300, page_stride=16 * 64 * 512, head_stride=64 * 512,
+             row_stride=512, k_offset=0, v_offset=256)
+    rc, p = plan_status(lens, **f)
+    assert rc == 0
+    for L in lens:
+        lo, ranges = chunk_ranges(p, int(L))
+        covered = [x for a, b in ranges for x in range(a, b)]
+        assert covered == list(range(lo, int(L)))
+        assert int(L) - lo == min(int(L), 1024)
+
+
+def test_split_and_merge_refuse_before_any_launch():
+    rc, p = plan_status([1024], **global_desc())
+    assert rc == 0
+    fake = 1 << 20  # never dereferenced: every refusal below returns before a launch
+    ws = p.workspace_bytes
+    bad = K.AttnDecodePlan.from_buffer_copy(p)
+    bad.magic = 0
+    L = K._lib
+    assert L.attn_decode_split(ctypes.byref(bad), fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_PLAN"]
+    assert L.attn_decode_merge(ctypes.byref(bad), fake, ws, fake, None) == S["ATTN_E_PLAN"]
+    assert L.attn_decode_split(ctypes.byref(p), None, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_decode_split(ctypes.byref(p), fake, fake, fake, fake, fake, ws - 1, None) == S["ATTN_E_WORKSPACE"]
+    assert L.attn_decode_split(ctypes.byref(p), fake, fake, fake, fake, fake + 4, ws, None) == S["ATTN_E_WORKSPACE"]
+    assert L.attn_decode_merge(ctypes.byref(p), fake, ws - 1, fake, None) == S["ATTN_E_WORKSPACE"]
+    assert L.attn_decode_merge(ctypes.byref(p), fake, ws, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_decode_split(None, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+
+
+def test_status_strings():
+    for name, code in S.items():
+        s = K.attn_decode_status_string(code)
+        assert s and s != "unknown status", name
+    assert K.attn_decode_status_string(12345) == "unknown status"
