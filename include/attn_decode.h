@@ -107,7 +107,10 @@ typedef struct attn_decode_desc {
  * Workspace layout (byte offsets from the workspace base, each region 256-byte
  * aligned, all float32, partition-major and contiguous in the output dimension;
  * gem design note, "Candidate ownership and storage"):
- *   part_m [B][Hq][num_chunks]        running maxima, natural-log units
+ *   part_m [B][Hq][num_chunks]        reference maxima, natural-log units: at most the
+ *                                     chunk's largest score and at least that minus 8 ln 2
+ *                                     (-inf for an empty chunk); part_l and part_o are
+ *                                     taken relative to it, as the merge identity allows
  *   part_l [B][Hq][num_chunks]        denominators S
  *   part_o [B][Hq][num_chunks][D]     numerators O (unnormalised)
  * The merge's level-1 group states live in on-chip memory and need no workspace.

@@ -10,9 +10,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_decode.so")
 SOURCES = [os.path.join(CSRC, "attn_decode.hip"), os.path.join(CSRC, "plan.cpp")]
-# Packed fp32 VALU forms are kept out of the generated code.
+# Packed fp32 VALU forms are kept out of the generated code.  MFMA accumulators are
+# allocated as VGPRs (not AGPRs), so the softmax rescale touches them in place
+# instead of copying them across register files every tile.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function"]
 
 

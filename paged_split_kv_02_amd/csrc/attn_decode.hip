@@ -12,7 +12,9 @@
 //     probabilities), so the products keep ~16 mantissa bits while the inputs
 //     stay bf16, and no column is padding when G = 8;
 //   * online softmax in base 2 with scale*log2(e) folded into the query; the
-//     stored maxima are converted back to natural-log units;
+//     reference maximum moves only when a tile exceeds it by 2^8, so the
+//     accumulators are rarely rescaled; the stored reference is converted back
+//     to natural-log units (any reference <= the chunk maximum is a valid state);
 //   * masked keys (past L, before the window, padding slots of the last page)
 //     are excluded by select, and their V rows are zeroed before PV, so NaN or
 //     huge padding never reaches the sums.
@@ -53,6 +55,29 @@ struct SplitArgs {
 };
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Value of the lane holding the other bf16 part of the same head: column c ^ G
+// inside each 16-lane row (row rotation by 8 for G = 8, quad swap for G = 2).
+template <int G>
+__device__ __forceinline__ float partner(float v) {
+  static_assert(G == 8 || G == 2, "pairing defined for 8 or 2 heads per KV head");
+  const int x = __builtin_bit_cast(int, v);
+  const int y = G == 8 ? __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false)   // row_ror:8
+                       : __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  return __builtin_bit_cast(float, y);
+}
+
+// Uniform read of a page-table entry through the scalar cache (the table is never
+// written by these kernels).
+__device__ __forceinline__ int32_t load_page_id(const int32_t* row, int idx) {
+  typedef const int32_t __attribute__((address_space(4))) cint;
+  return *(cint*)(row + __builtin_amdgcn_readfirstlane(idx));
+}
+
+// The running maximum of a chunk is only moved when a tile's maximum exceeds it
+// by more than this (log2 units); until then probabilities stay below 2^8.  Any
+// reference at or below the true maximum gives a valid state for the merge.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -146,11 +171,22 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
     const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
     u32x4 stage[4][SLABS];
 
-    // Resolve the tile's page once; false if the table entry is outside the pool.
+    // Page ids are read once per page, the next page's id one page ahead; a tile
+    // never straddles two pages (16 divides the page size).
+    int cur_page = c0 / a.page_size;
+    int32_t cur_pid = load_page_id(trow, cur_page);
+    int32_t next_pid = cur_page + 1 < a.max_pages ? load_page_id(trow, cur_page + 1) : -1;
+    // Resolve the tile's rows; false if the table entry is outside the pool.
     auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
-      const int32_t pid = trow[tok0 / a.page_size];
-      if (pid < 0 || int64_t(pid) >= a.num_pages) return false;
-      *base = head_base + int64_t(pid) * a.page_stride + int64_t(tok0 % a.page_size) * a.row_stride;
+      const int page = tok0 / a.page_size;
+      if (page != cur_page) {
+        cur_page = page;
+        cur_pid = next_pid;
+        next_pid = page + 1 < a.max_pages ? load_page_id(trow, page + 1) : -1;
+      }
+      if (cur_pid < 0 || int64_t(cur_pid) >= a.num_pages) return false;
+      *base = head_base + int64_t(cur_pid) * a.page_stride +
+              int64_t(tok0 - page * a.page_size) * a.row_stride;
       return true;
     };
     // Column of staged piece sb (128 elements each) in the stored row.
@@ -183,21 +219,28 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
           poison = true;
           has_next = false;
         }
-        // Stage the tile (V rows of masked keys zeroed, so padding cannot leak
-        // through 0 * NaN), then start fetching the next one.
+        // Stage the tile, then start fetching the next one.
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int sb = 0; sb < SLABS; ++sb)
+            *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = stage[e][sb];
+        if (has_next) load_tile(nbase);
+        // Keys outside [lo, L) (first tile of a window, tail of the last page): zero
+        // their V rows so that padding cannot leak through 0 * NaN.
         const bool partial_tile = tok0 < lo || tok0 + kTile > L;
+        if (__builtin_expect(partial_tile, 0)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = tok0 + 4 * qg + e;
-          const bool dead = partial_tile && (t < lo || t >= L);
+          for (int e = 0; e < 4; ++e) {
+            const int t = tok0 + 4 * qg + e;
+            if (t < lo || t >= L) {
 #pragma unroll
-          for (int sb = 0; sb < SLABS; ++sb) {
-            u32x4 w = stage[e][sb];
-            if (dead && 128 * sb >= TV) w = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = w;
+              for (int b = 0; b < VGROUPS; ++b)
+                *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + TV + 128 * b + 8 * c) =
+                    u32x4{0u, 0u, 0u, 0u};
+            }
           }
         }
-        if (has_next) load_tile(nbase);
 
         // Scores of 16 keys x 16 columns (hi/lo parts of the G heads).  Key dim kd
         // sits at staged column kd (split / rotated part) or TV + kd (folded, kd >= ROT).
@@ -216,29 +259,31 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float full = s[i] + shfl_xor(s[i], G);
+          const float full = s[i] + partner<G>(s[i]);
           const int t = tok0 + 4 * qg + i;
           sc[i] = (t >= lo && t < L) ? full : -INFINITY;
           mx = fmaxf(mx, sc[i]);
         }
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        float alpha = 1.0f;
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-        if (m_new != -INFINITY) {
-          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-        }
-        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m_run = m_new;
-        if (__any(alpha != 1.0f)) {
+        // Move the reference maximum only when this tile exceeds it by the slack.
+        const bool grow = mx > m_run + kRescaleSlack;
+        if (__builtin_expect(__any(grow), 0)) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+          l_run *= alpha;
 #pragma unroll
           for (int b = 0; b < VGROUPS; ++b)
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
+          m_run = m_new;
         }
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (m_run != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+        }
+        l_run += (p[0] + p[1]) + (p[2] + p[3]);
         bf16x4 pop;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -278,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[b][jj][i] += shfl_xor(acc[b][jj][i], G);
+      for (int i = 0; i < 4; ++i) acc[b][jj][i] += partner<G>(acc[b][jj][i]);
 
   if (c < G) {
     const int64_t st = (int64_t(r) * a.num_q_heads + hq) * a.num_chunks + chunk;

@@ -62,9 +62,14 @@ def test_partials_match_oracle_per_chunk():
                     if st.m == -math.inf:
                         assert m[r, h, c] == -np.inf and l[r, h, c] == 0 and not np.any(o[r, h, c]), (r, h, c)
                         continue
-                    assert abs(m[r, h, c] - st.m) <= 1e-5 * max(1.0, abs(st.m)), (r, h, c, m[r, h, c], st.m)
-                    assert abs(l[r, h, c] - st.l) <= 1e-5 * st.l, (r, h, c)
-                    d = np.max(np.abs(o[r, h, c] / l[r, h, c] - st.acc / st.l))
+                    # The kernel's reference maximum may sit below the chunk maximum by
+                    # at most 8 (log2 units); the state it describes must be the same.
+                    mg = float(m[r, h, c])
+                    assert mg <= st.m + 1e-5 * max(1.0, abs(st.m)), (r, h, c, mg, st.m)
+                    assert mg >= st.m - 8 * math.log(2) - 1e-5, (r, h, c, mg, st.m)
+                    k = math.exp(mg - st.m)
+                    assert abs(l[r, h, c] * k - st.l) <= 1e-5 * st.l, (r, h, c)
+                    d = np.max(np.abs(o[r, h, c] * k / st.l - st.acc / st.l))
                     assert d <= 1e-4, (r, h, c, d)
     check(got, oracle.decode_attention(wl), "partials case")
 
