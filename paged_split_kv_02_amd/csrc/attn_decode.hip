@@ -1,7 +1,8 @@
 // Paged split-KV decode attention for gfx950 (MI355X): partial and merge kernels
 // and the C-ABI entry points that launch them.
 //
-// Partial kernel (one wave = one key chunk of one (request, KV head)):
+// Partial kernel (one workgroup = one key chunk of one (request, KV head); each of
+// its four waves streams a quarter of the chunk and the quarters are merged in LDS):
 //   * the G query heads of a KV head share every K/V byte the wave streams; each
 //     row is fetched from HBM once (gem design note, "Candidate ownership and
 //     storage": stage each K row once for the eight query heads);
@@ -116,10 +117,9 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const int c = lane & 15;   // MFMA row/column index inside a 16-block
   const int qg = lane >> 4;  // lane group: selects k sub-range / output rows
   const int wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x * kWavesPerBlock + wave;
+  const int chunk = blockIdx.x;  // one chunk per workgroup, one quarter per wave
   const int g = blockIdx.y;
   const int r = blockIdx.z;
-  if (chunk >= a.num_chunks) return;
   uint16_t* tile = tiles[wave].v;
 
   const int L = a.seq_lens[r];
@@ -128,8 +128,56 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
   bool poison = L < 1 || int64_t(L) > cap ||
                 int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
-  const int c0 = start + chunk * a.chunk_len;
-  const int c1 = min(c0 + a.chunk_len, L);
+  const int quarter = a.chunk_len / kWavesPerBlock;
+  const int c0 = start + chunk * a.chunk_len + wave * quarter;
+  const int c1 = min(c0 + quarter, L);
+  const bool has_work = !poison && c0 < c1;
+  const int32_t* trow = a.table + int64_t(r) * a.max_pages;
+  const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
+  u32x4 stage[4][SLABS];
+
+  // Page ids are read once per page, the next page's id one page ahead; a tile
+  // never straddles two pages (16 divides the page size).
+  int cur_page = c0 / a.page_size;
+  int32_t cur_pid = -1, next_pid = -1;
+  if (has_work) {
+    cur_pid = load_page_id(trow, cur_page);
+    next_pid = cur_page + 1 < a.max_pages ? load_page_id(trow, cur_page + 1) : -1;
+  }
+  // Resolve the tile's rows; false if the table entry is outside the pool.
+  auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
+    const int page = tok0 / a.page_size;
+    if (page != cur_page) {
+      cur_page = page;
+      cur_pid = next_pid;
+      next_pid = page + 1 < a.max_pages ? load_page_id(trow, page + 1) : -1;
+    }
+    if (cur_pid < 0 || int64_t(cur_pid) >= a.num_pages) return false;
+    *base = head_base + int64_t(cur_pid) * a.page_stride +
+            int64_t(tok0 - page * a.page_size) * a.row_stride;
+    return true;
+  };
+  // Column of staged piece sb (128 elements each) in the stored row.
+  auto src_col = [&](int sb) -> int64_t {
+    if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
+    return sb < VGROUPS ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VGROUPS);
+  };
+  // Lane (c, qg) fetches rows 4qg + e, 16 bytes at 128 sb + 8c: every instruction
+  // reads four whole 256-byte row pieces, so each line is requested once.
+  auto load_tile = [&](const uint16_t* base) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t* row = base + int64_t(4 * qg + e) * a.row_stride + 8 * c;
+#pragma unroll
+      for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col(sb));
+    }
+  };
+
+  // Start streaming the first tile before the query is prepared.
+  const uint16_t* base = nullptr;
+  const bool first_ok = has_work && tile_base(c0, &base);
+  if (has_work && !first_ok) poison = true;
+  if (first_ok) load_tile(base);
 
   // Query operand: column c holds head (c % G), high part for c < G, low part for
   // G <= c < 2G, zero beyond.  Dims of k-step j for lane group qg: 32j + 8qg + [0, 8).
@@ -166,52 +214,9 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (!poison && c0 < c1) {
-    const int32_t* trow = a.table + int64_t(r) * a.max_pages;
-    const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
-    u32x4 stage[4][SLABS];
-
-    // Page ids are read once per page, the next page's id one page ahead; a tile
-    // never straddles two pages (16 divides the page size).
-    int cur_page = c0 / a.page_size;
-    int32_t cur_pid = load_page_id(trow, cur_page);
-    int32_t next_pid = cur_page + 1 < a.max_pages ? load_page_id(trow, cur_page + 1) : -1;
-    // Resolve the tile's rows; false if the table entry is outside the pool.
-    auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
-      const int page = tok0 / a.page_size;
-      if (page != cur_page) {
-        cur_page = page;
-        cur_pid = next_pid;
-        next_pid = page + 1 < a.max_pages ? load_page_id(trow, page + 1) : -1;
-      }
-      if (cur_pid < 0 || int64_t(cur_pid) >= a.num_pages) return false;
-      *base = head_base + int64_t(cur_pid) * a.page_stride +
-              int64_t(tok0 - page * a.page_size) * a.row_stride;
-      return true;
-    };
-    // Column of staged piece sb (128 elements each) in the stored row.
-    auto src_col = [&](int sb) -> int64_t {
-      if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
-      return sb < VGROUPS ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VGROUPS);
-    };
-    // Lane (c, qg) fetches rows 4qg + e, 16 bytes at 128 sb + 8c: every instruction
-    // reads four whole 256-byte row pieces, so each line is requested once.
-    auto load_tile = [&](const uint16_t* base) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t* row = base + int64_t(4 * qg + e) * a.row_stride + 8 * c;
-#pragma unroll
-        for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col(sb));
-      }
-    };
-
+  if (first_ok) {
     int tok0 = c0;
-    const uint16_t* base;
-    if (!tile_base(tok0, &base)) {
-      poison = true;
-    } else {
-      load_tile(base);
-      for (;;) {
+    for (;;) {
         const int next = tok0 + kTile;
         bool has_next = next < c1;
         const uint16_t* nbase = nullptr;
@@ -311,11 +316,10 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
         }
         if (!has_next) break;
         tok0 = next;
-      }
     }
   }
 
-  // Chunk state: sum l over the lane groups, add the low columns onto the high ones.
+  // Quarter state: sum l over the lane groups, add the low columns onto the high ones.
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
 #pragma unroll
@@ -325,25 +329,66 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[b][jj][i] += partner<G>(acc[b][jj][i]);
 
+  // Workgroup merge of the four quarters (fixed order) into the chunk's state.  Each
+  // wave parks (m, l, O) of its G heads in its own LDS tile; after the barrier the
+  // workgroup folds them head by head, 4 dims per thread.
+  struct Parked {
+    float m[G], l[G];
+    floatx4 o[G][D / 4];
+  };
+  static_assert(sizeof(Parked) <= sizeof(RowTile<COLS>), "parked state must fit the tile");
+  Parked* mine = reinterpret_cast<Parked*>(tile);
+  const float qnan = __builtin_nanf("");
   if (c < G) {
-    const int64_t st = (int64_t(r) * a.num_q_heads + hq) * a.num_chunks + chunk;
-    const float qnan = __builtin_nanf("");
     if (qg == 0) {
-      a.part_m[st] = poison ? qnan : (m_run == -INFINITY ? -INFINITY : m_run * kLn2);
-      a.part_l[st] = poison ? qnan : l_run;
+      mine->m[c] = poison ? qnan : m_run;  // log2 units, -inf when empty
+      mine->l[c] = l_run;
     }
-    float* o = a.part_o + st * D;
 #pragma unroll
     for (int b = 0; b < VGROUPS; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        floatx4 w0 = {acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
-        floatx4 w1 = {acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
-        if (poison) w0 = w1 = floatx4{qnan, qnan, qnan, qnan};
-        float* dst = o + 128 * b + 32 * qg + 8 * i;
-        *reinterpret_cast<floatx4*>(dst) = w0;
-        *reinterpret_cast<floatx4*>(dst + 4) = w1;
+        const int d = 128 * b + 32 * qg + 8 * i;  // dims d .. d + 7
+        mine->o[c][d / 4] = floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+        mine->o[c][d / 4 + 1] = floatx4{acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
       }
+  }
+  __syncthreads();
+  const Parked* parked[kWavesPerBlock];
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) parked[w] = reinterpret_cast<const Parked*>(tiles[w].v);
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 64 * kWavesPerBlock) {
+    const int h = idx / (D / 4);
+    const int d4 = idx % (D / 4);
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const float x = parked[w]->m[h];
+      nan |= x != x;
+      M = fmaxf(M, x);
+    }
+    float S = 0.0f;
+    floatx4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float x = parked[w]->m[h];
+        const float wt = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
+        S += wt * parked[w]->l[h];
+        O += wt * parked[w]->o[h][d4];
+      }
+    }
+    const int64_t st = (int64_t(r) * a.num_q_heads + g * G + h) * a.num_chunks + chunk;
+    if (nan) {
+      M = S = qnan;
+      O = floatx4{qnan, qnan, qnan, qnan};
+    }
+    if (d4 == 0) {
+      a.part_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
+      a.part_l[st] = S;
+    }
+    *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O;
   }
 }
 
@@ -496,7 +541,7 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   args.num_chunks = plan->num_chunks;
   args.qscale = d.scale * kLog2e;
 
-  const dim3 grid((plan->num_chunks + kWavesPerBlock - 1) / kWavesPerBlock, d.num_kv_heads, d.batch);
+  const dim3 grid(plan->num_chunks, d.num_kv_heads, d.batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)

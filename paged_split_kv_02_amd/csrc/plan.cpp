@@ -98,20 +98,21 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   }
   if (max_span > INT32_MAX) return ATTN_E_OVERFLOW;
 
-  // Chunking: enough waves to give every SIMD of the chip one chunk, never a
-  // chunk shorter than a tile; an explicit count is honoured (trailing chunks
-  // may then be empty).
+  // Chunking: one chunk per workgroup, one quarter of it per wave, so that every
+  // SIMD of the chip streams one quarter; a quarter is never shorter than a tile.
+  // An explicit count is honoured (trailing chunks may then be empty).
   const int64_t tiles = ceil_div(max_span, kTile);
   int64_t n = d.num_chunks;
   if (n == 0) {
     const int64_t units = int64_t(d.batch) * d.num_kv_heads;
-    n = ceil_div(kTargetWaves, units);
-    if (n > tiles) n = tiles;
+    n = ceil_div(kTargetWaves / kWavesPerBlock, units);
+    const int64_t most = ceil_div(tiles, kWavesPerBlock);
+    if (n > most) n = most;
     if (n < 1) n = 1;
   }
   if (n > (int64_t(1) << 24)) return ATTN_E_OVERFLOW;
-  const int64_t chunk_tiles = ceil_div(tiles, n);
-  const int64_t chunk_len = chunk_tiles * kTile;
+  const int64_t quarter_tiles = ceil_div(tiles, n * kWavesPerBlock);
+  const int64_t chunk_len = quarter_tiles * kTile * kWavesPerBlock;
   if (d.num_chunks == 0) n = ceil_div(max_span, chunk_len);
 
   // Level-1 groups: at most kMergeGroups per (request, head), so the merge's second
@@ -122,8 +123,8 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   if (gm > n) gm = n;
   const int64_t ng = ceil_div(n, gm);
 
-  // Grid limits: blocks along x carry chunk quads, y the KV heads, z the requests.
-  if (ceil_div(n, kWavesPerBlock) > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535 ||
+  // Grid limits: blocks along x carry chunks, y the KV heads, z the requests.
+  if (n > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535 ||
       d.num_q_heads > 65535)
     return ATTN_E_OVERFLOW;
 

@@ -9,7 +9,7 @@ namespace attn {
 
 constexpr uint64_t kPlanMagic = 0x5041474544534b56ull;  // "PAGEDSKV"
 constexpr int kTile = 16;            // keys per tile = rows of one 16x16 MFMA block
-constexpr int kWavesPerBlock = 4;    // one chunk per wave, four waves per workgroup
+constexpr int kWavesPerBlock = 4;    // one chunk per workgroup, one quarter per wave
 constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
 

@@ -167,9 +167,9 @@ def chunk_ranges(p, L):
 
 @pytest.mark.parametrize("lens,fields,expect", [
     ([1024], dict(num_chunks=8), dict(num_chunks=8, chunk_len=128)),
-    ([163336], dict(), dict(num_chunks=256, chunk_len=640)),
-    ([10602], dict(), dict(num_chunks=221, chunk_len=48)),
-    ([100], dict(num_chunks=16), dict(num_chunks=16, chunk_len=16)),
+    ([163336], dict(), dict(num_chunks=64, chunk_len=2560)),
+    ([10602], dict(), dict(num_chunks=56, chunk_len=192)),
+    ([100], dict(num_chunks=16), dict(num_chunks=16, chunk_len=64)),
 ])
 def test_chunking(lens, fields, expect):
     L = lens[0]
@@ -178,7 +178,7 @@ def test_chunking(lens, fields, expect):
     assert rc == 0
     for k, v in expect.items():
         assert getattr(p, k) == v, (k, getattr(p, k))
-    assert p.chunk_len % p.tile == 0 and p.tile == 16
+    assert p.chunk_len % (4 * p.tile) == 0 and p.tile == 16
     lo, ranges = chunk_ranges(p, L)
     covered = [x for a, b in ranges for x in range(a, b)]
     assert covered == list(range(lo, L)), "chunks must tile [lo, L) in order"
