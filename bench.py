@@ -289,6 +289,34 @@ def main():
                               "num_chunks": vres.plan.num_chunks, "timing": "median, cache flushed"}
             print(f"# {name}: {vms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
             del vres
+        # the step that feeds decode: a 10,602-token prompt's K/V rows written into pages
+        # (fp32 in, bf16 rows out), and a single decode-token append
+        import paged_split_kv_02_amd as K
+        wlw = synth.global_decode(10602, seed=5)
+        wres = Resident(wlw)
+        gen = torch.Generator(device="cuda:0").manual_seed(5)
+        for name, n in (("kv-write-prompt-10602-split", 10602), ("kv-write-append-1-split", 1)):
+            kk = torch.randn(1, n, 4, 512, generator=gen, device="cuda:0")
+            vv = torch.randn(1, n, 4, 512, generator=gen, device="cuda:0")
+            start = torch.tensor([10602 - n], dtype=torch.int32, device="cuda:0")
+            times = []
+            for it in range(23):
+                flush()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                K.attn_kv_write(wres.plan, kk, vv, n, start, wres.pool, wres.table)
+                b.record()
+                torch.cuda.synchronize()
+                if it >= 3:
+                    times.append(a.elapsed_time(b))
+            t = median(times)
+            moved = kk.numel() * 4 + vv.numel() * 4 + n * 4 * 1024 * 2
+            variants[name] = {"us": round(t * 1e3, 2), "bytes": moved,
+                              "gbs": round(moved / (t * 1e-3) / 1e9, 1),
+                              "timing": "median of 20, cache flushed"}
+            print(f"# {name}: {t * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del wres
         line["variants"] = variants
         del flush_buf
 

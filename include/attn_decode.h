@@ -175,6 +175,39 @@ int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void
 int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace, size_t workspace_bytes,
                       float* out, void* stream);
 
+/*
+ * Write new tokens' K/V rows into the pool: the step that feeds decode.  Each
+ * forward's k/v rows are copied into the pages through the table (TensorFold PR
+ * #1619, body), in the pool's row format (pegainfer PR #1055, "Description": the
+ * hd512 prep writes either form).  Values arrive as float32 and are stored as bf16,
+ * rounded to nearest with ties to even.
+ *   k          device float32 [batch][num_new][num_kv_heads][kc]; kc = head_dim for
+ *              SPLIT (row columns k_offset..), rot_cols for FOLDED (the rotated part)
+ *   v          device float32 [batch][num_new][num_kv_heads][head_dim] (columns v_offset..)
+ *   start_pos  device int32 [batch]: logical position of each request's first new token;
+ *              token i goes to position start_pos[r] + i (a decode step appends at L - 1)
+ *   kv_pool    device bf16 pool, written in place
+ *   page_table device int32 [batch][max_pages_per_seq]
+ *   bad_rows   device int32, may be NULL: set to 1 if any row was skipped because its
+ *              position is past the table row or its page id is outside the pool (such
+ *              rows are never written); the caller clears it beforehand
+ * Only the addressed row columns are written.  Uses the plan's layout (its lengths are
+ * not consulted).  ATTN_E_INVALID_ARG on null pointers or num_new < 1.
+ */
+int attn_kv_write(const attn_decode_plan_t* plan, const float* k, const float* v, int32_t num_new,
+                  const int32_t* start_pos, void* kv_pool, const int32_t* page_table,
+                  int32_t* bad_rows, void* stream);
+
+/*
+ * Fold K's norm weight into the query for a FOLDED pool (pegainfer PR #1055,
+ * "Description"): q_out[r][h][d] = q[r][h][d] for d < rot_cols, else the float32
+ * product q[r][h][d] * norm_w[d - rot_cols].  q and q_out are device float32
+ * [batch][num_q_heads][head_dim] (may alias); norm_w is device float32
+ * [head_dim - rot_cols].  ATTN_E_UNSUPPORTED for a SPLIT plan.
+ */
+int attn_query_fold(const attn_decode_plan_t* plan, const float* q, const float* norm_w,
+                    float* q_out, void* stream);
+
 /* Static, NUL-terminated text for a status code. */
 const char* attn_decode_status_string(int status);
 

@@ -6,3 +6,4 @@ this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
 library; the two meet only at the seeded inputs built by ``synth``.
 """
 from .attention import *  # noqa: F401,F403
+from .kv_write import *  # noqa: F401,F403

@@ -15,6 +15,7 @@ from . import build as _build
 
 __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_plan",
            "attn_decode_split", "attn_decode_merge", "attn_decode_status_string", "make_desc",
+           "attn_kv_write", "attn_query_fold",
            "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "STATUS", "LIB_PATH", "SYMBOLS"]
 
 ATTN_KV_SPLIT = 0
@@ -23,7 +24,7 @@ STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
           "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
 SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_merge",
-           "attn_decode_status_string")
+           "attn_decode_status_string", "attn_kv_write", "attn_query_fold")
 LIB_PATH = _build.LIB
 
 
@@ -66,6 +67,10 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode_split.restype = ctypes.c_int
     lib.attn_decode_merge.argtypes = [ctypes.POINTER(AttnDecodePlan), P, ctypes.c_size_t, P, P]
     lib.attn_decode_merge.restype = ctypes.c_int
+    lib.attn_kv_write.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, ctypes.c_int32, P, P, P, P, P]
+    lib.attn_kv_write.restype = ctypes.c_int
+    lib.attn_query_fold.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P]
+    lib.attn_query_fold.restype = ctypes.c_int
     lib.attn_decode_status_string.argtypes = [ctypes.c_int]
     lib.attn_decode_status_string.restype = ctypes.c_char_p
     return lib
@@ -141,3 +146,19 @@ def attn_decode_merge(plan: AttnDecodePlan, workspace, out, workspace_bytes=None
                                 _stream(stream))
     if rc != 0:
         raise AttnDecodeError("attn_decode_merge", rc)
+
+
+def attn_kv_write(plan: AttnDecodePlan, k, v, num_new: int, start_pos, kv_pool, page_table,
+                  bad_rows=None, stream=None) -> None:
+    rc = _lib.attn_kv_write(ctypes.byref(plan), _ptr(k), _ptr(v), int(num_new), _ptr(start_pos),
+                            _ptr(kv_pool), _ptr(page_table), _ptr(bad_rows), _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_kv_write", rc)
+
+
+def attn_query_fold(plan: AttnDecodePlan, q, norm_w, q_out, stream=None) -> None:
+    rc = _lib.attn_query_fold(ctypes.byref(plan), _ptr(q), _ptr(norm_w), _ptr(q_out),
+                              _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_query_fold", rc)
+

@@ -484,6 +484,74 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
+struct WriteArgs {
+  const float* k;
+  const float* v;
+  const int32_t* start_pos;
+  uint16_t* pool;
+  const int32_t* table;
+  int32_t* bad_rows;
+  int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
+  int32_t num_kv_heads, head_dim, kcols, num_new, page_size, max_pages;
+};
+
+// New K/V rows into their pages: one workgroup per (request, token, KV head) row, one
+// thread per 16 output bytes (8 values, read as two 16-byte fp32 loads, rounded to bf16
+// with ties to even).  The row's position and page are workgroup-uniform.  Rows whose
+// position or page is outside the table / pool are skipped and flagged.
+__global__ __launch_bounds__(128) void kv_write_kernel(WriteArgs a) {
+  const int64_t row = blockIdx.x;  // ((r * num_new) + i) * num_kv_heads + g
+  const int g = int(row % a.num_kv_heads);
+  const int64_t ri = row / a.num_kv_heads;
+  const int i = int(ri % a.num_new);
+  const int r = int(ri / a.num_new);
+  const int pc = threadIdx.x;
+  const int kp = a.kcols / 8;
+  if (pc >= kp + a.head_dim / 8) return;
+  const int64_t pos = int64_t(a.start_pos[r]) + i;
+  bool ok = pos >= 0 && pos < int64_t(a.max_pages) * a.page_size;
+  int32_t pid = -1;
+  if (ok) {
+    pid = a.table[int64_t(r) * a.max_pages + pos / a.page_size];
+    ok = pid >= 0 && int64_t(pid) < a.num_pages;
+  }
+  if (!ok) {
+    if (a.bad_rows && pc == 0) *a.bad_rows = 1;
+    return;
+  }
+  const float* src;
+  int64_t col;
+  if (pc < kp) {
+    src = a.k + row * a.kcols + 8 * pc;
+    col = a.k_offset + 8 * pc;
+  } else {
+    src = a.v + row * a.head_dim + 8 * (pc - kp);
+    col = a.v_offset + 8 * (pc - kp);
+  }
+  const floatx4 x0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src));
+  const floatx4 x1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4));
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[e] = (__bf16)x0[e];
+    y[e + 4] = (__bf16)x1[e];
+  }
+  uint16_t* dst = a.pool + int64_t(pid) * a.page_stride + int64_t(g) * a.head_stride +
+                  (pos % a.page_size) * a.row_stride + col;
+  *reinterpret_cast<bf16x8*>(dst) = y;
+}
+
+// q' = q with columns rot.. multiplied by the norm weight (one float32 product each).
+__global__ __launch_bounds__(256) void query_fold_kernel(const float* q, const float* w, float* out,
+                                                          int64_t quads, int head_dim, int rot) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= quads) return;
+  const int d = int((4 * t) % head_dim);
+  floatx4 x = *reinterpret_cast<const floatx4*>(q + 4 * t);
+  if (d >= rot) x *= *reinterpret_cast<const floatx4*>(w + (d - rot));
+  *reinterpret_cast<floatx4*>(out + 4 * t) = x;
+}
+
 template <int D, int G, bool FOLDED>
 void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
@@ -570,3 +638,58 @@ extern "C" int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace
     launch_merge<256>(*plan, static_cast<char*>(workspace), out, s);
   return launch_status();
 }
+
+extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, const float* v,
+                             int32_t num_new, const int32_t* start_pos, void* kv_pool,
+                             const int32_t* page_table, int32_t* bad_rows, void* stream) {
+  using namespace attn;
+  int rc = check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (!k || !v || !start_pos || !kv_pool || !page_table || num_new < 1) return ATTN_E_INVALID_ARG;
+  const attn_decode_desc& d = plan->desc;
+  const int kcols = d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim;
+  const int row_pieces = (kcols + d.head_dim) / 8;  // at most 128 for the supported shapes
+  int64_t rows;
+  if (__builtin_mul_overflow(int64_t(d.batch) * d.num_kv_heads, int64_t(num_new), &rows))
+    return ATTN_E_OVERFLOW;
+  if (rows > INT32_MAX || row_pieces > 128) return ATTN_E_OVERFLOW;
+  WriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.start_pos = start_pos;
+  a.pool = static_cast<uint16_t*>(kv_pool);
+  a.table = page_table;
+  a.bad_rows = bad_rows;
+  a.page_stride = d.page_stride;
+  a.head_stride = d.head_stride;
+  a.row_stride = d.row_stride;
+  a.k_offset = d.k_offset;
+  a.v_offset = d.v_offset;
+  a.num_pages = d.num_pages;
+  a.num_kv_heads = d.num_kv_heads;
+  a.head_dim = d.head_dim;
+  a.kcols = kcols;
+  a.num_new = num_new;
+  a.page_size = d.page_size;
+  a.max_pages = d.max_pages_per_seq;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(kv_write_kernel, dim3(unsigned(rows)), dim3(row_pieces), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
+extern "C" int attn_query_fold(const attn_decode_plan_t* plan, const float* q, const float* norm_w,
+                               float* q_out, void* stream) {
+  using namespace attn;
+  int rc = check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (!q || !norm_w || !q_out) return ATTN_E_INVALID_ARG;
+  const attn_decode_desc& d = plan->desc;
+  if (d.format != ATTN_KV_FOLDED) return ATTN_E_UNSUPPORTED;
+  const int64_t quads = int64_t(d.batch) * d.num_q_heads * d.head_dim / 4;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(query_fold_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), q, norm_w, q_out, quads, d.head_dim, d.rot_cols);
+  return launch_status();
+}
+

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "attn_decode.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_decode_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\sT\s(attn_decode_\w+)$", out, re.M))
+    exported = set(re.findall(r"\sT\s(attn_\w+)$", out, re.M))
     assert set(names) <= exported
 
 
@@ -217,6 +217,11 @@ def test_split_and_merge_refuse_before_any_launch():
     assert L.attn_decode_merge(ctypes.byref(p), fake, ws - 1, fake, None) == S["ATTN_E_WORKSPACE"]
     assert L.attn_decode_merge(ctypes.byref(p), fake, ws, None, None) == S["ATTN_E_INVALID_ARG"]
     assert L.attn_decode_split(None, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_kv_write(ctypes.byref(bad), fake, fake, 1, fake, fake, fake, None, None) == S["ATTN_E_PLAN"]
+    assert L.attn_kv_write(ctypes.byref(p), fake, fake, 0, fake, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_kv_write(ctypes.byref(p), None, fake, 1, fake, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_query_fold(ctypes.byref(p), fake, fake, fake, None) == S["ATTN_E_UNSUPPORTED"]  # split plan
+    assert L.attn_query_fold(ctypes.byref(bad), fake, fake, fake, None) == S["ATTN_E_PLAN"]
 
 
 def test_status_strings():
