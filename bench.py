@@ -87,8 +87,8 @@ class Resident:
         self.table = torch.from_numpy(wl.table).to(dev)
         self.lens = torch.from_numpy(wl.seq_lens).to(dev)
         self.ws = torch.empty(int(self.plan.workspace_bytes), dtype=torch.uint8, device=dev)
-        self.out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, dtype=torch.float32,
-                               device=dev)
+        self.out = torch.empty(wl.batch * wl.num_rows, wl.num_q_heads, wl.head_dim,
+                               dtype=torch.float32, device=dev)
 
     def split(self):
         self.K.attn_decode_split(self.plan, self.q, self.pool, self.table, self.lens, self.ws)
@@ -101,7 +101,7 @@ class Resident:
         entries, and the chunk states written."""
         wl, p = self.wl, self.plan
         pages = sum(-(-int(L) // wl.page_size) for L in wl.seq_lens)
-        states = wl.batch * wl.num_q_heads * p.num_chunks
+        states = wl.batch * wl.num_rows * wl.num_q_heads * p.num_chunks
         return (wl.kv_bytes() + wl.q.size * 4 + pages * 4 + states * (wl.head_dim + 2) * 4)
 
 
@@ -275,13 +275,16 @@ def main():
             flush_buf.zero_()  # 1 GiB of writes evicts the 256 MB infinity cache
         for name, maker, n_steps in (
                 ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
-                ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20)):
+                ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
+                ("global-decode-163336-split-4rows",
+                 lambda: synth.make_workload([163336], **synth.GLOBAL, seed=6, num_rows=4,
+                                             spare_pages=1), 20)):
             vwl = maker()
             vres = Resident(vwl)
             vt = time_steps(vres, n_steps, 3, flush=flush)
             vms = median(vt["step_ms"])
             vsplit = median(vt["split_ms"])
-            variants[name] = {"us_per_step": round(vms * 1e3, 2),
+            variants[name] = {"us_per_step": round(vms * 1e3, 2), "query_rows": vwl.num_rows,
                               "partial_kernel_us": round(vsplit * 1e3, 2),
                               "kv_bytes": vwl.kv_bytes(),
                               "effective_gbs": round(vwl.kv_bytes() / (vms * 1e-3) / 1e9, 1),

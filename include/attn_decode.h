@@ -88,6 +88,11 @@ typedef struct attn_decode_desc {
   int32_t num_chunks;         /* key chunks per (request, KV head); 0 = choose automatically */
   int32_t merge_group;        /* chunk partials per level-1 group; 0 = choose automatically,
                                  else at least ceil(chunks / 8) (at most 8 groups) */
+  int32_t num_rows;           /* query rows per request, 0 or 1 = ordinary decode; n > 1 is a
+                                 window: row i is the token at position L - n + i and attends
+                                 causally to the keys before L - n + i + 1 (drafted verify
+                                 windows through the paged decode, TensorFold PR #1619, review
+                                 thread); q and out are then [batch][n][num_q_heads][head_dim] */
   float scale;                /* score = scale * q . k (1/sqrt(D) in the workloads) */
   int64_t num_pages;          /* pages in the pool; table entries outside [0, num_pages) poison */
   int64_t page_stride;        /* elements between pages */
@@ -99,14 +104,15 @@ typedef struct attn_decode_desc {
 
 /*
  * A validated plan (host-only POD).  Chunk c of request r covers key positions
- *   [start_r + c * chunk_len, start_r + (c + 1) * chunk_len)  intersected with [lo_r, L_r)
- * where lo_r = max(0, L_r - window) (0 without a window) and
- * start_r = lo_r rounded down to a multiple of `tile`.  A chunk with no visible key
- * yields the empty partial (-inf, 0, 0).
+ *   [start_r + c * chunk_len, start_r + (c + 1) * chunk_len)  intersected with the keys
+ * a query row sees, where lo_r = max(0, L_r - rows + 1 - window) (0 without a window)
+ * is the oldest key any row of the request sees and start_r = lo_r rounded down to a
+ * multiple of `tile`.  A chunk with no visible key yields the empty partial (-inf, 0, 0).
  *
  * Workspace layout (byte offsets from the workspace base, each region 256-byte
  * aligned, all float32, partition-major and contiguous in the output dimension;
  * gem design note, "Candidate ownership and storage"):
+ * (with several query rows, B counts requests x rows: row i of request r is r*rows + i)
  *   part_m [B][Hq][num_chunks]        reference maxima, natural-log units: at most the
  *                                     chunk's largest score and at least that minus 8 ln 2
  *                                     (-inf for an empty chunk); part_l and part_o are
@@ -125,7 +131,9 @@ typedef struct attn_decode_plan_t {
   int32_t merge_group;   /* chunk partials folded per level-1 group */
   int32_t num_groups;    /* level-1 states per (request, query head), at most 8 */
   int32_t max_span;      /* max over requests of L_r - start_r */
-  int32_t reserved;
+  int32_t num_rows;      /* query rows per request (>= 1) */
+  int32_t row_groups;    /* groups of up to 4 rows, one workgroup each (multi-row) */
+  int32_t grid_x;        /* workgroups along the chunk axis of the partial launch */
   uint64_t off_part_m, off_part_l, off_part_o;
   uint64_t workspace_bytes; /* bytes attn_decode_split / attn_decode_merge need */
 } attn_decode_plan_t;
@@ -136,7 +144,8 @@ typedef struct attn_decode_plan_t {
  * Refusals: null pointers or non-positive sizes (ATTN_E_INVALID_ARG); a shape
  * outside the supported list (ATTN_E_UNSUPPORTED); a stride or offset not a
  * multiple of 8, or rows overrunning their page (ATTN_E_INVALID_ARG); a length
- * below 1 (ATTN_E_INVALID_ARG); a length above max_pages_per_seq * page_size
+ * below 1 or below num_rows, or num_rows above 64 (ATTN_E_INVALID_ARG); a length
+ * above max_pages_per_seq * page_size
  * (ATTN_E_PAST_PAGES, TensorFold PR #1619, body: rows past a slot's pages are
  * refused); a merge_group below ceil(chunks / 8) (ATTN_E_UNSUPPORTED); any size
  * product that overflows, or a grid beyond the launch limits (ATTN_E_OVERFLOW;
@@ -149,7 +158,8 @@ int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
 /*
  * Enqueue the partial kernel: one online-softmax state per (request, query
  * head, chunk) into the workspace's part_* regions.
- *   q          device, float32 [batch][num_q_heads][head_dim] (FOLDED: the folded q')
+ *   q          device, float32 [batch][num_q_heads][head_dim] (FOLDED: the folded q'),
+ *              [batch][num_rows][num_q_heads][head_dim] with several query rows
  *   kv_pool    device, bf16 pool laid out as described for attn_decode_desc
  *   page_table device, int32 [batch][max_pages_per_seq]
  *   seq_lens   device, int32 [batch]; must equal the lengths given to the plan.  A
@@ -169,7 +179,8 @@ int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void
  * merge_group consecutive chunk states into a group state (out of place: the
  * chunk states are only read); level 2 folds the group states in ascending
  * order and writes O / S.
- *   out   device, float32 [batch][num_q_heads][head_dim]; nothing else is written.
+ *   out   device, float32 [batch][num_q_heads][head_dim] ([batch][num_rows][...] with
+ *         several query rows); nothing else is written.
  * Same error behaviour as attn_decode_split.
  */
 int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace, size_t workspace_bytes,

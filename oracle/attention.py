@@ -20,6 +20,10 @@ What it computes, and where the pages fix it
 * Windowed decode (sliding layers): the resident pages may hold one page more
   than the window and those older keys are masked (pegainfer PR #1057,
   Description).  Reading taken: position j is visible iff L - W <= j < L.
+* Several query rows per request (TensorFold PR #1619, review thread: drafted verify
+  windows go through the paged decode kernels): row i of an n-row window is the token at
+  position L - n + i and sees the keys before L - n + i + 1, i.e. each row is ordinary
+  decode at its own length.
 * Split-KV: each key chunk yields an online-softmax partial (running max M, sum
   S, unnormalised numerator O); partials merge with the exact rescaling identity
   M = max(Ma, Mb), S = Sa e^(Ma-M) + Sb e^(Mb-M), O likewise, then O / S; empty
@@ -121,17 +125,26 @@ def dense_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -
 
 
 def decode_attention(wl) -> np.ndarray:
-    """fp64 output [B][Hq][D] of one decode step over the paged pool."""
+    """fp64 output of one decode step over the paged pool: [B][Hq][D], or
+    [B][rows][Hq][D] when the workload has a window of several query rows.
+
+    Query row i of a window of n rows sits at position L - n + i and attends causally:
+    to the keys at positions before L - n + i + 1 (and, with a sliding window, not older
+    than W keys back from there).  One row is ordinary decode.
+    """
     G = wl.num_q_heads // wl.num_kv_heads
-    out = np.empty((wl.batch, wl.num_q_heads, wl.head_dim), dtype=np.float64)
+    n = getattr(wl, "num_rows", 1)
+    q = wl.q if n > 1 else wl.q[:, None]
+    out = np.empty((wl.batch, n, wl.num_q_heads, wl.head_dim), dtype=np.float64)
     for r in range(wl.batch):
-        lo, L = visible_range(int(wl.seq_lens[r]), wl.window)
-        pos = np.arange(lo, L)
-        for g in range(wl.num_kv_heads):
-            K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
-            heads = slice(g * G, (g + 1) * G)
-            out[r, heads] = dense_attention(wl.q[r, heads], K, V, wl.scale)
-    return out
+        for i in range(n):
+            lo, L = visible_range(int(wl.seq_lens[r]) - n + 1 + i, wl.window)
+            pos = np.arange(lo, L)
+            for g in range(wl.num_kv_heads):
+                K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
+                heads = slice(g * G, (g + 1) * G)
+                out[r, i, heads] = dense_attention(q[r, i, heads], K, V, wl.scale)
+    return out if n > 1 else out[:, 0]
 
 
 # --------------------------------------------------------------------------------------
@@ -218,18 +231,22 @@ def split_kv_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float
     return finalize(fold(groups))
 
 
-def paged_partials(wl, r: int, g: int, ranges: Sequence[tuple[int, int]]) -> list[list[State]]:
-    """Per-chunk states for the G query heads of KV head g of request r.
+def paged_partials(wl, r: int, g: int, ranges: Sequence[tuple[int, int]],
+                   row: int = 0) -> list[list[State]]:
+    """Per-chunk states for the G query heads of KV head g of request r (query row
+    `row` of a multi-row window).
 
-    ``ranges`` are position intervals [a, b); positions outside the visible
+    ``ranges`` are position intervals [a, b); positions outside the row's visible
     range are dropped.  Returns states[h_in_group][chunk].
     """
     G = wl.num_q_heads // wl.num_kv_heads
-    lo, L = visible_range(int(wl.seq_lens[r]), wl.window)
+    n = getattr(wl, "num_rows", 1)
+    q = wl.q if n > 1 else wl.q[:, None]
+    lo, L = visible_range(int(wl.seq_lens[r]) - n + 1 + row, wl.window)
     out = [[] for _ in range(G)]
     for a, b in ranges:
         pos = np.arange(max(a, lo), min(b, L))
         K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
         for i in range(G):
-            out[i].append(partial_state(wl.q[r, g * G + i], K, V, wl.scale))
+            out[i].append(partial_state(q[r, row, g * G + i], K, V, wl.scale))
     return out

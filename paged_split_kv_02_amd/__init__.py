@@ -34,7 +34,8 @@ class AttnDecodeDesc(ctypes.Structure):
                 ("format", ctypes.c_int32), ("rot_cols", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
-                ("merge_group", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("merge_group", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("scale", ctypes.c_float),
                 ("num_pages", ctypes.c_int64), ("page_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64),
                 ("k_offset", ctypes.c_int64), ("v_offset", ctypes.c_int64)]
@@ -45,7 +46,8 @@ class AttnDecodePlan(ctypes.Structure):
                 ("group_size", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("chunk_len", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("merge_group", ctypes.c_int32), ("num_groups", ctypes.c_int32),
-                ("max_span", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_span", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("row_groups", ctypes.c_int32), ("grid_x", ctypes.c_int32),
                 ("off_part_m", ctypes.c_uint64), ("off_part_l", ctypes.c_uint64),
                 ("off_part_o", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 

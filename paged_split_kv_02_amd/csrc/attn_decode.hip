@@ -52,6 +52,7 @@ struct SplitArgs {
   float* part_o;
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_q_heads, page_size, max_pages, window, chunk_len, num_chunks;
+  int32_t num_rows, row_groups;  // query rows per request; groups of 4 rows (multi-row kernel)
   float qscale;  // scale * log2(e)
 };
 
@@ -89,27 +90,194 @@ __device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Per-wave LDS tile: the 16 stored rows of one key tile, padded by 16 bytes per
-// row.  Staging writes (one row, 16 consecutive 16-byte pieces per 16-lane pass)
-// and the QK reads (16 rows, one column per pass) both fall in distinct banks.
+// LDS tile: the 16 stored rows of one key tile, padded by 16 bytes per row.
+// Staging writes (one row, 16 consecutive 16-byte pieces per 16-lane pass) and the
+// QK reads (16 rows, one column per pass) both fall in distinct banks.
 template <int COLS>
 struct alignas(16) RowTile {
   static constexpr int kPitch = COLS + 8;  // elements
   uint16_t v[kTile * kPitch];
 };
 
+// Compile-time shape of one partial kernel instance.
+template <int D, bool FOLDED>
+struct Shape {
+  static constexpr int KSTEPS = D / 32;    // 16x16x32 MFMA steps over the key dimension
+  static constexpr int VGROUPS = D / 128;  // 128-dim slabs of V per tile
+  static constexpr int ROT = FOLDED ? 128 : 0;
+  // Columns staged per row: split K | V (2D), folded rotated K | V (ROT + D).
+  static constexpr int COLS = FOLDED ? ROT + D : 2 * D;
+  static constexpr int SLABS = COLS / 128;  // 256-byte pieces per row
+  static constexpr int P = RowTile<COLS>::kPitch;
+  static constexpr int TV = FOLDED ? ROT : D;  // staged column of V[0]
+};
+
+// Query operand of lane (c, qg) for one query row: column c holds head (c % G) of KV
+// head g, the high bf16 part of q*scale*log2(e) for c < G, the low remainder for
+// G <= c < 2G, zero beyond; k-step j covers dims 32j + 8qg + [0, 8).
+template <int D, int G>
+__device__ __forceinline__ void make_query_operand(const float* qrow_heads, int g, int c, int qg,
+                                                   float qscale, bf16x8 (&qop)[D / 32]) {
+  const int part = c / G;
+  const float* qrow = qrow_heads + int64_t(g * G + c % G) * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    bf16x8 v;
+    if (part < 2) {
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * qscale;
+        const __bf16 h = (__bf16)x;
+        v[e] = part == 0 ? h : (__bf16)(x - (float)h);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+    }
+    qop[j] = v;
+  }
+}
+
+// One staged tile of 16 keys for one query row: QK^T on MFMA, online softmax over the
+// keys tok0 + 4qg + i visible to the row (lo <= key < hi), PV on MFMA.  The caller has
+// zeroed the V rows of keys no row may see.
+template <int D, int G, bool FOLDED>
+__device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo, int hi,
+                                          const bf16x8 (&qop)[D / 32], int c, int qg,
+                                          float& m_run, float& l_run,
+                                          floatx4 (&acc)[D / 128][8]) {
+  using S = Shape<D, FOLDED>;
+  const int part = c / G;
+  // Scores of 16 keys x 16 columns (hi/lo parts of the G heads).  Key dim kd sits at
+  // staged column kd (split / rotated part) or TV + kd (folded, kd >= ROT).
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < S::KSTEPS; ++j) {
+    const int kd = 32 * j + 8 * qg;
+    const int col = (FOLDED && kd >= S::ROT) ? S::TV + kd : kd;
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(tile + c * S::P + col);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[j], s, 0, 0, 0);
+  }
+
+  // Online softmax (base 2); lane holds keys tok0 + 4qg + i.
+  float sc[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float full = s[i] + partner<G>(s[i]);
+    const int t = tok0 + 4 * qg + i;
+    sc[i] = (t >= lo && t < hi) ? full : -INFINITY;
+    mx = fmaxf(mx, sc[i]);
+  }
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  // Move the reference maximum only when this tile exceeds it by the slack.
+  const bool grow = mx > m_run + kRescaleSlack;
+  if (__builtin_expect(__any(grow), 0)) {
+    const float m_new = grow ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+    l_run *= alpha;
+#pragma unroll
+    for (int b = 0; b < S::VGROUPS; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
+    m_run = m_new;
+  }
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m_run != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+  }
+  l_run += (p[0] + p[1]) + (p[2] + p[3]);
+  bf16x4 pop;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const __bf16 h = (__bf16)p[i];
+    const __bf16 l = (__bf16)(p[i] - (float)h);
+    pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
+  }
+
+  // PV: lane row c of slab b, step jj <-> dim 128b + 8c + jj; keys 4qg + [0, 4).  The
+  // transposed V operand is built from four 16-byte row reads with byte permutes
+  // (on gfx950 this measured faster than the LDS transpose load for this tile).
+#pragma unroll
+  for (int b = 0; b < S::VGROUPS; ++b) {
+    u32x4 w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = *reinterpret_cast<const u32x4*>(tile + (4 * qg + e) * S::P + S::TV + 128 * b + 8 * c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x2 even = {perm(w[1][u], w[0][u], 0x05040100u), perm(w[3][u], w[2][u], 0x05040100u)};
+      const u32x2 odd = {perm(w[1][u], w[0][u], 0x07060302u), perm(w[3][u], w[2][u], 0x07060302u)};
+      acc[b][2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, even), pop,
+                                                               acc[b][2 * u], 0, 0, 0);
+      acc[b][2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, odd),
+                                                                   pop, acc[b][2 * u + 1], 0, 0, 0);
+    }
+  }
+}
+
+// Zero the V rows of a staged tile whose keys lie outside [lo, hi), for the 4 rows
+// 4qg + e this lane group owns, so padding cannot leak through 0 * NaN.
+template <int D, bool FOLDED>
+__device__ __forceinline__ void zero_dead_rows(uint16_t* tile, int tok0, int lo, int hi, int c,
+                                               int qg, int e0, int e1) {
+  using S = Shape<D, FOLDED>;
+#pragma unroll
+  for (int e = e0; e < e1; ++e) {
+    const int t = tok0 + 4 * qg + e;
+    if (t < lo || t >= hi) {
+#pragma unroll
+      for (int b = 0; b < S::VGROUPS; ++b)
+        *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * S::P + S::TV + 128 * b + 8 * c) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Column of staged piece sb (128 elements each) in the stored row.
+template <int D, bool FOLDED>
+__device__ __forceinline__ int64_t src_col(const SplitArgs& a, int sb) {
+  constexpr int VG = D / 128;
+  if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
+  return sb < VG ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VG);
+}
+
+// Page ids of one table row, read once per page through the scalar cache with the next
+// page's id fetched a page ahead.  Lookups must be monotone in position.
+struct PageWalker {
+  const int32_t* trow;
+  int64_t num_pages;
+  int page_size, max_pages, cur_page;
+  int32_t cur_pid, next_pid;
+  __device__ __forceinline__ void start(int tok) {
+    cur_page = tok / page_size;
+    cur_pid = load_page_id(trow, cur_page);
+    next_pid = cur_page + 1 < max_pages ? load_page_id(trow, cur_page + 1) : -1;
+  }
+  // Page id of position tok (a tile never straddles two pages), -1 if outside the pool.
+  __device__ __forceinline__ int32_t page_of(int tok) {
+    const int page = tok / page_size;
+    if (page != cur_page) {
+      cur_page = page;
+      cur_pid = next_pid;
+      next_pid = page + 1 < max_pages ? load_page_id(trow, page + 1) : -1;
+    }
+    return (cur_pid < 0 || int64_t(cur_pid) >= num_pages) ? -1 : cur_pid;
+  }
+};
+
 template <int D, int G, bool FOLDED>
 __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
-  constexpr int KSTEPS = D / 32;    // 16x16x32 MFMA steps over the key dimension
-  constexpr int VGROUPS = D / 128;  // 128-dim slabs of V per tile
-  constexpr int ROT = FOLDED ? 128 : 0;
-  // Columns staged per row: split K | V (2D), folded rotated K | V (ROT + D).
-  constexpr int COLS = FOLDED ? ROT + D : 2 * D;
-  constexpr int SLABS = COLS / 128;  // 256-byte pieces per row
-  constexpr int P = RowTile<COLS>::kPitch;
-  // Staged-tile columns of the K part and of V.
-  constexpr int TK = 0;
-  constexpr int TV = FOLDED ? ROT : D;
+  using S = Shape<D, FOLDED>;
+  constexpr int KSTEPS = S::KSTEPS;
+  constexpr int VGROUPS = S::VGROUPS;
+  constexpr int COLS = S::COLS;
+  constexpr int SLABS = S::SLABS;
+  constexpr int P = S::P;
   static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
   __shared__ RowTile<COLS> tiles[kWavesPerBlock];
 
@@ -132,35 +300,18 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const int c0 = start + chunk * a.chunk_len + wave * quarter;
   const int c1 = min(c0 + quarter, L);
   const bool has_work = !poison && c0 < c1;
-  const int32_t* trow = a.table + int64_t(r) * a.max_pages;
   const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
   u32x4 stage[4][SLABS];
 
-  // Page ids are read once per page, the next page's id one page ahead; a tile
-  // never straddles two pages (16 divides the page size).
-  int cur_page = c0 / a.page_size;
-  int32_t cur_pid = -1, next_pid = -1;
-  if (has_work) {
-    cur_pid = load_page_id(trow, cur_page);
-    next_pid = cur_page + 1 < a.max_pages ? load_page_id(trow, cur_page + 1) : -1;
-  }
+  PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
+  if (has_work) pw.start(c0);
   // Resolve the tile's rows; false if the table entry is outside the pool.
   auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
-    const int page = tok0 / a.page_size;
-    if (page != cur_page) {
-      cur_page = page;
-      cur_pid = next_pid;
-      next_pid = page + 1 < a.max_pages ? load_page_id(trow, page + 1) : -1;
-    }
-    if (cur_pid < 0 || int64_t(cur_pid) >= a.num_pages) return false;
-    *base = head_base + int64_t(cur_pid) * a.page_stride +
-            int64_t(tok0 - page * a.page_size) * a.row_stride;
+    const int32_t pid = pw.page_of(tok0);
+    if (pid < 0) return false;
+    *base = head_base + int64_t(pid) * a.page_stride +
+            int64_t(tok0 % a.page_size) * a.row_stride;
     return true;
-  };
-  // Column of staged piece sb (128 elements each) in the stored row.
-  auto src_col = [&](int sb) -> int64_t {
-    if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
-    return sb < VGROUPS ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VGROUPS);
   };
   // Lane (c, qg) fetches rows 4qg + e, 16 bytes at 128 sb + 8c: every instruction
   // reads four whole 256-byte row pieces, so each line is requested once.
@@ -169,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
     for (int e = 0; e < 4; ++e) {
       const uint16_t* row = base + int64_t(4 * qg + e) * a.row_stride + 8 * c;
 #pragma unroll
-      for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col(sb));
+      for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col<D, FOLDED>(a, sb));
     }
   };
 
@@ -179,143 +330,41 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   if (has_work && !first_ok) poison = true;
   if (first_ok) load_tile(base);
 
-  // Query operand: column c holds head (c % G), high part for c < G, low part for
-  // G <= c < 2G, zero beyond.  Dims of k-step j for lane group qg: 32j + 8qg + [0, 8).
-  const int part = c / G;
-  const int hq = g * G + (c % G);
   bf16x8 qop[KSTEPS];
-  {
-    const float* qrow = a.q + (int64_t(r) * a.num_q_heads + hq) * D;
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      bf16x8 v;
-      if (part < 2) {
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg);
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * a.qscale;
-          const __bf16 h = (__bf16)x;
-          v[e] = part == 0 ? h : (__bf16)(x - (float)h);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qop[j] = v;
-    }
-  }
+  make_query_operand<D, G>(a.q + int64_t(r) * a.num_q_heads * D, g, c, qg, a.qscale, qop);
+  const int hq = g * G + (c % G);
 
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  floatx4 acc[VGROUPS][8];
+  floatx4 acc[D / 128][8];  // slab b, step jj: lane (c, qg) rows 4qg + i <-> dims 128b + 8(4qg+i) + jj
 #pragma unroll
-  for (int b = 0; b < VGROUPS; ++b)
+  for (int b = 0; b < D / 128; ++b)
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   if (first_ok) {
     int tok0 = c0;
     for (;;) {
-        const int next = tok0 + kTile;
-        bool has_next = next < c1;
-        const uint16_t* nbase = nullptr;
-        if (has_next && !tile_base(next, &nbase)) {
-          poison = true;
-          has_next = false;
-        }
-        // Stage the tile, then start fetching the next one.
+      const int next = tok0 + kTile;
+      bool has_next = next < c1;
+      const uint16_t* nbase = nullptr;
+      if (has_next && !tile_base(next, &nbase)) {
+        poison = true;
+        has_next = false;
+      }
+      // Stage the tile, then start fetching the next one.
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int sb = 0; sb < SLABS; ++sb)
-            *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = stage[e][sb];
-        if (has_next) load_tile(nbase);
-        // Keys outside [lo, L) (first tile of a window, tail of the last page): zero
-        // their V rows so that padding cannot leak through 0 * NaN.
-        const bool partial_tile = tok0 < lo || tok0 + kTile > L;
-        if (__builtin_expect(partial_tile, 0)) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = tok0 + 4 * qg + e;
-            if (t < lo || t >= L) {
-#pragma unroll
-              for (int b = 0; b < VGROUPS; ++b)
-                *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + TV + 128 * b + 8 * c) =
-                    u32x4{0u, 0u, 0u, 0u};
-            }
-          }
-        }
-
-        // Scores of 16 keys x 16 columns (hi/lo parts of the G heads).  Key dim kd
-        // sits at staged column kd (split / rotated part) or TV + kd (folded, kd >= ROT).
-        floatx4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KSTEPS; ++j) {
-          const int kd = 32 * j + 8 * qg;
-          const int col = (FOLDED && kd >= ROT) ? TV + kd : TK + kd;
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(tile + c * P + col);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[j], s, 0,
-                                                      0, 0);
-        }
-
-        // Online softmax over this tile (base 2); lane holds keys tok0 + 4qg + i.
-        float sc[4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float full = s[i] + partner<G>(s[i]);
-          const int t = tok0 + 4 * qg + i;
-          sc[i] = (t >= lo && t < L) ? full : -INFINITY;
-          mx = fmaxf(mx, sc[i]);
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        // Move the reference maximum only when this tile exceeds it by the slack.
-        const bool grow = mx > m_run + kRescaleSlack;
-        if (__builtin_expect(__any(grow), 0)) {
-          const float m_new = grow ? mx : m_run;
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
-          l_run *= alpha;
-#pragma unroll
-          for (int b = 0; b < VGROUPS; ++b)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
-          m_run = m_new;
-        }
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-        if (m_run != -INFINITY) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
-        }
-        l_run += (p[0] + p[1]) + (p[2] + p[3]);
-        bf16x4 pop;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const __bf16 h = (__bf16)p[i];
-          const __bf16 l = (__bf16)(p[i] - (float)h);
-          pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
-        }
-
-        // PV: lane row c of slab b, step jj <-> dim 128b + 8c + jj; keys 4qg + [0, 4).
-#pragma unroll
-        for (int b = 0; b < VGROUPS; ++b) {
-          u32x4 w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = *reinterpret_cast<const u32x4*>(tile + (4 * qg + e) * P + TV + 128 * b + 8 * c);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const u32x2 even = {perm(w[1][u], w[0][u], 0x05040100u), perm(w[3][u], w[2][u], 0x05040100u)};
-            const u32x2 odd = {perm(w[1][u], w[0][u], 0x07060302u), perm(w[3][u], w[2][u], 0x07060302u)};
-            acc[b][2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(bf16x4, even), pop, acc[b][2 * u], 0, 0, 0);
-            acc[b][2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(bf16x4, odd), pop, acc[b][2 * u + 1], 0, 0, 0);
-          }
-        }
-        if (!has_next) break;
-        tok0 = next;
+        for (int sb = 0; sb < SLABS; ++sb)
+          *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = stage[e][sb];
+      if (has_next) load_tile(nbase);
+      // Keys outside [lo, L): first tile of a window, tail of the last page.
+      if (__builtin_expect(tok0 < lo || tok0 + kTile > L, 0))
+        zero_dead_rows<D, FOLDED>(tile, tok0, lo, L, c, qg, 0, 4);
+      tile_math<D, G, FOLDED>(tile, tok0, lo, L, qop, c, qg, m_run, l_run, acc);
+      if (!has_next) break;
+      tok0 = next;
     }
   }
 
@@ -323,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
 #pragma unroll
-  for (int b = 0; b < VGROUPS; ++b)
+  for (int b = 0; b < D / 128; ++b)
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
@@ -345,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
       mine->l[c] = l_run;
     }
 #pragma unroll
-    for (int b = 0; b < VGROUPS; ++b)
+    for (int b = 0; b < D / 128; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 128 * b + 32 * qg + 8 * i;  // dims d .. d + 7
@@ -389,6 +438,147 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
       a.part_l[st] = S;
     }
     *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O;
+  }
+}
+
+// Write one query row's chunk state: low columns added onto the high ones, maximum in
+// natural-log units, NaN everywhere if the chunk was poisoned.
+template <int D, int G>
+__device__ __forceinline__ void write_row_state(const SplitArgs& a, int64_t st, int c, int qg,
+                                                bool poison, float m_run, float l_run,
+                                                floatx4 (&acc)[D / 128][8]) {
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+#pragma unroll
+  for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][jj][i] += partner<G>(acc[b][jj][i]);
+  if (c >= G) return;
+  const float qnan = __builtin_nanf("");
+  if (qg == 0) {
+    a.part_m[st] = poison ? qnan : (m_run == -INFINITY ? -INFINITY : m_run * kLn2);
+    a.part_l[st] = poison ? qnan : l_run;
+  }
+  float* o = a.part_o + st * D;
+#pragma unroll
+  for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx4 w0 = {acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+      floatx4 w1 = {acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
+      if (poison) w0 = w1 = floatx4{qnan, qnan, qnan, qnan};
+      float* dst = o + 128 * b + 32 * qg + 8 * i;
+      *reinterpret_cast<floatx4*>(dst) = w0;
+      *reinterpret_cast<floatx4*>(dst + 4) = w1;
+    }
+}
+
+// Several query rows per request (a verify window): row i sits at position
+// L - rows + i and attends causally.  One workgroup = one key chunk of one (request,
+// KV head, group of up to four rows); wave w serves row 4*group + w.  The four waves
+// fetch each tile together (wave w the rows 4qg + w) into a double-buffered LDS tile,
+// so every K/V byte is read once for all the rows of the group.  Workgroups of the
+// same chunk and different row groups are 8 apart in launch order, i.e. on the same
+// XCD, so the later group finds the rows in that XCD's L2.
+template <int D, int G, bool FOLDED>
+__global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
+  using S = Shape<D, FOLDED>;
+  static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
+  __shared__ RowTile<S::COLS> tiles[2];
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int qg = lane >> 4;
+  const int wave = threadIdx.x >> 6;
+  const int lo8 = blockIdx.x % 8;
+  const int hi8 = blockIdx.x / 8;
+  const int rg = hi8 % a.row_groups;
+  const int chunk = (hi8 / a.row_groups) * 8 + lo8;
+  const int g = blockIdx.y;
+  const int r = blockIdx.z;
+  if (chunk >= a.num_chunks) return;  // padding of the launch order (whole workgroup)
+
+  const int rows = a.num_rows;
+  const int row = rg * kWavesPerBlock + wave;
+  const bool row_active = row < rows;
+  const int L = a.seq_lens[r];
+  const int first_hi = L - rows + 1;  // keys the first row sees: [.., first_hi)
+  const int lo_all = (a.window > 0 && first_hi > a.window) ? first_hi - a.window : 0;
+  const int hi = L - rows + row + 1;  // this wave's row
+  const int lo = (a.window > 0 && hi > a.window) ? hi - a.window : 0;
+  const int start = lo_all & ~(kTile - 1);
+  const int64_t cap = int64_t(a.max_pages) * a.page_size;
+  bool poison = L < rows || int64_t(L) > cap ||
+                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
+  const int c0 = start + chunk * a.chunk_len;
+  const int c1 = min(c0 + a.chunk_len, L);
+  const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
+
+  PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
+  // Three tiles stream ahead of the math; each register set holds this wave's quarter
+  // of one tile (rows 4qg + wave, 16 bytes at 128 sb + 8c).
+  constexpr int kAhead = 3;
+  u32x4 stage[kAhead][S::SLABS];
+  int end = (!poison && c0 < c1) ? c1 : c0;  // tiles from `end` on are not processed
+  auto fetch = [&](u32x4 (&buf)[S::SLABS], int tok0) {
+    const int32_t pid = pw.page_of(tok0);
+    if (pid < 0) {
+      poison = true;
+      end = tok0;
+      return;
+    }
+    const uint16_t* row_ptr = head_base + int64_t(pid) * a.page_stride +
+                              int64_t(tok0 % a.page_size + 4 * qg + wave) * a.row_stride + 8 * c;
+#pragma unroll
+    for (int sb = 0; sb < S::SLABS; ++sb) buf[sb] = load_nt(row_ptr + src_col<D, FOLDED>(a, sb));
+  };
+  if (c0 < end) {
+    pw.start(c0);
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+      if (c0 + k * kTile < end) fetch(stage[k], c0 + k * kTile);
+  }
+  bf16x8 qop[S::KSTEPS];
+  if (row_active)
+    make_query_operand<D, G>(a.q + (int64_t(r) * rows + row) * a.num_q_heads * D, g, c, qg, a.qscale,
+                             qop);
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  floatx4 acc[D / 128][8];  // slab b, step jj: lane (c, qg) rows 4qg + i <-> dims 128b + 8(4qg+i) + jj
+#pragma unroll
+  for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // One tile: stage this wave's quarter into the shared buffer, refill the registers
+  // kAhead tiles ahead, wait for the whole tile, then this wave's row does the math.
+  // Every wave runs the same tiles, so the barrier is uniform over the workgroup.
+  int buf = 0;
+  auto step = [&](u32x4 (&regs)[S::SLABS], int tok0) {
+    uint16_t* tile = tiles[buf].v;
+#pragma unroll
+    for (int sb = 0; sb < S::SLABS; ++sb)
+      *reinterpret_cast<u32x4*>(tile + (4 * qg + wave) * S::P + 128 * sb + 8 * c) = regs[sb];
+    if (tok0 + kAhead * kTile < end) fetch(regs, tok0 + kAhead * kTile);
+    if (__builtin_expect(tok0 < lo_all || tok0 + kTile > L, 0))
+      zero_dead_rows<D, FOLDED>(tile, tok0, lo_all, L, c, qg, wave, wave + 1);
+    __syncthreads();  // the tile is complete; the other buffer is free again
+    if (row_active) tile_math<D, G, FOLDED>(tile, tok0, lo, hi, qop, c, qg, m_run, l_run, acc);
+    buf ^= 1;
+  };
+  for (int tok0 = c0; tok0 < end; tok0 += kAhead * kTile) {
+    step(stage[0], tok0);
+    if (tok0 + kTile >= end) break;
+    step(stage[1], tok0 + kTile);
+    if (tok0 + 2 * kTile >= end) break;
+    step(stage[2], tok0 + 2 * kTile);
+  }
+  if (row_active) {
+    const int hq = g * G + (c % G);
+    const int64_t st = ((int64_t(r) * rows + row) * a.num_q_heads + hq) * a.num_chunks + chunk;
+    write_row_state<D, G>(a, st, c, qg, poison, m_run, l_run, acc);
   }
 }
 
@@ -554,13 +744,17 @@ __global__ __launch_bounds__(256) void query_fold_kernel(const float* q, const f
 
 template <int D, int G, bool FOLDED>
 void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
-                     args);
+  if (args.num_rows > 1)
+    hipLaunchKernelGGL((rows_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
+                       args);
+  else
+    hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
+                       args);
 }
 
 template <int D>
 void launch_merge(const attn_decode_plan_t& p, char* ws, float* out, hipStream_t s) {
-  const int64_t bh = int64_t(p.desc.batch) * p.desc.num_q_heads;
+  const int64_t bh = int64_t(p.desc.batch) * p.num_rows * p.desc.num_q_heads;
   MergeArgs m{reinterpret_cast<const float*>(ws + p.off_part_m),
               reinterpret_cast<const float*>(ws + p.off_part_l),
               reinterpret_cast<const float*>(ws + p.off_part_o), out, p.num_chunks, p.merge_group};
@@ -607,9 +801,11 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   args.window = d.window;
   args.chunk_len = plan->chunk_len;
   args.num_chunks = plan->num_chunks;
+  args.num_rows = plan->num_rows;
+  args.row_groups = plan->row_groups;
   args.qscale = d.scale * kLog2e;
 
-  const dim3 grid(plan->num_chunks, d.num_kv_heads, d.batch);
+  const dim3 grid(plan->grid_x, d.num_kv_heads, d.batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)

@@ -60,7 +60,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   const attn_decode_desc& d = *desc;
   if (d.batch < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.head_dim < 1 ||
       d.page_size < 1 || d.max_pages_per_seq < 1 || d.window < 0 || d.num_chunks < 0 ||
-      d.merge_group < 0 || d.num_pages < 1)
+      d.merge_group < 0 || d.num_pages < 1 || d.num_rows < 0)
     return ATTN_E_INVALID_ARG;
   if (d.num_q_heads % d.num_kv_heads != 0) return ATTN_E_UNSUPPORTED;
   if (d.format != ATTN_KV_SPLIT && d.format != ATTN_KV_FOLDED) return ATTN_E_INVALID_ARG;
@@ -85,35 +85,45 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
       return ATTN_E_OVERFLOW;
   }
 
-  // Lengths: 1 <= L <= pages in a table row * page size.
+  // Query rows: 1 = ordinary decode; a window of n rows uses groups of four rows.
+  const int64_t rows = d.num_rows < 1 ? 1 : d.num_rows;
+  if (rows > kMaxRows) return ATTN_E_INVALID_ARG;
+  const int64_t groups = rows > 1 ? ceil_div(rows, kWavesPerBlock) : 1;
+
+  // Lengths: rows <= L <= pages in a table row * page size.
   const int64_t cap = int64_t(d.max_pages_per_seq) * d.page_size;
   int64_t max_span = 0;
   for (int r = 0; r < d.batch; ++r) {
     const int64_t L = lens[r];
-    if (L < 1) return ATTN_E_INVALID_ARG;
+    if (L < 1 || L < rows) return ATTN_E_INVALID_ARG;
     if (L > cap) return ATTN_E_PAST_PAGES;
-    const int64_t lo = d.window > 0 && L > d.window ? L - d.window : 0;
+    const int64_t first_hi = L - rows + 1;  // keys the first row sees: [.., first_hi)
+    const int64_t lo = d.window > 0 && first_hi > d.window ? first_hi - d.window : 0;
     const int64_t start = lo / kTile * kTile;
     if (L - start > max_span) max_span = L - start;
   }
   if (max_span > INT32_MAX) return ATTN_E_OVERFLOW;
 
-  // Chunking: one chunk per workgroup, one quarter of it per wave, so that every
-  // SIMD of the chip streams one quarter; a quarter is never shorter than a tile.
-  // An explicit count is honoured (trailing chunks may then be empty).
+  // Chunking.  One row: one chunk per workgroup, one quarter of it per wave, so that
+  // every SIMD of the chip streams one quarter; a quarter is never shorter than a
+  // tile.  Several rows: the four waves share each tile (one row each), so a chunk is
+  // whole tiles.  An explicit count is honoured (trailing chunks may then be empty).
+  const int64_t split = rows > 1 ? 1 : kWavesPerBlock;  // waves a chunk is cut into
   const int64_t tiles = ceil_div(max_span, kTile);
   int64_t n = d.num_chunks;
   if (n == 0) {
-    const int64_t units = int64_t(d.batch) * d.num_kv_heads;
+    const int64_t units = int64_t(d.batch) * d.num_kv_heads * groups;
     n = ceil_div(kTargetWaves / kWavesPerBlock, units);
-    const int64_t most = ceil_div(tiles, kWavesPerBlock);
+    const int64_t most = ceil_div(tiles, split);
     if (n > most) n = most;
     if (n < 1) n = 1;
   }
   if (n > (int64_t(1) << 24)) return ATTN_E_OVERFLOW;
-  const int64_t quarter_tiles = ceil_div(tiles, n * kWavesPerBlock);
-  const int64_t chunk_len = quarter_tiles * kTile * kWavesPerBlock;
+  const int64_t piece_tiles = ceil_div(tiles, n * split);
+  const int64_t chunk_len = piece_tiles * kTile * split;
   if (d.num_chunks == 0) n = ceil_div(max_span, chunk_len);
+  // Launch order of the multi-row kernel: row groups of a chunk 8 workgroups apart.
+  const int64_t grid_x = groups > 1 ? ceil_div(n, 8) * 8 * groups : n;
 
   // Level-1 groups: at most kMergeGroups per (request, head), so the merge's second
   // level fits one workgroup.
@@ -123,8 +133,8 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   if (gm > n) gm = n;
   const int64_t ng = ceil_div(n, gm);
 
-  // Grid limits: blocks along x carry chunks, y the KV heads, z the requests.
-  if (n > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535 ||
+  // Grid limits: blocks along x carry chunks (and row groups), y the KV heads, z the requests.
+  if (grid_x > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535 ||
       d.num_q_heads > 65535)
     return ATTN_E_OVERFLOW;
 
@@ -139,9 +149,13 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   p.merge_group = int32_t(gm);
   p.num_groups = int32_t(ng);
   p.max_span = int32_t(max_span);
+  p.num_rows = int32_t(rows);
+  p.row_groups = int32_t(groups);
+  p.grid_x = int32_t(grid_x);
 
-  uint64_t bh, states, elems;
-  if (!mul_ok(uint64_t(d.batch), uint64_t(d.num_q_heads), &bh) ||
+  uint64_t brows, bh, states, elems;
+  if (!mul_ok(uint64_t(d.batch), uint64_t(rows), &brows) ||
+      !mul_ok(brows, uint64_t(d.num_q_heads), &bh) ||
       !mul_ok(bh, uint64_t(n), &states) || !mul_ok(states, uint64_t(d.head_dim), &elems))
     return ATTN_E_OVERFLOW;
   if (bh > 65535) return ATTN_E_OVERFLOW;  // merge grid rows

@@ -12,6 +12,7 @@ constexpr int kTile = 16;            // keys per tile = rows of one 16x16 MFMA b
 constexpr int kWavesPerBlock = 4;    // one chunk per workgroup, one quarter per wave
 constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
+constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)
 
 bool shape_supported(const attn_decode_desc& d);
 int64_t row_extent(const attn_decode_desc& d);

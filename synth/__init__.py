@@ -68,15 +68,17 @@ class Workload:
     seq_lens: np.ndarray     # int32 [B]
     fold_w: Optional[np.ndarray] = None   # float32 [D - rot_cols] (folded pair only)
     q_unfolded: Optional[np.ndarray] = None
+    num_rows: int = 1        # query rows per request; > 1 makes q [B][rows][Hq][D]
 
     @property
     def group_size(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
     def visible(self, r: int) -> tuple[int, int]:
-        """[lo, hi) of the key positions request r attends to (data layout helper)."""
+        """[lo, hi) of the key positions request r's rows attend to, together."""
         L = int(self.seq_lens[r])
-        lo = max(0, L - self.window) if self.window > 0 else 0
+        first = L - self.num_rows + 1      # keys the first query row sees: [.., first)
+        lo = max(0, first - self.window) if self.window > 0 else 0
         return lo, L
 
     def desc_fields(self, num_chunks: int = 0, merge_group: int = 0) -> dict:
@@ -88,7 +90,8 @@ class Workload:
                     window=self.window, num_chunks=num_chunks, merge_group=merge_group,
                     scale=self.scale, num_pages=self.num_pages, page_stride=self.page_stride,
                     head_stride=self.head_stride, row_stride=self.row_stride,
-                    k_offset=self.k_offset, v_offset=self.v_offset)
+                    k_offset=self.k_offset, v_offset=self.v_offset,
+                    num_rows=self.num_rows)
 
     def kv_bytes(self) -> int:
         """Bytes of K/V rows a decode step must stream (visible keys only)."""
@@ -148,7 +151,7 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                   rot_cols: int = 128, seed: int = 0, table_seed: Optional[int] = None,
                   layout: str = HEAD_MAJOR, spare_pages: int = 4, pad: str = "nan",
                   max_pages: Optional[int] = None, extra_page: bool = True,
-                  scale: Optional[float] = None) -> Workload:
+                  scale: Optional[float] = None, num_rows: int = 1) -> Workload:
     """Build a decode-step workload.
 
     Data is drawn per (request, logical page) in ascending order from ``seed``;
@@ -156,6 +159,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     (default ``seed + 1000``), so two workloads that differ only in
     ``table_seed`` hold the same logical rows at different physical pages.
     Slots outside a request's visible keys and unused pages hold ``pad``.
+    ``num_rows`` > 1 gives every request a window of that many query rows (the last
+    positions of the request), q shaped [B][rows][Hq][D].
     """
     seq_lens = [int(x) for x in seq_lens]
     B = len(seq_lens)
@@ -168,7 +173,11 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
         raise ValueError(fmt)
     if max_pages is None:
         max_pages = max((L + page_size - 1) // page_size for L in seq_lens)
-    spans = [resident_pages(L, page_size, window, extra_page) for L in seq_lens]
+    if num_rows < 1 or any(L < num_rows for L in seq_lens):
+        raise ValueError("every request needs at least num_rows keys")
+    # the first row of a window sees keys [.., L - num_rows + 1): its window reaches furthest back
+    spans = [resident_pages(L, page_size, window + num_rows - 1 if window > 0 else 0, extra_page)
+             for L in seq_lens]
     needed = sum(p1 - p0 for p0, p1 in spans)
     num_pages = needed + spare_pages
     page_stride, head_stride, row_stride = _strides(layout, num_kv_heads, page_size, row_cols)
@@ -177,14 +186,15 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     tgen = _gen(seed + 1000 if table_seed is None else table_seed)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
-    q = torch.randn(B, num_q_heads, D, generator=gen, dtype=torch.float32).numpy()
+    qshape = (B, num_q_heads, D) if num_rows == 1 else (B, num_rows, num_q_heads, D)
+    q = torch.randn(*qshape, generator=gen, dtype=torch.float32).numpy()
     fold_w = None
     q_unfolded = None
     if fmt == FOLDED:
         fold_w = (torch.rand(D - rot, generator=gen, dtype=torch.float32) + 0.5).numpy()
         q_unfolded = q.copy()
         q = q.copy()
-        q[:, :, rot:] = (q_unfolded[:, :, rot:] * fold_w).astype(np.float32)
+        q[..., rot:] = (q_unfolded[..., rot:] * fold_w).astype(np.float32)
 
     padv = np.uint16(PADS[pad])
     pool = np.full(num_pages * page_stride, padv, dtype=np.uint16)
@@ -195,7 +205,7 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     k = 0
     for r, L in enumerate(seq_lens):
         p0, p1 = spans[r]
-        lo = max(0, L - window) if window > 0 else 0
+        lo = max(0, L - num_rows + 1 - window) if window > 0 else 0
         for j in range(p0, p1):
             pid = int(perm[k]); k += 1
             table[r, j] = pid
@@ -213,7 +223,7 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                     head_stride=head_stride, row_stride=row_stride, k_offset=k_off,
                     v_offset=v_off, q=q, pool=pool, table=table,
                     seq_lens=np.asarray(seq_lens, dtype=np.int32), fold_w=fold_w,
-                    q_unfolded=q_unfolded)
+                    q_unfolded=q_unfolded, num_rows=num_rows)
 
 
 def _store_page(dst: np.ndarray, block: np.ndarray, layout: str, hkv: int, ps: int, cols: int):

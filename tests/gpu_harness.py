@@ -43,7 +43,7 @@ class Device:
         nws = int(self.plan.workspace_bytes)
         self.ws_buf = torch.full((nws + WS_GUARD,), 0xA5, dtype=torch.uint8, device=dev)
         self.ws = self.ws_buf[:nws]
-        n = wl.batch * wl.num_q_heads * wl.head_dim
+        n = wl.batch * wl.num_rows * wl.num_q_heads * wl.head_dim
         self.out_buf = torch.full((n + 2 * GUARD,), 0, dtype=torch.int32, device=dev)
         self.out_buf.fill_(SENTINEL)
         self.out_f = self.out_buf.view(torch.float32)
@@ -61,7 +61,9 @@ class Device:
 
     def result(self) -> np.ndarray:
         wl = self.wl
-        return self.out.cpu().numpy().reshape(wl.batch, wl.num_q_heads, wl.head_dim).copy()
+        shape = (wl.batch, wl.num_q_heads, wl.head_dim) if wl.num_rows == 1 else \
+            (wl.batch, wl.num_rows, wl.num_q_heads, wl.head_dim)
+        return self.out.cpu().numpy().reshape(shape).copy()
 
     def guards_intact(self) -> bool:
         ob = self.out_buf.cpu().numpy()
@@ -73,7 +75,7 @@ class Device:
         """(m, l, o) chunk states as numpy: [B][Hq][n], [B][Hq][n], [B][Hq][n][D]."""
         p, wl = self.plan, self.wl
         ws = self.ws.cpu().numpy()
-        B, H, n, D = wl.batch, wl.num_q_heads, p.num_chunks, wl.head_dim
+        B, H, n, D = wl.batch * wl.num_rows, wl.num_q_heads, p.num_chunks, wl.head_dim
 
         def region(off, count):
             return ws[off:off + 4 * count].view(np.float32)
@@ -85,7 +87,8 @@ class Device:
     def chunk_ranges(self, r):
         p = self.plan
         L = int(self.wl.seq_lens[r])
-        lo = max(0, L - p.desc.window) if p.desc.window > 0 else 0
+        first_hi = L - self.wl.num_rows + 1
+        lo = max(0, first_hi - p.desc.window) if p.desc.window > 0 else 0
         start = lo // p.tile * p.tile
         return [(start + c * p.chunk_len, start + (c + 1) * p.chunk_len) for c in range(p.num_chunks)]
 

@@ -25,6 +25,21 @@ def _bf16_to_float(bits: int) -> float:
     return struct.unpack(">f", struct.pack(">I", (int(bits) & 0xFFFF) << 16))[0]
 
 
+def brute_force_rows(wl) -> np.ndarray:
+    """Multi-row window by brute force: row i is single-row decode of length L - n + 1 + i,
+    evaluated by brute_force_decode on a copy whose lengths are cut to that value."""
+    import copy
+    n = wl.num_rows
+    out = np.zeros((wl.batch, n, wl.num_q_heads, wl.head_dim))
+    for i in range(n):
+        one = copy.copy(wl)
+        one.num_rows = 1
+        one.q = np.ascontiguousarray(wl.q[:, i])
+        one.seq_lens = (wl.seq_lens - n + 1 + i).astype(np.int32)
+        out[:, i] = brute_force_decode(one)
+    return out
+
+
 def brute_force_decode(wl) -> np.ndarray:
     """Pure-Python decode attention: explicit flat indexing, exp without max shift, fsum.
 
@@ -349,7 +364,35 @@ def pin_fail_closed():
         raise AssertionError("finalize of the empty state returned")
 
 
+def pin_query_rows():
+    """A window of n query rows: row i is ordinary decode at length L - n + 1 + i (brute
+    force per row), the last row is the single-row decode of the whole context, and the
+    first row of an n-row window over L keys equals the last row of a window over
+    L - n + 1 keys.  Whole context and sliding window."""
+    for W, fmt in ((0, "split"), (6, "split"), (0, "folded")):
+        D = 17 if fmt == "split" else 512
+        wl = synth.make_workload([9, 4, 16], num_q_heads=4, num_kv_heads=2, head_dim=D, page_size=4,
+                                 window=W, fmt=fmt, seed=30, num_rows=4, pad="big", spare_pages=2)
+        got = oracle.decode_attention(wl)
+        assert got.shape == (3, 4, 4, D)
+        _assert_close(got, brute_force_rows(wl), 1e-13, f"rows W={W} {fmt}")
+    wl = synth.make_workload([40, 33], num_q_heads=8, num_kv_heads=1, head_dim=64, page_size=8,
+                             seed=31, num_rows=5)
+    rows = oracle.decode_attention(wl)
+    import copy
+    last = copy.copy(wl)
+    last.num_rows = 1
+    last.q = np.ascontiguousarray(wl.q[:, -1])
+    assert np.array_equal(rows[:, -1], oracle.decode_attention(last))
+    first = copy.copy(wl)
+    first.num_rows = 1
+    first.q = np.ascontiguousarray(wl.q[:, 0])
+    first.seq_lens = (wl.seq_lens - 4).astype(np.int32)
+    assert np.array_equal(rows[:, 0], oracle.decode_attention(first))
+
+
 ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, pin_needle,
             pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
             pin_empty_merge_identity, pin_merge_identity_values, pin_window,
-            pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed]
+            pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed,
+            pin_query_rows]

@@ -1,0 +1,72 @@
+"""GPU parity of multi-row decode (a window of query rows per request, causal inside
+the window) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_harness import Device, note
+from tests.test_gpu_parity import check, run_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_rows_global(rows, fmt):
+    wl = synth.make_workload([3000, 777, rows + 5], **synth.GLOBAL, fmt=fmt, seed=40 + rows,
+                             num_rows=rows, pad="nan")
+    dev, got = run_case(wl, f"rows={rows} {fmt}")
+    assert dev.plan.num_rows == rows
+    check(got, oracle.decode_attention(wl), f"rows={rows} {fmt}")
+
+
+@pytest.mark.parametrize("rows", [2, 4, 7])
+def test_rows_sliding_window(rows):
+    wl = synth.make_workload([1030, 1024 + rows - 1, 40, 3000], **synth.SLIDING, seed=50 + rows,
+                             num_rows=rows, pad="nan", max_pages=64)
+    _, got = run_case(wl, f"sliding rows={rows}")
+    check(got, oracle.decode_attention(wl), f"sliding rows={rows}")
+
+
+def test_rows_minimal_lengths_and_explicit_chunks():
+    """L == rows (the first row sees one key: exactly v_0), and more chunks than tiles."""
+    wl = synth.make_workload([4, 4], **synth.GLOBAL, seed=60, num_rows=4, pad="big")
+    dev, got = run_case(wl, "rows=4 L=4 n=9", num_chunks=9)
+    check(got, oracle.decode_attention(wl), "rows L=4")
+    v0 = oracle.gather_rows(wl, 0, 0, np.array([0]))[0][512:1024]
+    v0 = (v0.astype(np.uint32) << 16).view(np.float32)
+    for h in range(8):
+        assert np.array_equal(got[0, 0, h].view(np.uint32), v0.view(np.uint32))
+
+
+def test_rows_partials_per_chunk():
+    wl = synth.make_workload([900], **synth.GLOBAL, seed=61, num_rows=3)
+    dev, got = run_case(wl, "rows=3 partials n=5", num_chunks=5)
+    m, l, o = dev.partials()
+    ranges = dev.chunk_ranges(0)
+    for row in range(3):
+        for g in range(4):
+            states = oracle.paged_partials(wl, 0, g, ranges, row=row)
+            for i in range(8):
+                h = g * 8 + i
+                for c, st in enumerate(states[i]):
+                    b = row  # partial rows are (request * rows + row)
+                    if st.m == -math.inf:
+                        assert m[b, h, c] == -np.inf and l[b, h, c] == 0
+                        continue
+                    mg = float(m[b, h, c])
+                    assert st.m - 8 * math.log(2) - 1e-5 <= mg <= st.m + 1e-5 * max(1, abs(st.m))
+                    k = math.exp(mg - st.m)
+                    assert abs(l[b, h, c] * k - st.l) <= 1e-5 * st.l
+                    assert np.max(np.abs(o[b, h, c] * k / st.l - st.acc / st.l)) <= 1e-4
+    check(got, oracle.decode_attention(wl), "rows partial case")
+
+
+def test_rows_full_size_163k():
+    note("[gpu] rows=4 at 163,336: generating")
+    wl = synth.make_workload([163336], **synth.GLOBAL, seed=62, num_rows=4, spare_pages=1)
+    dev, got = run_case(wl, "rows=4 L=163336")
+    check(got, oracle.decode_attention(wl), "rows=4 163K")

@@ -229,3 +229,22 @@ def test_status_strings():
         s = K.attn_decode_status_string(code)
         assert s and s != "unknown status", name
     assert K.attn_decode_status_string(12345) == "unknown status"
+
+
+def test_rows_plan():
+    rc, p = plan_status([1000, 2000], **global_desc(2048, batch=2, num_rows=4))
+    assert rc == 0 and p.num_rows == 4 and p.row_groups == 1 and p.grid_x == p.num_chunks
+    assert p.chunk_len % 16 == 0
+    rc, p = plan_status([1000], **global_desc(1024, num_rows=8))
+    assert rc == 0 and p.row_groups == 2 and p.grid_x == -(-p.num_chunks // 8) * 8 * 2
+    # workspace counts request x row states
+    rc, p1 = plan_status([1000], **global_desc(1024, num_rows=1, num_chunks=16))
+    rc, p3 = plan_status([1000], **global_desc(1024, num_rows=3, num_chunks=16))
+    assert p3.workspace_bytes >= 3 * (p1.workspace_bytes - 512)
+    rc, _ = plan_status([3], **global_desc(1024, num_rows=4))
+    assert rc == S["ATTN_E_INVALID_ARG"]          # fewer keys than rows
+    rc, _ = plan_status([1000], **global_desc(1024, num_rows=65))
+    assert rc == S["ATTN_E_INVALID_ARG"]
+    rc, _ = plan_status([1000], **global_desc(1024, num_rows=-1))
+    assert rc == S["ATTN_E_INVALID_ARG"]
+

@@ -103,7 +103,25 @@ _orig_keys_values = OA.keys_values
 _orig_dense = OA.dense_attention
 _orig_visible = OA.visible_range
 
+def _rows_off_by_one(wl):
+    n = getattr(wl, "num_rows", 1)
+    if n == 1:
+        return _orig_decode(wl)
+    import copy
+    one = copy.copy(wl)
+    one.num_rows = 1
+    outs = []
+    for i in range(n):
+        one.q = np.ascontiguousarray(wl.q[:, i])
+        one.seq_lens = np.minimum(wl.seq_lens - n + 2 + i, wl.seq_lens).astype(np.int32)
+        outs.append(_orig_decode(one))
+    return np.stack(outs, axis=1)
+
+
+_orig_decode = OA.decode_attention
+
 MUTANTS = {
+    "rows_see_one_key_too_many": ("decode_attention", _rows_off_by_one),
     "k_v_swapped": ("keys_values", _kv_swapped),
     "gqa_modulo": ("decode_attention", _gqa_modulo),
     "scale_dropped": ("dense_attention", _no_scale),
