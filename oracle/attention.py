@@ -32,8 +32,18 @@ What it computes, and where the pages fix it
   merge runs in two levels: groups of consecutive chunk partials first, then the
   group states (pegainfer PR #1055, Description).
 
-All arithmetic is float64.  bf16 inputs widen exactly; fp32 queries widen
-exactly.  Library primitives used as steps: numpy's matmul, exp, max and sum.
+* Stored element types (the KV precisions other than bf16: F32 KV in the gem design
+  note, "Fixed production shape"; F16 and quantised KV named there as separate axes).
+  Reading taken for "quantised": FP8 E4M3 as defined by the OCP 8-bit floating point
+  specification (OFP8, the E4M3 encoding: bias 7, three mantissa bits, subnormals,
+  no infinities, only S.1111.111 is NaN), with one dequantisation factor for all of K
+  and one for all of V: the key used is stored value * k_scale, the value
+  stored value * v_scale.  Other element types take factors too (1 by default).
+
+All arithmetic is float64.  Every stored element type widens exactly (bf16, f16,
+FP8 and f32 values are all float64 values); fp32 queries widen exactly.  Library
+primitives used as steps: numpy's matmul, exp, max and sum, and numpy's IEEE binary16
+and binary32 types for widening f16 and f32 bit patterns.
 """
 from __future__ import annotations
 
@@ -44,7 +54,8 @@ from typing import Sequence
 import numpy as np
 
 __all__ = [
-    "InvalidState", "State", "bf16_bits_to_f64", "visible_range", "row_view", "gather_rows",
+    "InvalidState", "State", "bf16_bits_to_f64", "f16_bits_to_f64", "e4m3_bits_to_f64",
+    "f32_bits_to_f64", "stored_to_f64", "visible_range", "row_view", "gather_rows",
     "keys_values", "dense_attention", "decode_attention", "partial_state", "empty_state",
     "merge", "finalize", "split_kv_attention", "paged_partials", "validate",
 ]
@@ -60,6 +71,50 @@ class InvalidState(ValueError):
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 is the upper half of an IEEE binary32, so widening is exact."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns to float64 (numpy's half type as the widening step)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes to float64, from the encoding's fields.
+
+    sign s = bit 7, exponent e = bits 6..3 (bias 7), mantissa m = bits 2..0:
+      e == 0      : (-1)^s * m/8 * 2^(1-7)       (subnormal; m = 0 gives +-0)
+      otherwise   : (-1)^s * (1 + m/8) * 2^(e-7)
+      e = 15, m = 7 : NaN (the only non-finite codes; there is no infinity)
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** (1 - 7), (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((b & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def f32_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary32 bit patterns to float64."""
+    return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+
+
+def stored_to_f64(bits: np.ndarray, kv_dtype: str = "bf16") -> np.ndarray:
+    """Stored element bit patterns of the given type, widened to float64 (no scaling)."""
+    if kv_dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if kv_dtype == "f16":
+        return f16_bits_to_f64(bits)
+    if kv_dtype == "fp8_e4m3":
+        return e4m3_bits_to_f64(bits)
+    if kv_dtype == "f32":
+        return f32_bits_to_f64(bits)
+    raise ValueError(f"unknown element type {kv_dtype}")
+
+
+def _stored_rows(wl, r: int, g: int, positions: np.ndarray) -> np.ndarray:
+    return stored_to_f64(gather_rows(wl, r, g, positions), getattr(wl, "kv_dtype", "bf16"))
 
 
 def visible_range(L: int, window: int) -> tuple[int, int]:
@@ -82,7 +137,7 @@ def row_view(wl) -> np.ndarray:
 
 
 def gather_rows(wl, r: int, g: int, positions: np.ndarray) -> np.ndarray:
-    """bf16 bits of the stored rows of KV head g at logical positions of request r."""
+    """Bit patterns of the stored rows of KV head g at logical positions of request r."""
     positions = np.asarray(positions, dtype=np.int64)
     pages = wl.table[r][positions // wl.page_size].astype(np.int64)
     if positions.size and (pages.min() < 0 or pages.max() >= wl.num_pages):
@@ -97,14 +152,18 @@ def keys_values(wl, rows_f64: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     split : k = row[k_off : k_off+D],  v = row[v_off : v_off+D]
     folded: the score is q'[0:rot].row[k_off : k_off+rot] + q'[rot:D].v[rot:D],
             so the effective key is (row[k_off : k_off+rot], v[rot:D]).
+    Stored values are dequantised: K columns times k_scale, V columns times v_scale
+    (the folded key's V columns are V columns, so they take v_scale).
     """
     D = wl.head_dim
-    V = rows_f64[:, wl.v_offset:wl.v_offset + D]
+    ks = float(getattr(wl, "k_scale", 1.0))
+    vs = float(getattr(wl, "v_scale", 1.0))
+    V = rows_f64[:, wl.v_offset:wl.v_offset + D] * vs
     if wl.fmt == "split":
-        K = rows_f64[:, wl.k_offset:wl.k_offset + D]
+        K = rows_f64[:, wl.k_offset:wl.k_offset + D] * ks
     else:
         rot = wl.rot_cols
-        K = np.concatenate([rows_f64[:, wl.k_offset:wl.k_offset + rot], V[:, rot:]], axis=1)
+        K = np.concatenate([rows_f64[:, wl.k_offset:wl.k_offset + rot] * ks, V[:, rot:]], axis=1)
     return K, V
 
 
@@ -141,7 +200,7 @@ def decode_attention(wl) -> np.ndarray:
             lo, L = visible_range(int(wl.seq_lens[r]) - n + 1 + i, wl.window)
             pos = np.arange(lo, L)
             for g in range(wl.num_kv_heads):
-                K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
+                K, V = keys_values(wl, _stored_rows(wl, r, g, pos))
                 heads = slice(g * G, (g + 1) * G)
                 out[r, i, heads] = dense_attention(q[r, i, heads], K, V, wl.scale)
     return out if n > 1 else out[:, 0]
@@ -246,7 +305,7 @@ def paged_partials(wl, r: int, g: int, ranges: Sequence[tuple[int, int]],
     out = [[] for _ in range(G)]
     for a, b in ranges:
         pos = np.arange(max(a, lo), min(b, L))
-        K, V = keys_values(wl, bf16_bits_to_f64(gather_rows(wl, r, g, pos)))
+        K, V = keys_values(wl, _stored_rows(wl, r, g, pos))
         for i in range(G):
             out[i].append(partial_state(q[r, row, g * G + i], K, V, wl.scale))
     return out

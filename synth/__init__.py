@@ -16,9 +16,12 @@ Shapes and distributions follow the workloads on the pages:
 * sliding layers: head dim 256, window 1024, pages of 64 (pegainfer PR #1057,
   Description).
 
-q, K and V are N(0, 1); q stays fp32, K/V are rounded to bf16 with
-round-to-nearest-even.  Random numbers come from a seeded torch CPU generator
-(Mersenne Twister stream, deterministic for a given seed on any host).
+q, K and V are N(0, 1); q stays fp32.  K/V are stored in the pool's element
+type: bf16 or f16 (round-to-nearest-even), f32 (as drawn) or FP8 E4M3 codes of
+x / scale (round-to-nearest-even, clamped to the largest finite code) with one
+dequantisation factor for K and one for V.  Random numbers come from a seeded
+torch CPU generator (Mersenne Twister stream, deterministic for a given seed on
+any host); the same seed draws the same N(0, 1) values whatever the element type.
 """
 from __future__ import annotations
 
@@ -35,10 +38,30 @@ FOLDED = "folded"
 HEAD_MAJOR = "head_major"    # pool[page][kv_head][slot][cols]
 TOKEN_MAJOR = "token_major"  # pool[page][slot][kv_head][cols]
 
-# bf16 bit patterns used to make unused slots hostile.
+# Element types of the K/V pool (the C descriptor's kv_dtype codes).
+BF16 = "bf16"
+F16 = "f16"
+FP8 = "fp8_e4m3"
+F32 = "f32"
+KV_DTYPES = {BF16: 0, F16: 1, FP8: 2, F32: 3}
+KV_BYTES = {BF16: 2, F16: 2, FP8: 1, F32: 4}
+KV_NUMPY = {BF16: np.uint16, F16: np.uint16, FP8: np.uint8, F32: np.uint32}
+# Default dequantisation factors of FP8 pools (not powers of two, K != V).
+FP8_K_SCALE = 0.0175
+FP8_V_SCALE = 0.0225
+FP8_MAX = 448.0
+
+# Bit patterns used to make unused slots hostile: a quiet NaN, a huge finite value
+# (about 1e30; the largest finite value for f16 and FP8) and zero.
 BF16_QNAN = 0x7FC0
-BF16_BIG = 0x7149          # about 1e30
+BF16_BIG = 0x7149
 PADS = {"nan": BF16_QNAN, "big": BF16_BIG, "zero": 0x0000}
+PADS_BY_DTYPE = {
+    BF16: PADS,
+    F16: {"nan": 0x7E00, "big": 0x7BFF, "zero": 0},
+    FP8: {"nan": 0x7F, "big": 0x7E, "zero": 0},
+    F32: {"nan": 0x7FC00000, "big": 0x7149F2CA, "zero": 0},
+}
 
 
 @dataclasses.dataclass
@@ -56,19 +79,22 @@ class Workload:
     scale: float
     layout: str
     num_pages: int
-    row_cols: int            # bf16 columns per stored row
+    row_cols: int            # stored columns (elements) per row
     page_stride: int         # elements between pages
     head_stride: int         # elements between KV heads inside a page
     row_stride: int          # elements between consecutive slots
     k_offset: int            # column where the K part starts
     v_offset: int            # column where V starts
     q: np.ndarray            # float32 [B][Hq][D]  (folded: the folded query)
-    pool: np.ndarray         # uint16 bf16 bits, flat, num_pages * page_stride
+    pool: np.ndarray         # element bit patterns (uint8/16/32), flat, num_pages * page_stride
     table: np.ndarray        # int32 [B][max_pages], -1 where no page
     seq_lens: np.ndarray     # int32 [B]
     fold_w: Optional[np.ndarray] = None   # float32 [D - rot_cols] (folded pair only)
     q_unfolded: Optional[np.ndarray] = None
     num_rows: int = 1        # query rows per request; > 1 makes q [B][rows][Hq][D]
+    kv_dtype: str = BF16     # element type of the pool
+    k_scale: float = 1.0     # K = stored value * k_scale
+    v_scale: float = 1.0     # V = stored value * v_scale
 
     @property
     def group_size(self) -> int:
@@ -91,22 +117,36 @@ class Workload:
                     scale=self.scale, num_pages=self.num_pages, page_stride=self.page_stride,
                     head_stride=self.head_stride, row_stride=self.row_stride,
                     k_offset=self.k_offset, v_offset=self.v_offset,
-                    num_rows=self.num_rows)
+                    num_rows=self.num_rows, kv_dtype=KV_DTYPES[self.kv_dtype],
+                    k_scale=self.k_scale, v_scale=self.v_scale)
 
     def kv_bytes(self) -> int:
         """Bytes of K/V rows a decode step must stream (visible keys only)."""
         n = sum(self.visible(r)[1] - self.visible(r)[0] for r in range(self.batch))
-        return n * self.num_kv_heads * self.row_cols * 2
+        return n * self.num_kv_heads * self.row_cols * KV_BYTES[self.kv_dtype]
 
 
 def _gen(seed: int) -> torch.Generator:
     return torch.Generator().manual_seed(int(seed))
 
 
-def _normal_bf16(gen: torch.Generator, shape) -> np.ndarray:
-    """N(0,1) fp32 rounded to bf16 (RNE), returned as uint16 bit patterns."""
+def _normal_stored(gen: torch.Generator, shape, kv_dtype: str, k_scale: float,
+                   v_scale: float, k_cols: slice) -> np.ndarray:
+    """N(0,1) fp32 values in the pool's element type (bit patterns).  FP8 codes are
+    x / scale, with K's factor on the ``k_cols`` columns and V's on the rest."""
     x = torch.randn(*shape, generator=gen, dtype=torch.float32)
-    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if kv_dtype == BF16:
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if kv_dtype == F16:
+        return x.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    if kv_dtype == F32:
+        return x.numpy().view(np.uint32).copy()
+    if kv_dtype == FP8:
+        div = torch.full((shape[-1],), float(v_scale), dtype=torch.float32)
+        div[k_cols] = float(k_scale)
+        y = (x / div).clamp(-FP8_MAX, FP8_MAX)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    raise ValueError(kv_dtype)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -151,7 +191,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                   rot_cols: int = 128, seed: int = 0, table_seed: Optional[int] = None,
                   layout: str = HEAD_MAJOR, spare_pages: int = 4, pad: str = "nan",
                   max_pages: Optional[int] = None, extra_page: bool = True,
-                  scale: Optional[float] = None, num_rows: int = 1) -> Workload:
+                  scale: Optional[float] = None, num_rows: int = 1, kv_dtype: str = BF16,
+                  k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> Workload:
     """Build a decode-step workload.
 
     Data is drawn per (request, logical page) in ascending order from ``seed``;
@@ -160,7 +201,9 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     ``table_seed`` hold the same logical rows at different physical pages.
     Slots outside a request's visible keys and unused pages hold ``pad``.
     ``num_rows`` > 1 gives every request a window of that many query rows (the last
-    positions of the request), q shaped [B][rows][Hq][D].
+    positions of the request), q shaped [B][rows][Hq][D].  ``kv_dtype`` picks the
+    pool's element type; the dequantisation factors default to 1 (FP8: the
+    FP8_K_SCALE / FP8_V_SCALE pair).
     """
     seq_lens = [int(x) for x in seq_lens]
     B = len(seq_lens)
@@ -171,6 +214,12 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
         row_cols, k_off, v_off, rot = rot_cols + D, 0, rot_cols, rot_cols
     else:
         raise ValueError(fmt)
+    if kv_dtype not in KV_DTYPES:
+        raise ValueError(kv_dtype)
+    if k_scale is None:
+        k_scale = FP8_K_SCALE if kv_dtype == FP8 else 1.0
+    if v_scale is None:
+        v_scale = FP8_V_SCALE if kv_dtype == FP8 else 1.0
     if max_pages is None:
         max_pages = max((L + page_size - 1) // page_size for L in seq_lens)
     if num_rows < 1 or any(L < num_rows for L in seq_lens):
@@ -196,8 +245,10 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
         q = q.copy()
         q[..., rot:] = (q_unfolded[..., rot:] * fold_w).astype(np.float32)
 
-    padv = np.uint16(PADS[pad])
-    pool = np.full(num_pages * page_stride, padv, dtype=np.uint16)
+    etype = KV_NUMPY[kv_dtype]
+    padv = etype(PADS_BY_DTYPE[kv_dtype][pad])
+    pool = np.full(num_pages * page_stride, padv, dtype=etype)
+    k_cols = slice(k_off, k_off + (rot if fmt == FOLDED else D))
     perm = torch.randperm(num_pages, generator=tgen).numpy().astype(np.int32)
     table = np.full((B, max_pages), -1, dtype=np.int32)
     pool_pages = pool.reshape(num_pages, page_stride)
@@ -209,7 +260,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
         for j in range(p0, p1):
             pid = int(perm[k]); k += 1
             table[r, j] = pid
-            block = _normal_bf16(gen, (num_kv_heads, page_size, row_cols))
+            block = _normal_stored(gen, (num_kv_heads, page_size, row_cols), kv_dtype,
+                                   k_scale, v_scale, k_cols)
             # positions of this page that are outside the visible range get the pad
             pos = j * page_size + np.arange(page_size)
             dead = (pos >= L) | (pos < lo)
@@ -223,7 +275,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                     head_stride=head_stride, row_stride=row_stride, k_offset=k_off,
                     v_offset=v_off, q=q, pool=pool, table=table,
                     seq_lens=np.asarray(seq_lens, dtype=np.int32), fold_w=fold_w,
-                    q_unfolded=q_unfolded, num_rows=num_rows)
+                    q_unfolded=q_unfolded, num_rows=num_rows, kv_dtype=kv_dtype,
+                    k_scale=float(k_scale), v_scale=float(v_scale))
 
 
 def _store_page(dst: np.ndarray, block: np.ndarray, layout: str, hkv: int, ps: int, cols: int):
@@ -243,6 +296,8 @@ def split_pair_of_folded(wl: Workload) -> Workload:
     """
     if wl.fmt != FOLDED:
         raise ValueError("need a folded workload")
+    if wl.kv_dtype != BF16:
+        raise ValueError("the split pair is defined for bf16 pools")
     D, rot = wl.head_dim, wl.rot_cols
     cols = 2 * D
     page_stride, head_stride, row_stride = _strides(wl.layout, wl.num_kv_heads, wl.page_size, cols)

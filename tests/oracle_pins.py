@@ -25,6 +25,32 @@ def _bf16_to_float(bits: int) -> float:
     return struct.unpack(">f", struct.pack(">I", (int(bits) & 0xFFFF) << 16))[0]
 
 
+def _f16_to_float(bits: int) -> float:
+    """Independent binary16 decode through the struct module's half-precision format."""
+    return struct.unpack("<e", struct.pack("<H", int(bits) & 0xFFFF))[0]
+
+
+def _e4m3_to_float(bits: int) -> float:
+    """Independent OCP E4M3 decode, one code at a time (sign, 4-bit exponent with bias
+    7, 3-bit mantissa; exponent 0 is subnormal; S.1111.111 is NaN)."""
+    b = int(bits) & 0xFF
+    if b & 0x7F == 0x7F:
+        return math.nan
+    sign = -1.0 if b >> 7 else 1.0
+    e, m = (b >> 3) & 15, b & 7
+    if e == 0:
+        return sign * math.ldexp(m, -9)
+    return sign * math.ldexp(8 + m, e - 10)
+
+
+def _f32_to_float(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", int(bits) & 0xFFFFFFFF))[0]
+
+
+_ELEMENT = {"bf16": _bf16_to_float, "f16": _f16_to_float, "fp8_e4m3": _e4m3_to_float,
+            "f32": _f32_to_float}
+
+
 def brute_force_rows(wl) -> np.ndarray:
     """Multi-row window by brute force: row i is single-row decode of length L - n + 1 + i,
     evaluated by brute_force_decode on a copy whose lengths are cut to that value."""
@@ -50,6 +76,8 @@ def brute_force_decode(wl) -> np.ndarray:
     D, G = wl.head_dim, wl.num_q_heads // wl.num_kv_heads
     out = np.zeros((wl.batch, wl.num_q_heads, D))
     pool = wl.pool
+    elem = _ELEMENT[wl.kv_dtype]
+    ks, vs = wl.k_scale, wl.v_scale
     for r in range(wl.batch):
         L = int(wl.seq_lens[r])
         lo = L - wl.window if (wl.window and L > wl.window) else 0
@@ -58,12 +86,12 @@ def brute_force_decode(wl) -> np.ndarray:
             for j in range(lo, L):
                 p = int(wl.table[r][j // wl.page_size])
                 base = p * wl.page_stride + g * wl.head_stride + (j % wl.page_size) * wl.row_stride
-                row = [_bf16_to_float(pool[base + c]) for c in range(wl.row_cols)]
-                v = row[wl.v_offset:wl.v_offset + D]
+                row = [elem(pool[base + c]) for c in range(wl.row_cols)]
+                v = [x * vs for x in row[wl.v_offset:wl.v_offset + D]]
                 if wl.fmt == "split":
-                    k = row[wl.k_offset:wl.k_offset + D]
+                    k = [x * ks for x in row[wl.k_offset:wl.k_offset + D]]
                 else:
-                    k = row[wl.k_offset:wl.k_offset + wl.rot_cols] + v[wl.rot_cols:]
+                    k = [x * ks for x in row[wl.k_offset:wl.k_offset + wl.rot_cols]] + v[wl.rot_cols:]
                 keys.append(k)
                 vals.append(v)
             for h in range(g * G, (g + 1) * G):
@@ -97,6 +125,16 @@ BRUTE_CASES = [
     ([16, 11, 4, 2], 4, 4, 17, 4, 5, "split", synth.HEAD_MAJOR),
 ]
 
+# Other stored element types: (kv_dtype, seq_lens, Hq, Hkv, D, page_size, window, fmt, layout)
+DTYPE_CASES = [
+    ("fp8_e4m3", [16, 7], 16, 2, 512, 4, 0, "split", synth.HEAD_MAJOR),
+    ("fp8_e4m3", [14, 9], 8, 1, 512, 4, 0, "folded", synth.TOKEN_MAJOR),
+    ("fp8_e4m3", [16, 11, 4], 4, 4, 17, 4, 5, "split", synth.TOKEN_MAJOR),
+    ("f16", [12, 5], 8, 2, 64, 4, 0, "split", synth.HEAD_MAJOR),
+    ("f16", [9], 8, 1, 512, 4, 0, "folded", synth.HEAD_MAJOR),
+    ("f32", [13, 3], 4, 2, 33, 4, 6, "split", synth.TOKEN_MAJOR),
+]
+
 
 def pin_brute_force():
     """Dense fp64 oracle == literal pure-Python softmax on tiny paged inputs."""
@@ -105,6 +143,84 @@ def pin_brute_force():
                                  window=W, fmt=fmt, rot_cols=128, seed=10 + i, layout=layout,
                                  spare_pages=3, pad="big")
         _assert_close(oracle.decode_attention(wl), brute_force_decode(wl), 1e-13, f"brute case {i}")
+
+
+def pin_dtype_brute_force():
+    """f16, FP8 E4M3 (with K and V dequantisation factors) and f32 pools: the fp64
+    oracle == literal pure-Python decode with its own per-element decoders."""
+    for i, (dt, lens, hq, hkv, D, ps, W, fmt, layout) in enumerate(DTYPE_CASES):
+        wl = synth.make_workload(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=ps,
+                                 window=W, fmt=fmt, rot_cols=128, seed=40 + i, layout=layout,
+                                 spare_pages=2, pad="nan", kv_dtype=dt)
+        assert wl.pool.dtype.itemsize == synth.KV_BYTES[dt]
+        _assert_close(oracle.decode_attention(wl), brute_force_decode(wl), 1e-13,
+                      f"dtype case {i} ({dt} {fmt})")
+
+
+def pin_e4m3_codes():
+    """All 256 E4M3 codes: the oracle's decode == torch's float8_e4m3fn widening, the
+    per-code decoder above, and the closed forms of the encoding (largest finite 448,
+    smallest subnormal 2^-9, smallest normal 2^-6, 1.0 = 0x38, two NaN codes, -0)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_bits_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    mine = np.array([_e4m3_to_float(c) for c in range(256)])
+    assert np.array_equal(got[fin], mine[fin]) and np.isnan(mine[~fin]).all()
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x39] == 1.125
+    assert np.flatnonzero(np.isnan(got)).tolist() == [0x7F, 0xFF]
+    assert got[0x80] == 0.0 and np.signbit(got[0x80])
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes must increase strictly"
+
+
+def pin_f16_f32_codes():
+    """Every binary16 pattern widens as torch's float16 does (and closed forms); binary32
+    closed forms."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.f16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.float16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], ref[~nan])
+    assert got[0x3C00] == 1.0 and got[0x0001] == 2.0 ** -24 and got[0x7BFF] == 65504.0
+    assert got[0x7C00] == math.inf and got[0xFC00] == -math.inf and got[0x0400] == 2.0 ** -14
+    f = oracle.f32_bits_to_f64(np.array([0x3F800000, 0x00000001, 0x7F7FFFFF, 0xC0490FDB],
+                                        dtype=np.uint32))
+    assert f[0] == 1.0 and f[1] == 2.0 ** -149 and f[2] == (2 - 2.0 ** -23) * 2.0 ** 127
+    assert f[3] == -3.1415927410125732
+
+
+def pin_dequant_factors():
+    """K's factor acts as a factor on the softmax scale, V's as a factor on the output:
+    decode(k_scale = a, v_scale = b) == b * decode(k_scale = 1, v_scale = 1, scale * a)."""
+    import copy
+    for fmt in ("split", "folded"):
+        D = 512 if fmt == "folded" else 64
+        wl = synth.make_workload([37, 20], num_q_heads=8, num_kv_heads=2, head_dim=D, page_size=8,
+                                 fmt=fmt, seed=44, kv_dtype="fp8_e4m3", pad="big")
+        got = oracle.decode_attention(wl)
+        one = copy.copy(wl)
+        one.v_scale = 1.0
+        if fmt == "split":
+            one.k_scale = 1.0
+            one.scale = wl.scale * wl.k_scale
+        else:
+            # folded: the query's rotated part meets K columns, the rest meets V columns
+            one.k_scale = 1.0
+            q = wl.q.astype(np.float64).copy()
+            q[..., :128] *= wl.k_scale
+            q[..., 128:] *= wl.v_scale
+            one.q = q
+        ref = wl.v_scale * oracle.decode_attention(one)
+        _assert_close(got, ref, 1e-13, f"dequantisation factors ({fmt})")
+        assert not np.allclose(got, oracle.decode_attention(copy.copy(one)), atol=1e-3)
 
 
 def pin_single_key():
@@ -395,4 +511,5 @@ ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, p
             pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
             pin_empty_merge_identity, pin_merge_identity_values, pin_window,
             pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed,
-            pin_query_rows]
+            pin_query_rows, pin_dtype_brute_force, pin_e4m3_codes, pin_f16_f32_codes,
+            pin_dequant_factors]

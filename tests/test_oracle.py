@@ -120,6 +120,37 @@ def _rows_off_by_one(wl):
 
 _orig_decode = OA.decode_attention
 
+
+def _k_factor_dropped(wl, rows):
+    import copy
+    one = copy.copy(wl)
+    one.k_scale = 1.0
+    return _orig_keys_values(one, rows)
+
+
+def _folded_key_takes_k_factor(wl, rows):
+    K, V = _orig_keys_values(wl, rows)
+    if wl.fmt == "folded":
+        K = K.copy()
+        K[:, wl.rot_cols:] *= wl.k_scale / wl.v_scale
+    return K, V
+
+
+def _e4m3_bias_8(bits):
+    return _orig_e4m3(bits) / 2.0
+
+
+def _e4m3_subnormal_as_normal(bits):
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    out = _orig_e4m3(bits)
+    e, m = (b >> 3) & 15, (b & 7).astype(np.float64)
+    sub = (e == 0) & (m > 0)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    return np.where(sub, sign * (1 + m / 8) * 2.0 ** -7, out)
+
+
+_orig_e4m3 = OA.e4m3_bits_to_f64
+
 MUTANTS = {
     "rows_see_one_key_too_many": ("decode_attention", _rows_off_by_one),
     "k_v_swapped": ("keys_values", _kv_swapped),
@@ -132,6 +163,10 @@ MUTANTS = {
     "gather_slot_page_swapped": ("gather_rows", _gather_slot_page_swapped),
     "softmax_max_wrong_axis": ("dense_attention", _dense_max_wrong_axis),
     "no_fail_closed": ("validate", _validate_lenient),
+    "k_factor_dropped": ("keys_values", _k_factor_dropped),
+    "folded_key_takes_k_factor": ("keys_values", _folded_key_takes_k_factor),
+    "e4m3_bias_8": ("e4m3_bits_to_f64", _e4m3_bias_8),
+    "e4m3_subnormal_as_normal": ("e4m3_bits_to_f64", _e4m3_subnormal_as_normal),
 }
 
 
