@@ -83,7 +83,7 @@ class Resident:
         self.K = K
         self.plan = K.attn_decode_plan(K.make_desc(**wl.desc_fields(num_chunks)), wl.seq_lens)
         self.q = torch.from_numpy(np.ascontiguousarray(wl.q, dtype=np.float32)).to(dev)
-        self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(dev)
+        self.pool = torch.from_numpy(wl.pool.view(np.uint8)).to(dev)
         self.table = torch.from_numpy(wl.table).to(dev)
         self.lens = torch.from_numpy(wl.seq_lens).to(dev)
         self.ws = torch.empty(int(self.plan.workspace_bytes), dtype=torch.uint8, device=dev)
@@ -278,13 +278,22 @@ def main():
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
                 ("global-decode-163336-split-4rows",
                  lambda: synth.make_workload([163336], **synth.GLOBAL, seed=6, num_rows=4,
-                                             spare_pages=1), 20)):
+                                             spare_pages=1), 20),
+                ("global-decode-163336-split-fp8e4m3",
+                 lambda: synth.global_decode(163336, seed=7, kv_dtype=synth.FP8), 20),
+                ("global-decode-163336-folded-fp8e4m3",
+                 lambda: synth.global_decode(163336, seed=8, fmt="folded", kv_dtype=synth.FP8), 20),
+                ("global-decode-163336-split-f16",
+                 lambda: synth.global_decode(163336, seed=9, kv_dtype=synth.F16), 20),
+                ("sliding-hd256-16ragged-w1024-fp8e4m3",
+                 lambda: synth.sliding_batch(seed=4, kv_dtype=synth.FP8), 20)):
             vwl = maker()
             vres = Resident(vwl)
             vt = time_steps(vres, n_steps, 3, flush=flush)
             vms = median(vt["step_ms"])
             vsplit = median(vt["split_ms"])
             variants[name] = {"us_per_step": round(vms * 1e3, 2), "query_rows": vwl.num_rows,
+                              "kv_dtype": vwl.kv_dtype,
                               "partial_kernel_us": round(vsplit * 1e3, 2),
                               "kv_bytes": vwl.kv_bytes(),
                               "effective_gbs": round(vwl.kv_bytes() / (vms * 1e-3) / 1e9, 1),

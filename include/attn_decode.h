@@ -56,6 +56,20 @@ enum {
                           weight already folded into q' by the caller (640 cols at D=512) */
 };
 
+/* Element types of the pool (kv_dtype).  BF16 is the pages' row type; F32 is the
+ * production KV type of the gem design note ("Fixed production shape"), where F16
+ * and quantised KV are named as further axes.  The quantised type taken here is
+ * FP8 E4M3 as the OCP 8-bit floating point specification defines it (bias 7,
+ * subnormals, no infinity, S.1111.111 = NaN), the FP8 encoding gfx950 converts
+ * natively.  Every type is widened exactly to the MFMA operand type (bf16 for BF16
+ * and FP8, f16 for F16); F32 is not yet served (ATTN_E_UNSUPPORTED). */
+enum {
+  ATTN_KV_BF16 = 0,
+  ATTN_KV_F16 = 1,
+  ATTN_KV_FP8_E4M3 = 2,
+  ATTN_KV_F32 = 3
+};
+
 /*
  * Shape and layout of one layer's paged pool and decode batch.
  *
@@ -64,10 +78,15 @@ enum {
  *   head_dim 256, 2 query heads per KV head, SPLIT (sliding layers, any window)
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *
- * Element (page p, KV head g, slot s, column c) of the pool is the bf16 at
+ * Element (page p, KV head g, slot s, column c) of the pool is the kv_dtype
+ * element at
  *   pool[p * page_stride + g * head_stride + s * row_stride + c]
- * All strides and offsets count bf16 elements and must be multiples of 8
- * (16-byte loads); every row of a page must lie inside its page_stride.
+ * All strides and offsets count elements of kv_dtype and must be multiples of 16
+ * bytes (8 BF16/F16 elements, 16 FP8 elements); every row of a page must lie
+ * inside its page_stride.
+ * The keys and values used are the stored values times k_scale and v_scale
+ * (dequantisation factors, one per tensor; 1 for an unscaled pool).  In a FOLDED
+ * row the unrotated part of the key is made of V columns, so it takes v_scale.
  * Logical key position j of request r lives in slot j % page_size of page
  * page_table[r * max_pages_per_seq + j / page_size] (TensorFold PR #1619, body).
  *
@@ -93,7 +112,10 @@ typedef struct attn_decode_desc {
                                  causally to the keys before L - n + i + 1 (drafted verify
                                  windows through the paged decode, TensorFold PR #1619, review
                                  thread); q and out are then [batch][n][num_q_heads][head_dim] */
+  int32_t kv_dtype;           /* ATTN_KV_BF16, ATTN_KV_F16 or ATTN_KV_FP8_E4M3 */
   float scale;                /* score = scale * q . k (1/sqrt(D) in the workloads) */
+  float k_scale;              /* K = stored * k_scale; finite and > 0 */
+  float v_scale;              /* V = stored * v_scale; finite and > 0 */
   int64_t num_pages;          /* pages in the pool; table entries outside [0, num_pages) poison */
   int64_t page_stride;        /* elements between pages */
   int64_t head_stride;        /* elements between KV heads inside a page */
@@ -142,8 +164,10 @@ typedef struct attn_decode_plan_t {
  * Validate `desc` and the host copy of the request lengths seq_lens_host[batch]
  * and fill `plan`.  No device call is made.
  * Refusals: null pointers or non-positive sizes (ATTN_E_INVALID_ARG); a shape
- * outside the supported list (ATTN_E_UNSUPPORTED); a stride or offset not a
- * multiple of 8, or rows overrunning their page (ATTN_E_INVALID_ARG); a length
+ * outside the supported list, or an element type without a kernel
+ * (ATTN_E_UNSUPPORTED); an unknown element type, a dequantisation factor that is
+ * not finite and positive, a stride or offset not a multiple of 16 bytes, or
+ * rows overrunning their page (ATTN_E_INVALID_ARG); a length
  * below 1 or below num_rows, or num_rows above 64 (ATTN_E_INVALID_ARG); a length
  * above max_pages_per_seq * page_size
  * (ATTN_E_PAST_PAGES, TensorFold PR #1619, body: rows past a slot's pages are
@@ -160,7 +184,8 @@ int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
  * head, chunk) into the workspace's part_* regions.
  *   q          device, float32 [batch][num_q_heads][head_dim] (FOLDED: the folded q'),
  *              [batch][num_rows][num_q_heads][head_dim] with several query rows
- *   kv_pool    device, bf16 pool laid out as described for attn_decode_desc
+ *   kv_pool    device, pool of kv_dtype elements laid out as described for
+ *              attn_decode_desc
  *   page_table device, int32 [batch][max_pages_per_seq]
  *   seq_lens   device, int32 [batch]; must equal the lengths given to the plan.  A
  *              device length or page id the plan cannot serve is not read past:

@@ -16,10 +16,15 @@ from . import build as _build
 __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_plan",
            "attn_decode_split", "attn_decode_merge", "attn_decode_status_string", "make_desc",
            "attn_kv_write", "attn_query_fold",
-           "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "STATUS", "LIB_PATH", "SYMBOLS"]
+           "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "ATTN_KV_BF16", "ATTN_KV_F16", "ATTN_KV_FP8_E4M3",
+           "ATTN_KV_F32", "STATUS", "LIB_PATH", "SYMBOLS"]
 
 ATTN_KV_SPLIT = 0
 ATTN_KV_FOLDED = 1
+ATTN_KV_BF16 = 0
+ATTN_KV_F16 = 1
+ATTN_KV_FP8_E4M3 = 2
+ATTN_KV_F32 = 3
 STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
           "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
@@ -35,7 +40,8 @@ class AttnDecodeDesc(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("merge_group", ctypes.c_int32), ("num_rows", ctypes.c_int32),
-                ("scale", ctypes.c_float),
+                ("kv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("num_pages", ctypes.c_int64), ("page_stride", ctypes.c_int64),
                 ("head_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64),
                 ("k_offset", ctypes.c_int64), ("v_offset", ctypes.c_int64)]
@@ -110,8 +116,11 @@ def _stream(stream) -> int:
 
 
 def make_desc(**fields) -> AttnDecodeDesc:
-    """An attn_decode_desc from keyword fields (missing integer fields are 0)."""
+    """An attn_decode_desc from keyword fields (missing fields are 0, except the
+    dequantisation factors k_scale and v_scale, which default to 1)."""
     d = AttnDecodeDesc()
+    d.k_scale = 1.0
+    d.v_scale = 1.0
     for k, v in fields.items():
         setattr(d, k, v)
     return d

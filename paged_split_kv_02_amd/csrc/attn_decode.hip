@@ -18,7 +18,11 @@
 //     to natural-log units (any reference <= the chunk maximum is a valid state);
 //   * masked keys (past L, before the window, padding slots of the last page)
 //     are excluded by select, and their V rows are zeroed before PV, so NaN or
-//     huge padding never reaches the sums.
+//     huge padding never reaches the sums;
+//   * pool element types: bf16 and f16 rows are staged as stored and multiplied on
+//     the MFMA of their own type; FP8 E4M3 rows are fetched at half the bytes and
+//     widened to bf16 (exactly) on their way into LDS.  The dequantisation factors
+//     fold into the query (K) and into the written state (V).
 // Merge (one launch): level 1 folds runs of consecutive chunk states into group
 // states held in LDS, out of place; level 2 folds the group states in order and
 // divides (pegainfer PR #1055, "Description": merge in two levels; gem design note,
@@ -35,6 +39,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -44,16 +51,19 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 struct SplitArgs {
   const float* q;
-  const uint16_t* pool;
+  const char* pool;
   const int32_t* table;
   const int32_t* seq_lens;
   float* part_m;
   float* part_l;
   float* part_o;
+  // Pool strides and column offsets in bytes.
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_q_heads, page_size, max_pages, window, chunk_len, num_chunks;
   int32_t num_rows, row_groups;  // query rows per request; groups of 4 rows (multi-row kernel)
-  float qscale;  // scale * log2(e)
+  float qscale_k;  // scale * log2(e) * k_scale: the query dims that meet K columns
+  float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
+  float vscale;    // v_scale, applied to the written numerators
 };
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -85,10 +95,87 @@ __device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Streaming 16-byte load that does not keep the line in the caches.
-__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
+// Stored element types.  A lane fetches 8 consecutive elements of a row at a time
+// (16 bytes of bf16/f16, 8 bytes of FP8) with a streaming load that does not keep the
+// line in the caches, and widens them to 8 MFMA operand elements (16 bytes) before
+// they are written to LDS.  kAhead = key tiles a wave of the single-row kernel keeps
+// in flight, so that about 32 KB per wave are requested ahead whatever the type.
+template <int KV>
+struct Elem;
+
+template <>
+struct Elem<ATTN_KV_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr bool kF16 = false;  // operand type: bf16
+  static constexpr int kAhead = 1;
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ Raw load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  static __device__ __forceinline__ u32x4 widen(Raw r) { return r; }
+};
+
+template <>
+struct Elem<ATTN_KV_F16> : Elem<ATTN_KV_BF16> {
+  static constexpr bool kF16 = true;  // operand type: f16
+};
+
+// FP8 E4M3 (OCP): v_cvt_pk_f32_fp8 widens two codes to f32 exactly (every code,
+// NaN and subnormals included); an E4M3 value has 3 mantissa bits, so the upper half
+// of its f32 pattern is the same value in bf16, and one byte permute packs two.
+template <>
+struct Elem<ATTN_KV_FP8_E4M3> {
+  static constexpr int kBytes = 1;
+  static constexpr bool kF16 = false;
+  static constexpr int kAhead = 2;
+  typedef u32x2 Raw;
+  static __device__ __forceinline__ Raw load(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  }
+  static __device__ __forceinline__ u32x4 widen(Raw r) {
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(int(r[i]), false);  // bytes 0, 1
+      const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(int(r[i]), true);   // bytes 2, 3
+      // (__float_as_uint, not __builtin_bit_cast: on a vector element subscript this
+      // hipcc bit-casts element 0 whatever the index.)
+      out[2 * i] = perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+      out[2 * i + 1] = perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    }
+    return out;
+  }
+};
+
+// MFMA operand type: bf16 or f16, with fp32 accumulation either way.
+template <bool F16>
+struct Ops;
+
+template <>
+struct Ops<false> {
+  typedef __bf16 T;
+  typedef bf16x8 T8;
+  typedef bf16x4 T4;
+  static __device__ __forceinline__ floatx4 mma32(T8 a, T8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 mma16(T4 a, T4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Ops<true> {
+  typedef _Float16 T;
+  typedef halfx8 T8;
+  typedef halfx4 T4;
+  static __device__ __forceinline__ floatx4 mma32(T8 a, T8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ floatx4 mma16(T4 a, T4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // LDS tile: the 16 stored rows of one key tile, padded by 16 bytes per row.
 // Staging writes (one row, 16 consecutive 16-byte pieces per 16-lane pass) and the
@@ -113,28 +200,32 @@ struct Shape {
 };
 
 // Query operand of lane (c, qg) for one query row: column c holds head (c % G) of KV
-// head g, the high bf16 part of q*scale*log2(e) for c < G, the low remainder for
-// G <= c < 2G, zero beyond; k-step j covers dims 32j + 8qg + [0, 8).
-template <int D, int G>
+// head g, the high operand-type part of q*scale*log2(e)*factor for c < G, the low
+// remainder for G <= c < 2G, zero beyond; k-step j covers dims 32j + 8qg + [0, 8).
+// Dims below kdims meet K columns (factor k_scale), the others V columns (v_scale).
+template <int D, int G, bool F16>
 __device__ __forceinline__ void make_query_operand(const float* qrow_heads, int g, int c, int qg,
-                                                   float qscale, bf16x8 (&qop)[D / 32]) {
+                                                   float qscale_k, float qscale_v, int kdims,
+                                                   typename Ops<F16>::T8 (&qop)[D / 32]) {
+  using T = typename Ops<F16>::T;
   const int part = c / G;
   const float* qrow = qrow_heads + int64_t(g * G + c % G) * D;
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
-    bf16x8 v;
+    typename Ops<F16>::T8 v;
+    const float qs = 32 * j < kdims ? qscale_k : qscale_v;
     if (part < 2) {
       const floatx4 x0 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg);
       const floatx4 x1 = *reinterpret_cast<const floatx4*>(qrow + 32 * j + 8 * qg + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * qscale;
-        const __bf16 h = (__bf16)x;
-        v[e] = part == 0 ? h : (__bf16)(x - (float)h);
+        const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * qs;
+        const T h = (T)x;
+        v[e] = part == 0 ? h : (T)(x - (float)h);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      for (int e = 0; e < 8; ++e) v[e] = (T)0.0f;
     }
     qop[j] = v;
   }
@@ -143,12 +234,14 @@ __device__ __forceinline__ void make_query_operand(const float* qrow_heads, int 
 // One staged tile of 16 keys for one query row: QK^T on MFMA, online softmax over the
 // keys tok0 + 4qg + i visible to the row (lo <= key < hi), PV on MFMA.  The caller has
 // zeroed the V rows of keys no row may see.
-template <int D, int G, bool FOLDED>
+template <int D, int G, bool FOLDED, bool F16>
 __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo, int hi,
-                                          const bf16x8 (&qop)[D / 32], int c, int qg,
-                                          float& m_run, float& l_run,
+                                          const typename Ops<F16>::T8 (&qop)[D / 32], int c,
+                                          int qg, float& m_run, float& l_run,
                                           floatx4 (&acc)[D / 128][8]) {
   using S = Shape<D, FOLDED>;
+  using O = Ops<F16>;
+  using T = typename O::T;
   const int part = c / G;
   // Scores of 16 keys x 16 columns (hi/lo parts of the G heads).  Key dim kd sits at
   // staged column kd (split / rotated part) or TV + kd (folded, kd >= ROT).
@@ -158,7 +251,7 @@ __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo
     const int kd = 32 * j + 8 * qg;
     const int col = (FOLDED && kd >= S::ROT) ? S::TV + kd : kd;
     const u32x4 kv = *reinterpret_cast<const u32x4*>(tile + c * S::P + col);
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[j], s, 0, 0, 0);
+    s = O::mma32(__builtin_bit_cast(typename O::T8, kv), qop[j], s);
   }
 
   // Online softmax (base 2); lane holds keys tok0 + 4qg + i.
@@ -191,12 +284,12 @@ __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
   }
   l_run += (p[0] + p[1]) + (p[2] + p[3]);
-  bf16x4 pop;
+  typename O::T4 pop;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const __bf16 h = (__bf16)p[i];
-    const __bf16 l = (__bf16)(p[i] - (float)h);
-    pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
+    const T h = (T)p[i];
+    const T l = (T)(p[i] - (float)h);
+    pop[i] = part == 0 ? h : (part == 1 ? l : (T)0.0f);
   }
 
   // PV: lane row c of slab b, step jj <-> dim 128b + 8c + jj; keys 4qg + [0, 4).  The
@@ -212,10 +305,8 @@ __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo
     for (int u = 0; u < 4; ++u) {
       const u32x2 even = {perm(w[1][u], w[0][u], 0x05040100u), perm(w[3][u], w[2][u], 0x05040100u)};
       const u32x2 odd = {perm(w[1][u], w[0][u], 0x07060302u), perm(w[3][u], w[2][u], 0x07060302u)};
-      acc[b][2 * u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, even), pop,
-                                                               acc[b][2 * u], 0, 0, 0);
-      acc[b][2 * u + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, odd),
-                                                                   pop, acc[b][2 * u + 1], 0, 0, 0);
+      acc[b][2 * u] = O::mma16(__builtin_bit_cast(typename O::T4, even), pop, acc[b][2 * u]);
+      acc[b][2 * u + 1] = O::mma16(__builtin_bit_cast(typename O::T4, odd), pop, acc[b][2 * u + 1]);
     }
   }
 }
@@ -238,12 +329,12 @@ __device__ __forceinline__ void zero_dead_rows(uint16_t* tile, int tok0, int lo,
   }
 }
 
-// Column of staged piece sb (128 elements each) in the stored row.
-template <int D, bool FOLDED>
+// Byte offset in the stored row of staged piece sb (128 elements each).
+template <int D, bool FOLDED, int EB>
 __device__ __forceinline__ int64_t src_col(const SplitArgs& a, int sb) {
   constexpr int VG = D / 128;
-  if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * (sb - 1);
-  return sb < VG ? a.k_offset + 128 * sb : a.v_offset + 128 * (sb - VG);
+  if (FOLDED) return sb == 0 ? a.k_offset : a.v_offset + 128 * EB * (sb - 1);
+  return sb < VG ? a.k_offset + 128 * EB * sb : a.v_offset + 128 * EB * (sb - VG);
 }
 
 // Page ids of one table row, read once per page through the scalar cache with the next
@@ -270,14 +361,16 @@ struct PageWalker {
   }
 };
 
-template <int D, int G, bool FOLDED>
+template <int D, int G, bool FOLDED, int KV>
 __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   using S = Shape<D, FOLDED>;
+  using E = Elem<KV>;
   constexpr int KSTEPS = S::KSTEPS;
-  constexpr int VGROUPS = S::VGROUPS;
   constexpr int COLS = S::COLS;
   constexpr int SLABS = S::SLABS;
   constexpr int P = S::P;
+  constexpr int EB = E::kBytes;
+  constexpr int kAhead = E::kAhead;
   static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
   __shared__ RowTile<COLS> tiles[kWavesPerBlock];
 
@@ -299,40 +392,42 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const int quarter = a.chunk_len / kWavesPerBlock;
   const int c0 = start + chunk * a.chunk_len + wave * quarter;
   const int c1 = min(c0 + quarter, L);
-  const bool has_work = !poison && c0 < c1;
-  const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
-  u32x4 stage[4][SLABS];
+  int end = (!poison && c0 < c1) ? c1 : c0;  // tiles from `end` on are not processed
+  const char* head_base = a.pool + int64_t(g) * a.head_stride;
+  typename E::Raw stage[kAhead][4][SLABS];
 
   PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
-  if (has_work) pw.start(c0);
-  // Resolve the tile's rows; false if the table entry is outside the pool.
-  auto tile_base = [&](int tok0, const uint16_t** base) -> bool {
+  // Fetch one tile into a register set.  Lane (c, qg) reads rows 4qg + e, 8 elements at
+  // 128 sb + 8c: every instruction covers four whole row pieces, so each line is
+  // requested once.  A table entry outside the pool poisons the chunk and ends it.
+  auto fetch = [&](typename E::Raw (&buf)[4][SLABS], int tok0) {
     const int32_t pid = pw.page_of(tok0);
-    if (pid < 0) return false;
-    *base = head_base + int64_t(pid) * a.page_stride +
-            int64_t(tok0 % a.page_size) * a.row_stride;
-    return true;
-  };
-  // Lane (c, qg) fetches rows 4qg + e, 16 bytes at 128 sb + 8c: every instruction
-  // reads four whole 256-byte row pieces, so each line is requested once.
-  auto load_tile = [&](const uint16_t* base) {
+    if (pid < 0) {
+      poison = true;
+      end = tok0;
+      return;
+    }
+    const char* base = head_base + int64_t(pid) * a.page_stride +
+                       int64_t(tok0 % a.page_size) * a.row_stride + 8 * EB * c;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint16_t* row = base + int64_t(4 * qg + e) * a.row_stride + 8 * c;
+      const char* row = base + int64_t(4 * qg + e) * a.row_stride;
 #pragma unroll
-      for (int sb = 0; sb < SLABS; ++sb) stage[e][sb] = load_nt(row + src_col<D, FOLDED>(a, sb));
+      for (int sb = 0; sb < SLABS; ++sb) buf[e][sb] = E::load(row + src_col<D, FOLDED, EB>(a, sb));
     }
   };
 
-  // Start streaming the first tile before the query is prepared.
-  const uint16_t* base = nullptr;
-  const bool first_ok = has_work && tile_base(c0, &base);
-  if (has_work && !first_ok) poison = true;
-  if (first_ok) load_tile(base);
+  // Start streaming the first tiles before the query is prepared.
+  if (c0 < end) {
+    pw.start(c0);
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+      if (c0 + k * kTile < end) fetch(stage[k], c0 + k * kTile);
+  }
 
-  bf16x8 qop[KSTEPS];
-  make_query_operand<D, G>(a.q + int64_t(r) * a.num_q_heads * D, g, c, qg, a.qscale, qop);
-  const int hq = g * G + (c % G);
+  typename Ops<E::kF16>::T8 qop[KSTEPS];
+  make_query_operand<D, G, E::kF16>(a.q + int64_t(r) * a.num_q_heads * D, g, c, qg, a.qscale_k,
+                                    a.qscale_v, FOLDED ? S::ROT : D, qop);
 
   float m_run = -INFINITY;
   float l_run = 0.0f;
@@ -342,29 +437,24 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (first_ok) {
-    int tok0 = c0;
-    for (;;) {
-      const int next = tok0 + kTile;
-      bool has_next = next < c1;
-      const uint16_t* nbase = nullptr;
-      if (has_next && !tile_base(next, &nbase)) {
-        poison = true;
-        has_next = false;
-      }
-      // Stage the tile, then start fetching the next one.
+  // One tile: widen and stage it, refill its registers kAhead tiles ahead, mask, math.
+  auto step = [&](typename E::Raw (&regs)[4][SLABS], int tok0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int sb = 0; sb < SLABS; ++sb)
-          *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = stage[e][sb];
-      if (has_next) load_tile(nbase);
-      // Keys outside [lo, L): first tile of a window, tail of the last page.
-      if (__builtin_expect(tok0 < lo || tok0 + kTile > L, 0))
-        zero_dead_rows<D, FOLDED>(tile, tok0, lo, L, c, qg, 0, 4);
-      tile_math<D, G, FOLDED>(tile, tok0, lo, L, qop, c, qg, m_run, l_run, acc);
-      if (!has_next) break;
-      tok0 = next;
+      for (int sb = 0; sb < SLABS; ++sb)
+        *reinterpret_cast<u32x4*>(tile + (4 * qg + e) * P + 128 * sb + 8 * c) = E::widen(regs[e][sb]);
+    if (tok0 + kAhead * kTile < end) fetch(regs, tok0 + kAhead * kTile);
+    // Keys outside [lo, L): first tile of a window, tail of the last page.
+    if (__builtin_expect(tok0 < lo || tok0 + kTile > L, 0))
+      zero_dead_rows<D, FOLDED>(tile, tok0, lo, L, c, qg, 0, 4);
+    tile_math<D, G, FOLDED, E::kF16>(tile, tok0, lo, L, qop, c, qg, m_run, l_run, acc);
+  };
+  for (int tok0 = c0; tok0 < end; tok0 += kAhead * kTile) {
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      if (tok0 + k * kTile >= end) break;
+      step(stage[k], tok0 + k * kTile);
     }
   }
 
@@ -437,7 +527,7 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
       a.part_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
       a.part_l[st] = S;
     }
-    *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O;
+    *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O * a.vscale;
   }
 }
 
@@ -466,8 +556,8 @@ __device__ __forceinline__ void write_row_state(const SplitArgs& a, int64_t st, 
   for (int b = 0; b < D / 128; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      floatx4 w0 = {acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
-      floatx4 w1 = {acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
+      floatx4 w0 = floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]} * a.vscale;
+      floatx4 w1 = floatx4{acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]} * a.vscale;
       if (poison) w0 = w1 = floatx4{qnan, qnan, qnan, qnan};
       float* dst = o + 128 * b + 32 * qg + 8 * i;
       *reinterpret_cast<floatx4*>(dst) = w0;
@@ -482,9 +572,11 @@ __device__ __forceinline__ void write_row_state(const SplitArgs& a, int64_t st, 
 // so every K/V byte is read once for all the rows of the group.  Workgroups of the
 // same chunk and different row groups are 8 apart in launch order, i.e. on the same
 // XCD, so the later group finds the rows in that XCD's L2.
-template <int D, int G, bool FOLDED>
+template <int D, int G, bool FOLDED, int KV>
 __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
   using S = Shape<D, FOLDED>;
+  using E = Elem<KV>;
+  constexpr int EB = E::kBytes;
   static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
   __shared__ RowTile<S::COLS> tiles[2];
 
@@ -514,25 +606,26 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
                 int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
   const int c0 = start + chunk * a.chunk_len;
   const int c1 = min(c0 + a.chunk_len, L);
-  const uint16_t* head_base = a.pool + int64_t(g) * a.head_stride;
+  const char* head_base = a.pool + int64_t(g) * a.head_stride;
 
   PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
-  // Three tiles stream ahead of the math; each register set holds this wave's quarter
-  // of one tile (rows 4qg + wave, 16 bytes at 128 sb + 8c).
-  constexpr int kAhead = 3;
-  u32x4 stage[kAhead][S::SLABS];
+  // Tiles stream ahead of the math (three of 16-bit rows, six of FP8 rows: the same
+  // bytes); each register set holds this wave's quarter of one tile (rows 4qg + wave,
+  // 8 elements at 128 sb + 8c).
+  constexpr int kAhead = 6 / EB;
+  typename E::Raw stage[kAhead][S::SLABS];
   int end = (!poison && c0 < c1) ? c1 : c0;  // tiles from `end` on are not processed
-  auto fetch = [&](u32x4 (&buf)[S::SLABS], int tok0) {
+  auto fetch = [&](typename E::Raw (&buf)[S::SLABS], int tok0) {
     const int32_t pid = pw.page_of(tok0);
     if (pid < 0) {
       poison = true;
       end = tok0;
       return;
     }
-    const uint16_t* row_ptr = head_base + int64_t(pid) * a.page_stride +
-                              int64_t(tok0 % a.page_size + 4 * qg + wave) * a.row_stride + 8 * c;
+    const char* row_ptr = head_base + int64_t(pid) * a.page_stride +
+                          int64_t(tok0 % a.page_size + 4 * qg + wave) * a.row_stride + 8 * EB * c;
 #pragma unroll
-    for (int sb = 0; sb < S::SLABS; ++sb) buf[sb] = load_nt(row_ptr + src_col<D, FOLDED>(a, sb));
+    for (int sb = 0; sb < S::SLABS; ++sb) buf[sb] = E::load(row_ptr + src_col<D, FOLDED, EB>(a, sb));
   };
   if (c0 < end) {
     pw.start(c0);
@@ -540,10 +633,10 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
     for (int k = 0; k < kAhead; ++k)
       if (c0 + k * kTile < end) fetch(stage[k], c0 + k * kTile);
   }
-  bf16x8 qop[S::KSTEPS];
+  typename Ops<E::kF16>::T8 qop[S::KSTEPS];
   if (row_active)
-    make_query_operand<D, G>(a.q + (int64_t(r) * rows + row) * a.num_q_heads * D, g, c, qg, a.qscale,
-                             qop);
+    make_query_operand<D, G, E::kF16>(a.q + (int64_t(r) * rows + row) * a.num_q_heads * D, g, c, qg,
+                                      a.qscale_k, a.qscale_v, FOLDED ? S::ROT : D, qop);
   float m_run = -INFINITY;
   float l_run = 0.0f;
   floatx4 acc[D / 128][8];  // slab b, step jj: lane (c, qg) rows 4qg + i <-> dims 128b + 8(4qg+i) + jj
@@ -556,24 +649,25 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
   // kAhead tiles ahead, wait for the whole tile, then this wave's row does the math.
   // Every wave runs the same tiles, so the barrier is uniform over the workgroup.
   int buf = 0;
-  auto step = [&](u32x4 (&regs)[S::SLABS], int tok0) {
+  auto step = [&](typename E::Raw (&regs)[S::SLABS], int tok0) {
     uint16_t* tile = tiles[buf].v;
 #pragma unroll
     for (int sb = 0; sb < S::SLABS; ++sb)
-      *reinterpret_cast<u32x4*>(tile + (4 * qg + wave) * S::P + 128 * sb + 8 * c) = regs[sb];
+      *reinterpret_cast<u32x4*>(tile + (4 * qg + wave) * S::P + 128 * sb + 8 * c) = E::widen(regs[sb]);
     if (tok0 + kAhead * kTile < end) fetch(regs, tok0 + kAhead * kTile);
     if (__builtin_expect(tok0 < lo_all || tok0 + kTile > L, 0))
       zero_dead_rows<D, FOLDED>(tile, tok0, lo_all, L, c, qg, wave, wave + 1);
     __syncthreads();  // the tile is complete; the other buffer is free again
-    if (row_active) tile_math<D, G, FOLDED>(tile, tok0, lo, hi, qop, c, qg, m_run, l_run, acc);
+    if (row_active)
+      tile_math<D, G, FOLDED, E::kF16>(tile, tok0, lo, hi, qop, c, qg, m_run, l_run, acc);
     buf ^= 1;
   };
   for (int tok0 = c0; tok0 < end; tok0 += kAhead * kTile) {
-    step(stage[0], tok0);
-    if (tok0 + kTile >= end) break;
-    step(stage[1], tok0 + kTile);
-    if (tok0 + 2 * kTile >= end) break;
-    step(stage[2], tok0 + 2 * kTile);
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      if (tok0 + k * kTile >= end) break;
+      step(stage[k], tok0 + k * kTile);
+    }
   }
   if (row_active) {
     const int hq = g * G + (c % G);
@@ -742,14 +836,23 @@ __global__ __launch_bounds__(256) void query_fold_kernel(const float* q, const f
   *reinterpret_cast<floatx4*>(out + 4 * t) = x;
 }
 
-template <int D, int G, bool FOLDED>
+template <int D, int G, bool FOLDED, int KV>
 void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
   if (args.num_rows > 1)
-    hipLaunchKernelGGL((rows_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
-                       args);
+    hipLaunchKernelGGL((rows_partial_kernel<D, G, FOLDED, KV>), grid, dim3(64 * kWavesPerBlock), 0,
+                       s, args);
   else
-    hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s,
-                       args);
+    hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED, KV>), grid, dim3(64 * kWavesPerBlock), 0,
+                       s, args);
+}
+
+template <int D, int G, bool FOLDED>
+void launch_split_kv(int kv_dtype, const SplitArgs& args, dim3 grid, hipStream_t s) {
+  switch (kv_dtype) {
+    case ATTN_KV_F16: launch_split<D, G, FOLDED, ATTN_KV_F16>(args, grid, s); break;
+    case ATTN_KV_FP8_E4M3: launch_split<D, G, FOLDED, ATTN_KV_FP8_E4M3>(args, grid, s); break;
+    default: launch_split<D, G, FOLDED, ATTN_KV_BF16>(args, grid, s); break;
+  }
 }
 
 template <int D>
@@ -782,18 +885,19 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
 
   char* ws = static_cast<char*>(workspace);
   SplitArgs args;
+  const int64_t eb = kv_elem_bytes(d.kv_dtype);
   args.q = q;
-  args.pool = static_cast<const uint16_t*>(kv_pool);
+  args.pool = static_cast<const char*>(kv_pool);
   args.table = page_table;
   args.seq_lens = seq_lens;
   args.part_m = reinterpret_cast<float*>(ws + plan->off_part_m);
   args.part_l = reinterpret_cast<float*>(ws + plan->off_part_l);
   args.part_o = reinterpret_cast<float*>(ws + plan->off_part_o);
-  args.page_stride = d.page_stride;
-  args.head_stride = d.head_stride;
-  args.row_stride = d.row_stride;
-  args.k_offset = d.k_offset;
-  args.v_offset = d.v_offset;
+  args.page_stride = d.page_stride * eb;
+  args.head_stride = d.head_stride * eb;
+  args.row_stride = d.row_stride * eb;
+  args.k_offset = d.k_offset * eb;
+  args.v_offset = d.v_offset * eb;
   args.num_pages = d.num_pages;
   args.num_q_heads = d.num_q_heads;
   args.page_size = d.page_size;
@@ -803,17 +907,19 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   args.num_chunks = plan->num_chunks;
   args.num_rows = plan->num_rows;
   args.row_groups = plan->row_groups;
-  args.qscale = d.scale * kLog2e;
+  args.qscale_k = d.scale * kLog2e * d.k_scale;
+  args.qscale_v = d.scale * kLog2e * d.v_scale;
+  args.vscale = d.v_scale;
 
   const dim3 grid(plan->grid_x, d.num_kv_heads, d.batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
-    launch_split<512, 8, false>(args, grid, s);
+    launch_split_kv<512, 8, false>(d.kv_dtype, args, grid, s);
   else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
-    launch_split<512, 8, true>(args, grid, s);
+    launch_split_kv<512, 8, true>(d.kv_dtype, args, grid, s);
   else
-    launch_split<256, 2, false>(args, grid, s);
+    launch_split_kv<256, 2, false>(d.kv_dtype, args, grid, s);
   return launch_status();
 }
 
@@ -843,6 +949,7 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
   if (rc != ATTN_OK) return rc;
   if (!k || !v || !start_pos || !kv_pool || !page_table || num_new < 1) return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
+  if (d.kv_dtype != ATTN_KV_BF16) return ATTN_E_UNSUPPORTED;
   const int kcols = d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim;
   const int row_pieces = (kcols + d.head_dim) / 8;  // at most 128 for the supported shapes
   int64_t rows;

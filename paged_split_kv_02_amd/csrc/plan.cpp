@@ -37,7 +37,22 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 namespace attn {
 
+int kv_elem_bytes(int kv_dtype) {
+  switch (kv_dtype) {
+    case ATTN_KV_BF16: return 2;
+    case ATTN_KV_F16: return 2;
+    case ATTN_KV_FP8_E4M3: return 1;
+    case ATTN_KV_F32: return 4;
+    default: return 0;
+  }
+}
+
+bool kv_dtype_served(int kv_dtype) {
+  return kv_dtype == ATTN_KV_BF16 || kv_dtype == ATTN_KV_F16 || kv_dtype == ATTN_KV_FP8_E4M3;
+}
+
 bool shape_supported(const attn_decode_desc& d) {
+  if (!kv_dtype_served(d.kv_dtype)) return false;
   const int g = d.num_q_heads / d.num_kv_heads;
   if (d.head_dim == 512 && g == 8) {
     if (d.format == ATTN_KV_SPLIT) return d.rot_cols == 0;
@@ -64,14 +79,19 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
     return ATTN_E_INVALID_ARG;
   if (d.num_q_heads % d.num_kv_heads != 0) return ATTN_E_UNSUPPORTED;
   if (d.format != ATTN_KV_SPLIT && d.format != ATTN_KV_FOLDED) return ATTN_E_INVALID_ARG;
+  const int eb = kv_elem_bytes(d.kv_dtype);
+  if (eb == 0) return ATTN_E_INVALID_ARG;
   if (!shape_supported(d)) return ATTN_E_UNSUPPORTED;
   if (!std::isfinite(d.scale)) return ATTN_E_INVALID_ARG;
+  if (!(std::isfinite(d.k_scale) && d.k_scale > 0.0f) ||
+      !(std::isfinite(d.v_scale) && d.v_scale > 0.0f))
+    return ATTN_E_INVALID_ARG;
   if (d.page_size % kTile != 0) return ATTN_E_UNSUPPORTED;
 
   // Layout: 16-byte aligned rows and columns, non-negative strides, rows inside their page.
   const int64_t v[] = {d.page_stride, d.head_stride, d.row_stride, d.k_offset, d.v_offset};
   for (int64_t x : v)
-    if (x < 0 || x % 8 != 0) return ATTN_E_INVALID_ARG;
+    if (x < 0 || x % (16 / eb) != 0) return ATTN_E_INVALID_ARG;
   {
     uint64_t a, b, c, e;
     if (!mul_ok(uint64_t(d.num_kv_heads - 1), uint64_t(d.head_stride), &a) ||
@@ -81,7 +101,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
     if (e > uint64_t(d.page_stride)) return ATTN_E_INVALID_ARG;
     uint64_t pool_elems;
     if (!mul_ok(uint64_t(d.num_pages), uint64_t(d.page_stride), &pool_elems) ||
-        pool_elems > (uint64_t(1) << 62))
+        pool_elems > (uint64_t(1) << 60))
       return ATTN_E_OVERFLOW;
   }
 

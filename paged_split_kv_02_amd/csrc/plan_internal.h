@@ -14,6 +14,10 @@ constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
 constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)
 
+// Bytes of one pool element of the given type, 0 for an unknown type.
+int kv_elem_bytes(int kv_dtype);
+// Element types the partial kernels read.
+bool kv_dtype_served(int kv_dtype);
 bool shape_supported(const attn_decode_desc& d);
 int64_t row_extent(const attn_decode_desc& d);
 int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan);

@@ -36,7 +36,7 @@ class Device:
         self.desc = K.make_desc(**wl.desc_fields(num_chunks, merge_group))
         self.plan = K.attn_decode_plan(self.desc, wl.seq_lens)
         self.q = torch.from_numpy(np.ascontiguousarray(wl.q, dtype=np.float32)).to(dev)
-        self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(dev)
+        self.pool = torch.from_numpy(wl.pool.view(np.uint8)).to(dev)
         self.table = torch.from_numpy(wl.table).to(dev)
         lens = wl.seq_lens if seq_lens_dev is None else np.asarray(seq_lens_dev, dtype=np.int32)
         self.lens = torch.from_numpy(lens).to(dev)

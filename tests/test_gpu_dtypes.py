@@ -1,0 +1,101 @@
+"""GPU parity for the pool element types other than bf16: f16 rows (multiplied on
+f16 MFMA), and FP8 E4M3 rows with K and V dequantisation factors (widened to bf16
+on their way into LDS), against the fp64 oracle at the same bar as bf16."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_harness import Device, note
+from tests.test_gpu_parity import check, check_partials, run_case
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [synth.F16, synth.FP8]
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+@pytest.mark.parametrize("dt", DTYPES)
+def test_global_ragged(dt, fmt):
+    wl = synth.make_workload([1000, 333, 17], **synth.GLOBAL, fmt=fmt, seed=70, kv_dtype=dt,
+                             spare_pages=3, pad="nan")
+    for n in (0, 9):
+        _, got = run_case(wl, f"{dt} {fmt} L=1000,333,17 n={n}", num_chunks=n)
+        check(got, oracle.decode_attention(wl), f"{dt} {fmt} n={n}")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_partials_per_chunk(dt):
+    wl = synth.make_workload([1000, 333], **synth.GLOBAL, seed=71, kv_dtype=dt, spare_pages=2)
+    dev, got = run_case(wl, f"{dt} partials n=9", num_chunks=9, merge_group=4)
+    check_partials(dev, wl)
+    check(got, oracle.decode_attention(wl), f"{dt} partials")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_hostile_padding_bit_identical(dt):
+    """NaN, the largest finite value or zero in every slot no query sees: same bits."""
+    outs = []
+    for pad in ("nan", "big", "zero"):
+        wl = synth.make_workload([1000, 257, 16], **synth.GLOBAL, seed=72, kv_dtype=dt, pad=pad,
+                                 spare_pages=3)
+        _, got = run_case(wl, f"{dt} pad {pad}")
+        outs.append(got)
+    check(outs[0], oracle.decode_attention(wl), f"{dt} padding")
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+def test_sliding_batch(dt):
+    wl = synth.sliding_batch(seed=73, kv_dtype=dt, pad="nan")
+    _, got = run_case(wl, f"{dt} sliding batch")
+    check(got, oracle.decode_attention(wl), f"{dt} sliding")
+
+
+@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("rows", [3, 4])
+def test_rows(dt, rows):
+    wl = synth.make_workload([2000, rows + 6], **synth.GLOBAL, seed=74 + rows, kv_dtype=dt,
+                             num_rows=rows, pad="nan")
+    _, got = run_case(wl, f"{dt} rows={rows}")
+    check(got, oracle.decode_attention(wl), f"{dt} rows={rows}")
+    ws = synth.make_workload([1030, 40], **synth.SLIDING, seed=76 + rows, kv_dtype=dt,
+                             num_rows=rows, pad="nan", max_pages=64)
+    _, got = run_case(ws, f"{dt} sliding rows={rows}")
+    check(got, oracle.decode_attention(ws), f"{dt} sliding rows={rows}")
+
+
+def test_fp8_widening_is_exact():
+    """FP8 codes with unit factors and the bf16 pool of the same values (E4M3 is a subset
+    of bf16) give identical bits: the kernel multiplies the same bf16 operands."""
+    wl8 = synth.make_workload([3000, 700], **synth.GLOBAL, seed=78, kv_dtype=synth.FP8,
+                              k_scale=1.0, v_scale=1.0, pad="nan")
+    # make sure every class of code is present in live rows: subnormals, +-448, +-0
+    live = np.flatnonzero(oracle.e4m3_bits_to_f64(wl8.pool) == oracle.e4m3_bits_to_f64(wl8.pool))
+    rng = np.random.default_rng(78)
+    pick = rng.choice(live, size=4000, replace=False)
+    wl8.pool[pick] = rng.choice(np.array([0x01, 0x81, 0x07, 0x87, 0x08, 0x7E, 0xFE, 0x00, 0x80],
+                                         dtype=np.uint8), size=pick.size)
+    bf = torch.from_numpy(wl8.pool.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    wl16 = synth.make_workload([3000, 700], **synth.GLOBAL, seed=78, pad="nan")
+    wl16.pool = bf.view(torch.int16).numpy().view(np.uint16)
+    wl16.table = wl8.table
+    _, got8 = run_case(wl8, "fp8 with extreme codes")
+    _, got16 = run_case(wl16, "bf16 of the same values")
+    assert np.array_equal(got8.view(np.uint32), got16.view(np.uint32))
+    # the absolute bar is stated for N(0, 1) values; here V reaches 448, so it scales by that
+    check(got8, oracle.decode_attention(wl8), "fp8 extreme codes", tol=2e-3 * 448)
+
+
+@pytest.mark.parametrize("dt,fmt", [(synth.FP8, "split"), (synth.FP8, "folded"),
+                                    (synth.F16, "split")])
+def test_full_length_163k(dt, fmt):
+    note(f"[gpu] {dt} {fmt} L=163336: generating")
+    wl = synth.global_decode(163336, seed=79, fmt=fmt, kv_dtype=dt)
+    dev = Device(wl)
+    got = dev.run()
+    assert dev.guards_intact()
+    note(f"[gpu] {dt} {fmt} L=163336: oracle (n={dev.plan.num_chunks})")
+    check(got, oracle.decode_attention(wl), f"{dt} {fmt} 163K")

@@ -92,12 +92,34 @@ S = K.STATUS
     ([1024], dict(num_pages=1 << 62), "ATTN_E_OVERFLOW"),
     ([1024], dict(num_chunks=-1), "ATTN_E_INVALID_ARG"),
     ([1024], dict(window=-1), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(kv_dtype=4), "ATTN_E_INVALID_ARG"),              # unknown element type
+    ([1024], dict(kv_dtype=-1), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(kv_dtype=3), "ATTN_E_UNSUPPORTED"),              # f32: no kernel yet
+    ([1024], dict(k_scale=0.0), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(v_scale=-0.5), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(k_scale=float("inf")), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(v_scale=float("nan")), "ATTN_E_INVALID_ARG"),
+    # FP8 rows: offsets and strides must be multiples of 16 elements (16 bytes)
+    ([1024], dict(kv_dtype=2, v_offset=520), "ATTN_E_INVALID_ARG"),
+    ([1024], dict(kv_dtype=2, row_stride=1032), "ATTN_E_INVALID_ARG"),
 ])
 def test_plan_refusals(lens, fields, status):
     f = global_desc()
     f.update(fields)
     rc, _ = plan_status(lens, **f)
     assert rc == S[status], (rc, K.attn_decode_status_string(rc))
+
+
+@pytest.mark.parametrize("kv_dtype", [0, 1, 2])
+def test_plan_accepts_served_element_types(kv_dtype):
+    rc, p = plan_status([1024], **global_desc(1024, kv_dtype=kv_dtype, k_scale=0.5, v_scale=3.0))
+    assert rc == 0
+    assert p.desc.kv_dtype == kv_dtype and p.desc.k_scale == 0.5 and p.desc.v_scale == 3.0
+    # 16-bit rows accept 8-element alignment; FP8 rows need 16
+    rc, _ = plan_status([1024], **global_desc(1024, kv_dtype=kv_dtype, v_offset=520,
+                                              row_stride=1032, head_stride=256 * 1032,
+                                              page_stride=4 * 256 * 1032))
+    assert rc == (0 if kv_dtype < 2 else S["ATTN_E_INVALID_ARG"])
 
 
 def test_plan_accepts_exact_capacity_and_refuses_one_past():
@@ -131,8 +153,13 @@ def test_workspace_matches_gem_scratch_contract():
 
 
 def test_size_limits_fail_closed():
-    """A pool whose element count passes 2^62, or a merge grid past 65535 rows, is refused."""
+    """A pool whose element count passes 2^60, or a merge grid past 65535 rows, is refused."""
     rc, _ = plan_status([1024], **global_desc(1024, num_pages=1 << 62))
+    assert rc == S["ATTN_E_OVERFLOW"]
+    # page_stride is 2^20 elements: 2^40 pages reach the limit exactly, one more passes it
+    rc, _ = plan_status([1024], **global_desc(1024, num_pages=1 << 40))
+    assert rc == 0
+    rc, _ = plan_status([1024], **global_desc(1024, num_pages=(1 << 40) + 1))
     assert rc == S["ATTN_E_OVERFLOW"]
     hkv = 8191
     f = global_desc(1024, batch=9, num_q_heads=8 * hkv, num_kv_heads=hkv,
