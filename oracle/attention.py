@@ -24,6 +24,16 @@ What it computes, and where the pages fix it
   windows go through the paged decode kernels): row i of an n-row window is the token at
   position L - n + i and sees the keys before L - n + i + 1, i.e. each row is ordinary
   decode at its own length.
+* Prefill (prompt rows): the generated global prefill reads the split or folded pool
+  beside the decode kernels (pegainfer PR #1055, Description), the sliding family's
+  prompt rows attend through a varlen kernel with a window lower bound over pages of
+  64 (pegainfer PR #1057, Description; its gates cover crossing the window, ragged
+  prompts, a continuation and a tiny prompt, Verification), and prompt rows read keys
+  through the slot's page-table row (TensorFold PR #1619, body).  Reading taken: a
+  request with n new rows and L keys in all holds its new rows at positions L - n ..
+  L - 1, and each row attends causally, i.e. exactly as a decode token at length
+  position + 1 (n = 0: nothing to compute; n < L: a continuation after L - n earlier
+  keys).
 * Split-KV: each key chunk yields an online-softmax partial (running max M, sum
   S, unnormalised numerator O); partials merge with the exact rescaling identity
   M = max(Ma, Mb), S = Sa e^(Ma-M) + Sb e^(Mb-M), O likewise, then O / S; empty
@@ -58,6 +68,7 @@ __all__ = [
     "f32_bits_to_f64", "stored_to_f64", "visible_range", "row_view", "gather_rows",
     "keys_values", "dense_attention", "decode_attention", "partial_state", "empty_state",
     "merge", "finalize", "split_kv_attention", "paged_partials", "validate",
+    "prefill_attention", "prefill_row_index",
 ]
 
 
@@ -204,6 +215,38 @@ def decode_attention(wl) -> np.ndarray:
                 heads = slice(g * G, (g + 1) * G)
                 out[r, i, heads] = dense_attention(q[r, i, heads], K, V, wl.scale)
     return out if n > 1 else out[:, 0]
+
+
+def prefill_row_index(wl) -> list[tuple[int, int]]:
+    """(request, position) of every packed query row of a prefill workload."""
+    out = []
+    for r in range(wl.batch):
+        L = int(wl.seq_lens[r])
+        n = int(wl.q_lens[r])
+        out.extend((r, L - n + i) for i in range(n))
+    return out
+
+
+def prefill_attention(wl, rows: Sequence[int] | None = None) -> np.ndarray:
+    """fp64 output of paged prefill: [T][Hq][D] over the packed query rows (T = sum of
+    the requests' new rows), or only the packed rows listed in ``rows``.
+
+    A row of request r at position p attends to the keys at positions lo .. p of that
+    request (lo = 0, or p + 1 - W with a sliding window W), through the page table.
+    """
+    G = wl.num_q_heads // wl.num_kv_heads
+    index = prefill_row_index(wl)
+    sel = range(len(index)) if rows is None else [int(t) for t in rows]
+    out = np.empty((len(sel), wl.num_q_heads, wl.head_dim), dtype=np.float64)
+    for k, t in enumerate(sel):
+        r, p = index[t]
+        lo, hi = visible_range(p + 1, wl.window)
+        pos = np.arange(lo, hi)
+        for g in range(wl.num_kv_heads):
+            K, V = keys_values(wl, _stored_rows(wl, r, g, pos))
+            heads = slice(g * G, (g + 1) * G)
+            out[k, heads] = dense_attention(wl.q[t, heads], K, V, wl.scale)
+    return out
 
 
 # --------------------------------------------------------------------------------------

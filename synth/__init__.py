@@ -92,6 +92,9 @@ class Workload:
     fold_w: Optional[np.ndarray] = None   # float32 [D - rot_cols] (folded pair only)
     q_unfolded: Optional[np.ndarray] = None
     num_rows: int = 1        # query rows per request; > 1 makes q [B][rows][Hq][D]
+    # Prefill: new query rows per request (ragged, 0 allowed); q is then packed
+    # [sum(q_lens)][Hq][D], request r owning rows q_starts[r] .. q_starts[r + 1].
+    q_lens: Optional[np.ndarray] = None
     kv_dtype: str = BF16     # element type of the pool
     k_scale: float = 1.0     # K = stored value * k_scale
     v_scale: float = 1.0     # V = stored value * v_scale
@@ -100,10 +103,20 @@ class Workload:
     def group_size(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
+    def rows_of(self, r: int) -> int:
+        """Query rows of request r (its last positions)."""
+        return int(self.q_lens[r]) if self.q_lens is not None else self.num_rows
+
+    @property
+    def q_starts(self) -> np.ndarray:
+        """int32 [B + 1]: packed query rows of request r are q_starts[r] .. q_starts[r + 1]."""
+        lens = self.q_lens if self.q_lens is not None else np.full(self.batch, self.num_rows)
+        return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
     def visible(self, r: int) -> tuple[int, int]:
         """[lo, hi) of the key positions request r's rows attend to, together."""
         L = int(self.seq_lens[r])
-        first = L - self.num_rows + 1      # keys the first query row sees: [.., first)
+        first = L - max(self.rows_of(r), 1) + 1   # keys the first query row sees: [.., first)
         lo = max(0, first - self.window) if self.window > 0 else 0
         return lo, L
 
@@ -192,7 +205,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                   layout: str = HEAD_MAJOR, spare_pages: int = 4, pad: str = "nan",
                   max_pages: Optional[int] = None, extra_page: bool = True,
                   scale: Optional[float] = None, num_rows: int = 1, kv_dtype: str = BF16,
-                  k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> Workload:
+                  k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                  q_lens: Optional[Sequence[int]] = None) -> Workload:
     """Build a decode-step workload.
 
     Data is drawn per (request, logical page) in ascending order from ``seed``;
@@ -203,7 +217,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     ``num_rows`` > 1 gives every request a window of that many query rows (the last
     positions of the request), q shaped [B][rows][Hq][D].  ``kv_dtype`` picks the
     pool's element type; the dequantisation factors default to 1 (FP8: the
-    FP8_K_SCALE / FP8_V_SCALE pair).
+    FP8_K_SCALE / FP8_V_SCALE pair).  ``q_lens`` (prefill) gives every request its own
+    number of query rows (0 .. L); q is then packed [sum(q_lens)][Hq][D].
     """
     seq_lens = [int(x) for x in seq_lens]
     B = len(seq_lens)
@@ -222,11 +237,19 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
         v_scale = FP8_V_SCALE if kv_dtype == FP8 else 1.0
     if max_pages is None:
         max_pages = max((L + page_size - 1) // page_size for L in seq_lens)
-    if num_rows < 1 or any(L < num_rows for L in seq_lens):
+    if q_lens is not None:
+        q_lens = [int(x) for x in q_lens]
+        if len(q_lens) != B or any(n < 0 or n > L for n, L in zip(q_lens, seq_lens)):
+            raise ValueError("q_lens must give 0 .. L rows per request")
+        rows = [max(n, 1) for n in q_lens]
+        num_rows = 1
+    else:
+        rows = [num_rows] * B
+    if num_rows < 1 or any(L < n for L, n in zip(seq_lens, rows)):
         raise ValueError("every request needs at least num_rows keys")
-    # the first row of a window sees keys [.., L - num_rows + 1): its window reaches furthest back
-    spans = [resident_pages(L, page_size, window + num_rows - 1 if window > 0 else 0, extra_page)
-             for L in seq_lens]
+    # the first row of a window sees keys [.., L - rows + 1): its window reaches furthest back
+    spans = [resident_pages(L, page_size, window + n - 1 if window > 0 else 0, extra_page)
+             for L, n in zip(seq_lens, rows)]
     needed = sum(p1 - p0 for p0, p1 in spans)
     num_pages = needed + spare_pages
     page_stride, head_stride, row_stride = _strides(layout, num_kv_heads, page_size, row_cols)
@@ -235,7 +258,10 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     tgen = _gen(seed + 1000 if table_seed is None else table_seed)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
-    qshape = (B, num_q_heads, D) if num_rows == 1 else (B, num_rows, num_q_heads, D)
+    if q_lens is not None:
+        qshape = (sum(q_lens), num_q_heads, D)
+    else:
+        qshape = (B, num_q_heads, D) if num_rows == 1 else (B, num_rows, num_q_heads, D)
     q = torch.randn(*qshape, generator=gen, dtype=torch.float32).numpy()
     fold_w = None
     q_unfolded = None
@@ -256,7 +282,7 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
     k = 0
     for r, L in enumerate(seq_lens):
         p0, p1 = spans[r]
-        lo = max(0, L - num_rows + 1 - window) if window > 0 else 0
+        lo = max(0, L - rows[r] + 1 - window) if window > 0 else 0
         for j in range(p0, p1):
             pid = int(perm[k]); k += 1
             table[r, j] = pid
@@ -276,7 +302,8 @@ def make_workload(seq_lens: Sequence[int], *, num_q_heads: int, num_kv_heads: in
                     v_offset=v_off, q=q, pool=pool, table=table,
                     seq_lens=np.asarray(seq_lens, dtype=np.int32), fold_w=fold_w,
                     q_unfolded=q_unfolded, num_rows=num_rows, kv_dtype=kv_dtype,
-                    k_scale=float(k_scale), v_scale=float(v_scale))
+                    k_scale=float(k_scale), v_scale=float(v_scale),
+                    q_lens=None if q_lens is None else np.asarray(q_lens, dtype=np.int32))
 
 
 def _store_page(dst: np.ndarray, block: np.ndarray, layout: str, hkv: int, ps: int, cols: int):
@@ -336,6 +363,22 @@ def global_decode(L: int, seed: int = 1, fmt: str = SPLIT, **kw) -> Workload:
     """Global-layer decode at context L (10,602 / 40,002 / 81,653 / 163,336)."""
     kw.setdefault("spare_pages", 1)
     return make_workload([L], **GLOBAL, fmt=fmt, seed=seed, **kw)
+
+
+def global_prefill(n: int, context: int = 0, seed: int = 11, fmt: str = SPLIT, **kw) -> Workload:
+    """Global-layer prefill: a prompt of n new rows after ``context`` earlier tokens,
+    one request (10,602 rows: the prompt length the pages measure)."""
+    kw.setdefault("spare_pages", 1)
+    return make_workload([context + n], **GLOBAL, fmt=fmt, seed=seed, q_lens=[n], **kw)
+
+
+def sliding_prefill(seed: int = 12, batch: int = 16, max_len: int = 4096, **kw) -> Workload:
+    """Sliding-layer varlen prefill: 16 ragged prompts, lengths drawn uniformly from
+    1..4096, window 1024, every row of every prompt new."""
+    g = _gen(seed + 77)
+    lens = (torch.randint(1, max_len + 1, (batch,), generator=g)).tolist()
+    kw.setdefault("max_pages", max_len // SLIDING["page_size"])
+    return make_workload(lens, **SLIDING, seed=seed, q_lens=lens, **kw)
 
 
 def sliding_batch(seed: int = 4, batch: int = 16, max_len: int = 4096, **kw) -> Workload:

@@ -507,9 +507,98 @@ def pin_query_rows():
     assert np.array_equal(rows[:, 0], oracle.decode_attention(first))
 
 
+def brute_force_prefill(wl) -> np.ndarray:
+    """Prefill by brute force: the packed row of request r at position p is single-row
+    decode of length p + 1 over request r alone, evaluated by brute_force_decode."""
+    import dataclasses
+    out = np.zeros((wl.q.shape[0], wl.num_q_heads, wl.head_dim))
+    t = 0
+    for r in range(wl.batch):
+        L, n = int(wl.seq_lens[r]), int(wl.q_lens[r])
+        for i in range(n):
+            one = dataclasses.replace(wl, batch=1, table=wl.table[r:r + 1],
+                                      seq_lens=np.array([L - n + i + 1], dtype=np.int32),
+                                      q=np.ascontiguousarray(wl.q[t][None]), q_lens=None,
+                                      num_rows=1)
+            out[t] = brute_force_decode(one)[0]
+            t += 1
+    return out
+
+
+PREFILL_CASES = [
+    # (seq_lens, q_lens, Hq, Hkv, D, page_size, window, fmt, layout, kv_dtype)
+    # window crossing, ragged, continuation, a request with no new rows
+    ([9, 4, 16, 5], [9, 2, 7, 0], 4, 2, 17, 4, 6, "split", synth.HEAD_MAJOR, "bf16"),
+    # fresh prompt and a one-row continuation over the folded row
+    ([12, 3], [12, 1], 8, 1, 512, 4, 0, "folded", synth.TOKEN_MAJOR, "bf16"),
+    # tiny: one key, one row
+    ([1], [1], 2, 1, 8, 4, 0, "split", synth.HEAD_MAJOR, "bf16"),
+    # other element types with their dequantisation factors
+    ([10, 6], [4, 6], 4, 2, 33, 4, 5, "split", synth.TOKEN_MAJOR, "fp8_e4m3"),
+    ([7], [7], 4, 1, 512, 4, 0, "folded", synth.HEAD_MAJOR, "f16"),
+]
+
+
+def pin_prefill_brute_force():
+    """Every prompt row against the pure-Python definition (causal, windowed, ragged,
+    continuation, zero and one-row requests, split and folded rows, FP8 and f16)."""
+    for k, (lens, ql, hq, hkv, D, ps, W, fmt, layout, dt) in enumerate(PREFILL_CASES):
+        wl = synth.make_workload(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=ps,
+                                 window=W, fmt=fmt, layout=layout, seed=90 + k, q_lens=ql,
+                                 kv_dtype=dt, pad="nan", spare_pages=2)
+        got = oracle.prefill_attention(wl)
+        assert got.shape == (sum(ql), hq, D)
+        _assert_close(got, brute_force_prefill(wl), 1e-13, f"prefill case {k}")
+
+
+def pin_prefill_rows_are_decode():
+    """A prompt row is decode at its own length: each packed row equals the (separately
+    pinned) decode oracle on request r alone with length position + 1, bit for bit; the
+    last row of a request equals decode over its whole context."""
+    import dataclasses
+    for W in (0, 12):
+        wl = synth.make_workload([40, 33, 20], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                 page_size=8, window=W, seed=95 + W, q_lens=[40, 5, 1])
+        got = oracle.prefill_attention(wl)
+        for t, (r, p) in enumerate(oracle.prefill_row_index(wl)):
+            one = dataclasses.replace(wl, batch=1, table=wl.table[r:r + 1],
+                                      seq_lens=np.array([p + 1], dtype=np.int32),
+                                      q=np.ascontiguousarray(wl.q[t][None]), q_lens=None,
+                                      num_rows=1)
+            assert np.array_equal(got[t], oracle.decode_attention(one)[0]), (W, t)
+        sel = oracle.prefill_attention(wl, rows=[39, 44, 45])
+        assert np.array_equal(sel, got[[39, 44, 45]])
+
+
+def pin_prefill_causality():
+    """Rewriting the keys and values after a row's position leaves that row's output
+    unchanged bit for bit and changes the later rows; the first row of a fresh prompt is
+    v0 exactly."""
+    wl = synth.make_workload([24], num_q_heads=4, num_kv_heads=1, head_dim=32, page_size=8,
+                             seed=97, q_lens=[24])
+    base = oracle.prefill_attention(wl)
+    v0 = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [0])))[1][0]
+    assert all(np.array_equal(base[0, h], v0) for h in range(4))
+    p = 10
+    other = synth.make_workload([24], num_q_heads=4, num_kv_heads=1, head_dim=32, page_size=8,
+                                seed=98, q_lens=[24])
+    pool = wl.pool.copy()
+    for j in range(p + 1, 24):
+        page, slot = int(wl.table[0][j // 8]), j % 8
+        opage = int(other.table[0][j // 8])
+        dst = page * wl.page_stride + slot * wl.row_stride
+        src = opage * other.page_stride + slot * other.row_stride
+        pool[dst:dst + wl.row_cols] = other.pool[src:src + other.row_cols]
+    import dataclasses
+    moved = oracle.prefill_attention(dataclasses.replace(wl, pool=pool))
+    assert np.array_equal(moved[:p + 1], base[:p + 1])
+    assert not np.array_equal(moved[p + 1:], base[p + 1:])
+
+
 ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, pin_needle,
             pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
             pin_empty_merge_identity, pin_merge_identity_values, pin_window,
             pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed,
             pin_query_rows, pin_dtype_brute_force, pin_e4m3_codes, pin_f16_f32_codes,
-            pin_dequant_factors]
+            pin_dequant_factors, pin_prefill_brute_force, pin_prefill_rows_are_decode,
+            pin_prefill_causality]

@@ -151,6 +151,27 @@ def _e4m3_subnormal_as_normal(bits):
 
 _orig_e4m3 = OA.e4m3_bits_to_f64
 
+
+def _prefill_rows_from_zero(wl):
+    return [(r, i) for r in range(wl.batch) for i in range(int(wl.q_lens[r]))]
+
+
+def _prefill_excludes_own_key(wl, rows=None):
+    import dataclasses
+    G = wl.num_q_heads // wl.num_kv_heads
+    index = OA.prefill_row_index(wl)
+    sel = range(len(index)) if rows is None else list(rows)
+    out = np.empty((len(sel), wl.num_q_heads, wl.head_dim))
+    for k, t in enumerate(sel):
+        r, p = index[t]
+        lo, hi = OA.visible_range(max(p, 1), wl.window)
+        for g in range(wl.num_kv_heads):
+            K, V = OA.keys_values(wl, OA.stored_to_f64(OA.gather_rows(wl, r, g, np.arange(lo, hi)),
+                                                       wl.kv_dtype))
+            hs = slice(g * G, (g + 1) * G)
+            out[k, hs] = OA.dense_attention(wl.q[t, hs], K, V, wl.scale)
+    return out
+
 MUTANTS = {
     "rows_see_one_key_too_many": ("decode_attention", _rows_off_by_one),
     "k_v_swapped": ("keys_values", _kv_swapped),
@@ -167,6 +188,8 @@ MUTANTS = {
     "folded_key_takes_k_factor": ("keys_values", _folded_key_takes_k_factor),
     "e4m3_bias_8": ("e4m3_bits_to_f64", _e4m3_bias_8),
     "e4m3_subnormal_as_normal": ("e4m3_bits_to_f64", _e4m3_subnormal_as_normal),
+    "prefill_rows_from_zero": ("prefill_row_index", _prefill_rows_from_zero),
+    "prefill_excludes_own_key": ("prefill_attention", _prefill_excludes_own_key),
 }
 
 
