@@ -244,6 +244,69 @@ int attn_kv_write(const attn_decode_plan_t* plan, const float* k, const float* v
 int attn_query_fold(const attn_decode_plan_t* plan, const float* q, const float* norm_w,
                     float* q_out, void* stream);
 
+/*
+ * Paged prefill: the prompt rows of a batch of requests, each row attending causally to
+ * its request's keys through the page table.  pegainfer PR #1055 ("Description") serves
+ * the global family's prompt rows through a generated prefill over the split or folded
+ * pool beside the split-KV decode; pegainfer PR #1057 ("Description") serves the sliding
+ * family's prompt rows through a varlen kernel with a window lower bound over pages of
+ * 64, and its "Verification" gates that kernel on crossing the window, ragged prompts, a
+ * continuation and a tiny prompt; TensorFold PR #1619 ("body") reads prompt rows through
+ * the slot's page-table row.
+ *
+ * Request r has q_starts[r + 1] - q_starts[r] = n_r new rows (0 allowed), packed in q
+ * and out at rows q_starts[r] .. q_starts[r + 1] - 1, and L_r = seq_lens[r] keys in all
+ * (its new rows' keys already written to the pool).  Its row i sits at position
+ * p = L_r - n_r + i and attends to the keys at positions lo .. p, lo = 0 without a
+ * window and max(0, p + 1 - window) with one: each row is a decode token at length
+ * p + 1 (n_r < L_r is a continuation after L_r - n_r earlier keys).
+ * The descriptor is the decode descriptor (num_chunks, merge_group and num_rows are not
+ * used).  Supported: the decode shapes, bf16 pools, page_size a multiple of 32.
+ * The output is written directly (no workspace, no merge): one workgroup owns
+ * row_tile consecutive rows of one (request, KV head) and walks their keys in
+ * key_tile-key tiles, staged once in on-chip memory for all its rows and heads.
+ */
+typedef struct attn_prefill_plan_t {
+  uint64_t magic;
+  attn_decode_desc desc;
+  int32_t group_size;  /* query heads per KV head */
+  int32_t key_tile;    /* keys per tile (32) */
+  int32_t row_tile;    /* query rows per workgroup (8 at GQA 8, 32 at GQA 2) */
+  int32_t total_rows;  /* q_starts[batch] */
+  int32_t max_rows;    /* largest n_r */
+  int32_t grid_x;      /* row tiles per (request, KV head): ceil(max_rows / row_tile) */
+} attn_prefill_plan_t;
+
+/*
+ * Validate `desc`, the host lengths seq_lens_host[batch] and the host row offsets
+ * q_starts_host[batch + 1], and fill `plan`.  No device call is made.
+ * Refusals as attn_decode_plan for the descriptor (ATTN_E_INVALID_ARG,
+ * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); an element type other than bf16 or a page size
+ * not a multiple of 32 (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
+ * more rows than keys in a request (ATTN_E_INVALID_ARG); a length above
+ * max_pages_per_seq * page_size (ATTN_E_PAST_PAGES).
+ */
+int attn_prefill_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
+                      const int32_t* q_starts_host, attn_prefill_plan_t* plan);
+
+/*
+ * Enqueue the prefill kernel.
+ *   q          device, float32 [total_rows][num_q_heads][head_dim] (FOLDED: folded q')
+ *   kv_pool    device, bf16 pool laid out as described for attn_decode_desc
+ *   page_table device, int32 [batch][max_pages_per_seq]
+ *   seq_lens   device, int32 [batch]; q_starts device, int32 [batch + 1]; both must equal
+ *              what the plan was given.  A request whose device offsets the plan cannot
+ *              serve is skipped (nothing written); one whose device length or page ids the
+ *              plan cannot serve gets NaN rows.  Nothing is read past the pool or the rows.
+ *   out        device, float32 [total_rows][num_q_heads][head_dim]; only rows of requests
+ *              are written.
+ * Returns ATTN_E_PLAN on a bad plan, ATTN_E_INVALID_ARG on null pointers,
+ * ATTN_E_LAUNCH if HIP refuses.
+ */
+int attn_prefill(const attn_prefill_plan_t* plan, const float* q, const void* kv_pool,
+                 const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_starts,
+                 float* out, void* stream);
+
 /* Static, NUL-terminated text for a status code. */
 const char* attn_decode_status_string(int status);
 

@@ -15,7 +15,8 @@ from . import build as _build
 
 __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_plan",
            "attn_decode_split", "attn_decode_merge", "attn_decode_status_string", "make_desc",
-           "attn_kv_write", "attn_query_fold",
+           "attn_kv_write", "attn_query_fold", "AttnPrefillPlan", "attn_prefill_plan",
+           "attn_prefill",
            "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "ATTN_KV_BF16", "ATTN_KV_F16", "ATTN_KV_FP8_E4M3",
            "ATTN_KV_F32", "STATUS", "LIB_PATH", "SYMBOLS"]
 
@@ -29,7 +30,8 @@ STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
           "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
 SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_merge",
-           "attn_decode_status_string", "attn_kv_write", "attn_query_fold")
+           "attn_decode_status_string", "attn_kv_write", "attn_query_fold",
+           "attn_prefill_plan", "attn_prefill")
 LIB_PATH = _build.LIB
 
 
@@ -58,6 +60,13 @@ class AttnDecodePlan(ctypes.Structure):
                 ("off_part_o", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
 
 
+class AttnPrefillPlan(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint64), ("desc", AttnDecodeDesc),
+                ("group_size", ctypes.c_int32), ("key_tile", ctypes.c_int32),
+                ("row_tile", ctypes.c_int32), ("total_rows", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("grid_x", ctypes.c_int32)]
+
+
 class AttnDecodeError(RuntimeError):
     def __init__(self, call: str, status: int):
         self.status = status
@@ -79,6 +88,11 @@ def _load() -> ctypes.CDLL:
     lib.attn_kv_write.restype = ctypes.c_int
     lib.attn_query_fold.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P]
     lib.attn_query_fold.restype = ctypes.c_int
+    lib.attn_prefill_plan.argtypes = [ctypes.POINTER(AttnDecodeDesc), P, P,
+                                      ctypes.POINTER(AttnPrefillPlan)]
+    lib.attn_prefill_plan.restype = ctypes.c_int
+    lib.attn_prefill.argtypes = [ctypes.POINTER(AttnPrefillPlan), P, P, P, P, P, P, P]
+    lib.attn_prefill.restype = ctypes.c_int
     lib.attn_decode_status_string.argtypes = [ctypes.c_int]
     lib.attn_decode_status_string.restype = ctypes.c_char_p
     return lib
@@ -165,6 +179,29 @@ def attn_kv_write(plan: AttnDecodePlan, k, v, num_new: int, start_pos, kv_pool, 
                             _ptr(kv_pool), _ptr(page_table), _ptr(bad_rows), _stream(stream))
     if rc != 0:
         raise AttnDecodeError("attn_kv_write", rc)
+
+
+def attn_prefill_plan(desc: AttnDecodeDesc, seq_lens_host, q_starts_host) -> AttnPrefillPlan:
+    """Validate and plan a prefill; host int32 arrays of length batch and batch + 1."""
+    import numpy as np
+    lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    starts = np.ascontiguousarray(q_starts_host, dtype=np.int32)
+    if lens.size != desc.batch or starts.size != desc.batch + 1:
+        raise ValueError("seq_lens needs batch entries and q_starts batch + 1")
+    plan = AttnPrefillPlan()
+    rc = _lib.attn_prefill_plan(ctypes.byref(desc), lens.ctypes.data, starts.ctypes.data,
+                                ctypes.byref(plan))
+    if rc != 0:
+        raise AttnDecodeError("attn_prefill_plan", rc)
+    return plan
+
+
+def attn_prefill(plan: AttnPrefillPlan, q, kv_pool, page_table, seq_lens, q_starts, out,
+                 stream=None) -> None:
+    rc = _lib.attn_prefill(ctypes.byref(plan), _ptr(q), _ptr(kv_pool), _ptr(page_table),
+                           _ptr(seq_lens), _ptr(q_starts), _ptr(out), _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_prefill", rc)
 
 
 def attn_query_fold(plan: AttnDecodePlan, q, norm_w, q_out, stream=None) -> None:

@@ -9,14 +9,17 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_decode.so")
-SOURCES = [os.path.join(CSRC, "attn_decode.hip"), os.path.join(CSRC, "plan.cpp")]
-# Packed fp32 VALU forms are kept out of the generated code.  MFMA accumulators are
-# allocated as VGPRs (not AGPRs), so the softmax rescale touches them in place
-# instead of copying them across register files every tile.
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
-         "-Wall", "-Wno-unused-function"]
+# Packed fp32 VALU forms are kept out of all generated code.
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-function"]
+# Decode kernels: MFMA accumulators are allocated as VGPRs (not AGPRs), so the softmax
+# rescale touches them in place instead of copying them across register files every
+# tile.  The prefill kernel keeps its larger accumulator set in the AGPRs.
+UNITS = [("attn_decode.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+         ("prefill.hip", []),
+         ("plan.cpp", [])]
+SOURCES = [os.path.join(CSRC, name) for name, _ in UNITS]
 
 
 def hipcc() -> str:
@@ -28,17 +31,30 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile the library; always recompiles.  Returns the path of the .so."""
-    fd, tmp = tempfile.mkstemp(prefix="libattn_decode.", suffix=".so.tmp", dir=HERE)
-    os.close(fd)
-    cmd = [hipcc(), *FLAGS, *SOURCES, "-o", tmp]
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="attn_build.") as tmpdir:
+        objs = []
+        for name, extra in UNITS:
+            obj = os.path.join(tmpdir, name + ".o")
+            _run([cc, *COMMON, *extra, "-c", os.path.join(CSRC, name), "-o", obj], verbose)
+            objs.append(obj)
+        fd, tmp = tempfile.mkstemp(prefix="libattn_decode.", suffix=".so.tmp", dir=HERE)
+        os.close(fd)
+        try:
+            _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        except RuntimeError:
+            os.unlink(tmp)
+            raise
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        os.unlink(tmp)
         raise RuntimeError("HIP build failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     if verbose:
         print(" ".join(cmd))
-    os.replace(tmp, LIB)
-    return LIB
 
 
 if __name__ == "__main__":

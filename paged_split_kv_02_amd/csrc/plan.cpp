@@ -70,9 +70,9 @@ int64_t row_extent(const attn_decode_desc& d) {
   return k_end > v_end ? k_end : v_end;
 }
 
-int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan) {
-  if (!desc || !lens || !plan) return ATTN_E_INVALID_ARG;
-  const attn_decode_desc& d = *desc;
+// Checks shared by the decode and prefill plans: sizes, format, element type, scale
+// factors, 16-byte aligned strides and offsets, rows inside their page, pool size.
+int check_desc(const attn_decode_desc& d) {
   if (d.batch < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.head_dim < 1 ||
       d.page_size < 1 || d.max_pages_per_seq < 1 || d.window < 0 || d.num_chunks < 0 ||
       d.merge_group < 0 || d.num_pages < 1 || d.num_rows < 0)
@@ -104,6 +104,14 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
         pool_elems > (uint64_t(1) << 60))
       return ATTN_E_OVERFLOW;
   }
+  return ATTN_OK;
+}
+
+int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan) {
+  if (!desc || !lens || !plan) return ATTN_E_INVALID_ARG;
+  const attn_decode_desc& d = *desc;
+  const int rc0 = check_desc(d);
+  if (rc0 != ATTN_OK) return rc0;
 
   // Query rows: 1 = ordinary decode; a window of n rows uses groups of four rows.
   const int64_t rows = d.num_rows < 1 ? 1 : d.num_rows;
@@ -188,6 +196,67 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   return ATTN_OK;
 }
 
+bool prefill_shape_supported(const attn_decode_desc& d) {
+  return shape_supported(d) && d.kv_dtype == ATTN_KV_BF16 && d.page_size % kPrefillKeys == 0;
+}
+
+int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,
+                      attn_prefill_plan_t* plan) {
+  if (!desc || !lens || !q_starts || !plan) return ATTN_E_INVALID_ARG;
+  const attn_decode_desc& d = *desc;
+  const int rc0 = check_desc(d);
+  if (rc0 != ATTN_OK) return rc0;
+  if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
+  // A tile's rows are addressed with 32-bit byte offsets from its first row.
+  {
+    const int64_t eb = kv_elem_bytes(d.kv_dtype);
+    uint64_t a, b;
+    if (!mul_ok(uint64_t(kPrefillKeys - 1), uint64_t(d.row_stride * eb), &a) ||
+        !add_ok(a, uint64_t(row_extent(d) * eb), &b) || b > uint64_t(INT32_MAX))
+      return ATTN_E_OVERFLOW;
+  }
+
+  // Rows of request r are q_starts[r] .. q_starts[r + 1] (0 allowed); they are its last
+  // positions, so there are at most L_r of them, and L_r fits the table row.
+  if (q_starts[0] != 0) return ATTN_E_INVALID_ARG;
+  const int64_t cap = int64_t(d.max_pages_per_seq) * d.page_size;
+  int64_t max_rows = 0;
+  for (int r = 0; r < d.batch; ++r) {
+    const int64_t n = int64_t(q_starts[r + 1]) - q_starts[r];
+    const int64_t L = lens[r];
+    if (n < 0 || L < n) return ATTN_E_INVALID_ARG;
+    if (L > cap) return ATTN_E_PAST_PAGES;
+    if (n > max_rows) max_rows = n;
+  }
+  const int64_t total = q_starts[d.batch];
+  const int64_t row_tile = kPrefillColumns / (d.num_q_heads / d.num_kv_heads) * kWavesPerBlock;
+  const int64_t tiles = ceil_div(max_rows, row_tile);
+  uint64_t elems;
+  if (!mul_ok(uint64_t(total), uint64_t(d.num_q_heads) * uint64_t(d.head_dim), &elems) ||
+      elems > (uint64_t(1) << 60))
+    return ATTN_E_OVERFLOW;
+  if (tiles > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535) return ATTN_E_OVERFLOW;
+
+  attn_prefill_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  p.magic = kPrefillMagic;
+  p.desc = d;
+  p.group_size = d.num_q_heads / d.num_kv_heads;
+  p.key_tile = kPrefillKeys;
+  p.row_tile = int32_t(row_tile);
+  p.total_rows = int32_t(total);
+  p.max_rows = int32_t(max_rows);
+  p.grid_x = int32_t(tiles);
+  *plan = p;
+  return ATTN_OK;
+}
+
+int check_prefill_plan(const attn_prefill_plan_t* plan) {
+  if (!plan) return ATTN_E_INVALID_ARG;
+  if (plan->magic != kPrefillMagic) return ATTN_E_PLAN;
+  return ATTN_OK;
+}
+
 int check_plan(const attn_decode_plan_t* plan) {
   if (!plan) return ATTN_E_INVALID_ARG;
   if (plan->magic != kPlanMagic) return ATTN_E_PLAN;
@@ -206,6 +275,11 @@ int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes
 extern "C" int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
                                 attn_decode_plan_t* plan) {
   return attn::make_plan(desc, seq_lens_host, plan);
+}
+
+extern "C" int attn_prefill_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
+                                 const int32_t* q_starts_host, attn_prefill_plan_t* plan) {
+  return attn::make_prefill_plan(desc, seq_lens_host, q_starts_host, plan);
 }
 
 extern "C" const char* attn_decode_status_string(int status) {

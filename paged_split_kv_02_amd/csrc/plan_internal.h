@@ -13,6 +13,9 @@ constexpr int kWavesPerBlock = 4;    // one chunk per workgroup, one quarter per
 constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
 constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)
+constexpr uint64_t kPrefillMagic = 0x4c4c494645525050ull;  // "PPREFILL"
+constexpr int kPrefillKeys = 32;     // keys per prefill tile (one page holds whole tiles)
+constexpr int kPrefillColumns = 16;  // (query row, head) columns per wave in prefill
 
 // Bytes of one pool element of the given type, 0 for an unknown type.
 int kv_elem_bytes(int kv_dtype);
@@ -21,6 +24,11 @@ bool kv_dtype_served(int kv_dtype);
 bool shape_supported(const attn_decode_desc& d);
 int64_t row_extent(const attn_decode_desc& d);
 int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_plan_t* plan);
+int check_desc(const attn_decode_desc& d);
+bool prefill_shape_supported(const attn_decode_desc& d);
+int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,
+                      attn_prefill_plan_t* plan);
+int check_prefill_plan(const attn_prefill_plan_t* plan);
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 

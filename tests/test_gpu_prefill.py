@@ -1,0 +1,209 @@
+"""GPU parity of paged prefill (attn_prefill through the C ABI) against the fp64 oracle.
+
+Bar: max |GPU - oracle| <= 2e-3 (the global prefill gate of pegainfer PR #1055,
+Verification, taken against fp64), NMSE <= 1e-4 and correlation >= 0.9999.  Cases follow
+the windowed prefill gates of pegainfer PR #1057 (Verification): crossing the window,
+ragged prompts, a continuation and a tiny prompt; plus hostile padding, page-permutation
+and layout invariance, determinism, full-size sampled rows, the slow rescale path and
+device-side mismatches.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_split_kv_02_amd as K
+import synth
+from tests.gpu_harness import SENTINEL, compare, fnv1a, note
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+GUARD_ROWS = 2
+
+
+class PrefillDevice:
+    """A prefill workload's buffers on the GPU, its plan, and a guarded output."""
+
+    def __init__(self, wl, q_starts_dev=None, seq_lens_dev=None, table=None):
+        dev = torch.device("cuda:0")
+        self.wl = wl
+        self.desc = K.make_desc(**wl.desc_fields())
+        self.plan = K.attn_prefill_plan(self.desc, wl.seq_lens, wl.q_starts)
+        self.q = torch.from_numpy(np.ascontiguousarray(wl.q, dtype=np.float32)).to(dev)
+        self.pool = torch.from_numpy(wl.pool.view(np.uint8)).to(dev)
+        self.table = torch.from_numpy(wl.table if table is None else table).to(dev)
+        lens = wl.seq_lens if seq_lens_dev is None else np.asarray(seq_lens_dev, dtype=np.int32)
+        starts = wl.q_starts if q_starts_dev is None else np.asarray(q_starts_dev, dtype=np.int32)
+        self.lens = torch.from_numpy(np.ascontiguousarray(lens)).to(dev)
+        self.starts = torch.from_numpy(np.ascontiguousarray(starts)).to(dev)
+        self.row = wl.num_q_heads * wl.head_dim
+        T = int(wl.q_starts[-1])
+        self.out_buf = torch.full(((T + 2 * GUARD_ROWS) * self.row,), SENTINEL, dtype=torch.int32,
+                                  device=dev)
+        self.out = self.out_buf.view(torch.float32)[GUARD_ROWS * self.row:(GUARD_ROWS + T) * self.row]
+
+    def launch(self):
+        K.attn_prefill(self.plan, self.q, self.pool, self.table, self.lens, self.starts, self.out)
+
+    def run(self) -> np.ndarray:
+        self.launch()
+        torch.cuda.synchronize()
+        wl = self.wl
+        return self.out.cpu().numpy().reshape(-1, wl.num_q_heads, wl.head_dim).copy()
+
+    def guards_intact(self) -> bool:
+        ob = self.out_buf.cpu().numpy()
+        g = GUARD_ROWS * self.row
+        return bool(np.all(ob[:g] == SENTINEL) and np.all(ob[-g:] == SENTINEL))
+
+
+def check(got, ref, what, tol=TOL):
+    st = compare(got, ref)
+    note(f"  {what}: max|d|={st['max_abs']:.3e} max|o|={st['max_ref']:.3e} "
+         f"nmse={st['nmse']:.3e} corr={st['corr']:.9f}")
+    assert st["finite"], what
+    assert st["max_abs"] <= tol, (what, st)
+    assert st["nmse"] <= 1e-4 and st["corr"] >= 0.9999, (what, st)
+    return st
+
+
+def run_case(wl, what, **kw):
+    note(f"[gpu] prefill {what}")
+    dev = PrefillDevice(wl, **kw)
+    got = dev.run()
+    assert dev.guards_intact(), f"{what}: wrote outside out"
+    return dev, got
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_global_ragged(fmt):
+    """Fresh prompts, a continuation after earlier keys, a one-row request, a request with
+    no new rows, rows crossing pages of 256 and row tiles cut by the prompt's end."""
+    wl = synth.make_workload([300, 610, 1, 45, 257], **synth.GLOBAL, fmt=fmt, seed=200,
+                             q_lens=[300, 37, 1, 0, 257], spare_pages=3, pad="nan")
+    _, got = run_case(wl, f"global {fmt} ragged")
+    check(got, oracle.prefill_attention(wl), f"global {fmt} ragged")
+
+
+def test_sliding_window_cases():
+    """Window 1024 over pages of 64: a prompt crossing the window (1300 rows), a
+    continuation whose first rows already reach past the window, a short prompt and a
+    tiny one."""
+    wl = synth.make_workload([1300, 1500, 70, 1], **synth.SLIDING, seed=201,
+                             q_lens=[1300, 150, 70, 1], max_pages=40, pad="nan")
+    _, got = run_case(wl, "sliding window cases")
+    rows = list(range(0, 1300, 7)) + list(range(1300, 1521))
+    ref = oracle.prefill_attention(wl, rows=rows)
+    check(got[rows], ref, "sliding window cases")
+
+
+def test_hostile_padding_bit_identical():
+    """NaN, a huge value or zero in every slot no prompt row sees: same output bits."""
+    outs = []
+    for pad in ("nan", "big", "zero"):
+        wl = synth.make_workload([200, 1100], **synth.SLIDING, seed=202, q_lens=[200, 90],
+                                 pad=pad, max_pages=20)
+        _, got = run_case(wl, f"padding {pad}")
+        outs.append(got)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    check(outs[0], oracle.prefill_attention(wl), "padding")
+
+
+def test_page_permutation_and_layout_invariance():
+    """The same logical rows at other physical pages, or with the slots of all KV heads
+    interleaved (token-major pages), give the same bits; so do repeated runs."""
+    base = synth.make_workload([700, 300], **synth.GLOBAL, seed=203, q_lens=[700, 64])
+    other = synth.make_workload([700, 300], **synth.GLOBAL, seed=203, q_lens=[700, 64],
+                                table_seed=999)
+    tm = synth.make_workload([700, 300], **synth.GLOBAL, seed=203, q_lens=[700, 64],
+                             layout=synth.TOKEN_MAJOR)
+    assert not np.array_equal(base.table, other.table)
+    dev, a = run_case(base, "permutation base")
+    hashes = {fnv1a(a)}
+    for _ in range(4):
+        hashes.add(fnv1a(dev.run()))
+    assert len(hashes) == 1, "repeated runs differ"
+    _, b = run_case(other, "permutation other table")
+    _, c = run_case(tm, "token-major pages")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    check(a[::5], oracle.prefill_attention(base, rows=range(0, 764, 5)), "permutation")
+
+
+def test_slow_path_on_a_dominant_key():
+    """A key planted at position 100 scores ~113 nat above every other key for the rows
+    after it: beyond the headroom of the no-rescale loop (the probabilities would overflow),
+    so the workgroups recompute with rescaling.  Rows before it are ordinary."""
+    wl = synth.make_workload([400], **synth.GLOBAL, seed=204, q_lens=[400], pad="nan")
+    u = np.ascontiguousarray(wl.q[150, 0], dtype=np.float32)   # query head 0 of row 150
+    wl.q[:, 0, :] = u                                          # every row of head 0 asks for u
+    key = synth.f32_to_bf16_bits((5.0 * u).astype(np.float32))
+    j = 100
+    pid = int(wl.table[0][j // wl.page_size])
+    base = pid * wl.page_stride + (j % wl.page_size) * wl.row_stride + wl.k_offset  # KV head 0
+    wl.pool[base:base + wl.head_dim] = key
+    _, got = run_case(wl, "dominant key")
+    ref = oracle.prefill_attention(wl)
+    check(got, ref, "dominant key")
+    v100 = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [j])))[1][0]
+    assert np.max(np.abs(got[j:, 0] - v100)) <= 1e-5
+
+
+def test_full_size_global_sampled():
+    """The 10,602-token prompt of one request (pages of 256, shuffled), split and folded,
+    at the launch configuration the bench times; sampled rows against the oracle: the first
+    rows, row-tile and page boundaries, the last rows and a seeded random sample."""
+    rng = np.random.default_rng(7)
+    n = 10602
+    rows = sorted(set([0, 1, 7, 8, 9, 255, 256, 257, 4095, 4096, n - 9, n - 8, n - 2, n - 1]
+                      + rng.integers(0, n, 24).tolist()))
+    for fmt in ("split", "folded"):
+        note(f"[gpu] prefill {fmt} n=10602: generating")
+        wl = synth.global_prefill(n, seed=205, fmt=fmt)
+        dev, got = run_case(wl, f"{fmt} 10602 rows")
+        check(got[rows], oracle.prefill_attention(wl, rows=rows), f"{fmt} 10602 sampled")
+        assert fnv1a(dev.run()) == fnv1a(got)
+
+
+def test_full_size_sliding_sampled():
+    """Sixteen ragged prompts (lengths 1..4096, seeded), window 1024, pages of 64: the
+    sliding-layer varlen prefill at the size the bench times; sampled rows per request."""
+    wl = synth.sliding_prefill(seed=12)
+    _, got = run_case(wl, "sliding 16 ragged prompts")
+    rng = np.random.default_rng(8)
+    starts = wl.q_starts
+    rows = []
+    for r in range(wl.batch):
+        a, b = int(starts[r]), int(starts[r + 1])
+        rows += sorted(set([a, b - 1] + rng.integers(a, b, 3).tolist()))
+    check(got[rows], oracle.prefill_attention(wl, rows=rows), "sliding 16 sampled")
+
+
+def test_device_mismatches_fail_closed():
+    """Device inputs the plan cannot serve: a request whose device offsets claim more rows
+    than the plan allows is skipped (its rows keep the sentinel); a device length below the
+    row count, or a page id outside the pool, turns that request's rows into NaN; the other
+    requests are unaffected."""
+    wl = synth.make_workload([300, 200, 100], **synth.GLOBAL, seed=206, q_lens=[300, 50, 100],
+                             spare_pages=2)
+    good = run_case(wl, "mismatch baseline")[1]
+    starts = wl.q_starts.copy()            # [0, 300, 350, 450]
+    bad_starts = starts.copy()
+    bad_starts[1] = 0                      # request 0 claims 0 rows, request 1 claims 350 > 300
+    dev = PrefillDevice(wl, q_starts_dev=bad_starts)
+    got = dev.run()
+    assert np.all(got[0:300].view(np.uint32) == SENTINEL)     # request 1 skipped: rows 0..299 untouched
+    assert np.array_equal(got[350:].view(np.uint32), good[350:].view(np.uint32))
+    assert dev.guards_intact()
+    lens = wl.seq_lens.copy()
+    lens[1] = 10                           # fewer keys than its 50 rows
+    got = PrefillDevice(wl, seq_lens_dev=lens).run()
+    assert np.all(np.isnan(got[300:350]))
+    assert np.array_equal(got[:300].view(np.uint32), good[:300].view(np.uint32))
+    table = wl.table.copy()
+    table[2, 0] = wl.num_pages + 5         # a page id outside the pool for request 2
+    got = PrefillDevice(wl, table=table).run()
+    assert np.all(np.isnan(got[350:450]))
+    assert np.array_equal(got[:350].view(np.uint32), good[:350].view(np.uint32))

@@ -275,3 +275,89 @@ def test_rows_plan():
     rc, _ = plan_status([1000], **global_desc(1024, num_rows=-1))
     assert rc == S["ATTN_E_INVALID_ARG"]
 
+
+
+# ---------------------------------------------------------------------------- prefill plan
+
+def prefill_status(lens, starts, **fields):
+    d = K.make_desc(**fields)
+    p = K.AttnPrefillPlan()
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    starts = np.ascontiguousarray(starts, dtype=np.int32)
+    return K._lib.attn_prefill_plan(ctypes.byref(d), lens.ctypes.data, starts.ctypes.data,
+                                    ctypes.byref(p)), p
+
+
+def test_prefill_plan_layout_matches_header(tmp_path):
+    pfields = [f for f, _ in K.AttnPrefillPlan._fields_]
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){",
+           'printf("%zu\\n", sizeof(attn_prefill_plan_t));']
+    src += [f'printf("%zu\\n", offsetof(attn_prefill_plan_t, {f}));' for f in pfields]
+    src += ["return 0;}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(c)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(K.AttnPrefillPlan)
+    assert vals[1:] == [getattr(K.AttnPrefillPlan, f).offset for f in pfields]
+
+
+def test_prefill_plan_tiles():
+    rc, p = prefill_status([1024], [0, 1000], **global_desc())
+    assert rc == 0 and p.row_tile == 8 and p.key_tile == 32 and p.total_rows == 1000
+    assert p.max_rows == 1000 and p.grid_x == 125 and p.group_size == 8
+    f = dict(batch=3, num_q_heads=32, num_kv_heads=16, head_dim=256, format=0, rot_cols=0,
+             page_size=64, max_pages_per_seq=64, window=1024, scale=1 / 16, num_pages=200,
+             page_stride=16 * 64 * 512, head_stride=64 * 512, row_stride=512, k_offset=0,
+             v_offset=256)
+    rc, p = prefill_status([4096, 30, 700], [0, 4096, 4096, 4196], **f)
+    assert rc == 0 and p.row_tile == 32 and p.max_rows == 4096 and p.grid_x == 128
+    assert p.total_rows == 4196
+
+
+@pytest.mark.parametrize("lens,starts,fields,status", [
+    ([1024], [1, 1000], dict(), "ATTN_E_INVALID_ARG"),            # offsets must start at 0
+    ([1024], [0, 1025], dict(), "ATTN_E_INVALID_ARG"),            # more rows than keys
+    ([10, 10], [0, 5, 4], dict(batch=2), "ATTN_E_INVALID_ARG"),   # decreasing offsets
+    ([1025], [0, 1], dict(), "ATTN_E_PAST_PAGES"),
+    ([1024], [0, 8], dict(kv_dtype=2), "ATTN_E_UNSUPPORTED"),     # FP8: decode only
+    ([1024], [0, 8], dict(kv_dtype=1), "ATTN_E_UNSUPPORTED"),     # f16: decode only
+    ([1024], [0, 8], dict(page_size=16, max_pages_per_seq=64), "ATTN_E_UNSUPPORTED"),
+    ([1024], [0, 8], dict(head_dim=128), "ATTN_E_UNSUPPORTED"),
+    ([1024], [0, 8], dict(row_stride=1020), "ATTN_E_INVALID_ARG"),
+    ([1024], [0, 8], dict(batch=0), "ATTN_E_INVALID_ARG"),
+    # rows of a tile must be reachable with 32-bit offsets
+    ([1024], [0, 8], dict(row_stride=1 << 26, head_stride=1 << 34, page_stride=1 << 36),
+     "ATTN_E_OVERFLOW"),
+])
+def test_prefill_plan_refusals(lens, starts, fields, status):
+    f = global_desc()
+    f.update(fields)
+    rc, _ = prefill_status(lens, starts, **f)
+    assert rc == S[status], (rc, status)
+
+
+def test_prefill_plan_allows_empty_requests():
+    rc, p = prefill_status([1024, 5], [0, 0, 0], **global_desc(batch=2))
+    assert rc == 0 and p.total_rows == 0 and p.grid_x == 0
+
+
+def test_prefill_refuses_before_any_launch():
+    rc, p = prefill_status([1024], [0, 100], **global_desc())
+    assert rc == 0
+    fake = 1 << 20  # never dereferenced: every refusal below returns before a launch
+    bad = K.AttnPrefillPlan.from_buffer_copy(p)
+    bad.magic = 0
+    L = K._lib
+    assert L.attn_prefill(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None) == S["ATTN_E_PLAN"]
+    assert L.attn_prefill(None, fake, fake, fake, fake, fake, fake, None) == S["ATTN_E_INVALID_ARG"]
+    for k in range(6):
+        args = [fake] * 6
+        args[k] = None
+        assert L.attn_prefill(ctypes.byref(p), *args, None) == S["ATTN_E_INVALID_ARG"], k
+    # a decode plan is not a prefill plan
+    rc, dp = plan_status([1024], **global_desc())
+    assert L.attn_prefill(ctypes.cast(ctypes.byref(dp), ctypes.POINTER(K.AttnPrefillPlan)),
+                          fake, fake, fake, fake, fake, fake, None) == S["ATTN_E_PLAN"]
