@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attention µs/step + effective HBM GB/s (% peak) at 163K ctx, hd512"
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_global163k_split.txt")
 
 
@@ -155,6 +156,45 @@ def time_steps(res, steps, warmup, flush=None):
         step_ms.append(a.elapsed_time(c))
         split_ms.append(a.elapsed_time(b))
     return dict(total_ms=sum(step_ms), wall_s=None, split_ms=split_ms, step_ms=step_ms)
+
+
+def prefill_flops(wl) -> int:
+    """Algorithmic FLOPs of a prefill: 4 * D per (row, query head, visible key) (QK^T and
+    PV, one multiply-add each), a row at position p seeing min(p + 1, window) keys."""
+    total_keys = 0
+    for r in range(wl.batch):
+        L, n = int(wl.seq_lens[r]), int(wl.q_lens[r])
+        for p in range(L - n, L):
+            total_keys += min(p + 1, wl.window) if wl.window > 0 else p + 1
+    return 4 * wl.head_dim * wl.num_q_heads * total_keys
+
+
+def time_prefill(wl, launches=10, warmup=2, flush=None):
+    """Median duration of attn_prefill launches (events on the launch stream)."""
+    import numpy as np
+    import torch
+    import paged_split_kv_02_amd as K
+    dev = torch.device("cuda:0")
+    plan = K.attn_prefill_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens, wl.q_starts)
+    q = torch.from_numpy(np.ascontiguousarray(wl.q, dtype=np.float32)).to(dev)
+    pool = torch.from_numpy(wl.pool.view(np.uint8)).to(dev)
+    table = torch.from_numpy(wl.table).to(dev)
+    lens = torch.from_numpy(wl.seq_lens).to(dev)
+    starts = torch.from_numpy(wl.q_starts).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    times = []
+    for it in range(warmup + launches):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        K.attn_prefill(plan, q, pool, table, lens, starts, out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if it >= warmup:
+            times.append(a.elapsed_time(b))
+    return median(times), plan
 
 
 def median(xs):
@@ -329,6 +369,26 @@ def main():
                               "timing": "median of 20, cache flushed"}
             print(f"# {name}: {t * 1e3:.1f} us", file=sys.stderr, flush=True)
         del wres
+        # paged prefill: a 10,602-token global prompt (split and folded rows) and the
+        # sliding layers' 16 ragged prompts; compute-bound (MFMA), reported in TFLOP/s
+        for name, maker in (("global-prefill-10602-split", lambda: synth.global_prefill(10602, seed=11)),
+                            ("global-prefill-10602-folded",
+                             lambda: synth.global_prefill(10602, seed=11, fmt="folded")),
+                            ("sliding-prefill-16ragged-w1024", lambda: synth.sliding_prefill(seed=12))):
+            pwl = maker()
+            t, plan = time_prefill(pwl, flush=flush)
+            fl = prefill_flops(pwl)
+            tf = fl / (t * 1e-3) / 1e12
+            variants[name] = {"us": round(t * 1e3, 1), "rows": int(pwl.q_starts[-1]),
+                              "algorithmic_flops": fl, "tflops": round(tf, 1),
+                              "frac_bf16_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                              "mfma_issued_tflops": round(2 * tf, 1),
+                              "note": "query and probabilities enter the MFMA as high+low bf16 "
+                                      "parts: the MFMA work issued is twice the algorithmic",
+                              "timing": "median of 10 launches, cache flushed"}
+            print(f"# {name}: {t * 1e3:.1f} us, {tf:.1f} TFLOP/s algorithmic", file=sys.stderr,
+                  flush=True)
+            del pwl
         line["variants"] = variants
         del flush_buf
 

@@ -229,7 +229,7 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
     if (n > max_rows) max_rows = n;
   }
   const int64_t total = q_starts[d.batch];
-  const int64_t row_tile = kPrefillColumns / (d.num_q_heads / d.num_kv_heads) * kWavesPerBlock;
+  const int64_t row_tile = (d.head_dim == 256 ? 2 : 1) * kPrefillColumns / (d.num_q_heads / d.num_kv_heads);
   const int64_t tiles = ceil_div(max_rows, row_tile);
   uint64_t elems;
   if (!mul_ok(uint64_t(total), uint64_t(d.num_q_heads) * uint64_t(d.head_dim), &elems) ||

@@ -15,7 +15,7 @@ constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in th
 constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)
 constexpr uint64_t kPrefillMagic = 0x4c4c494645525050ull;  // "PPREFILL"
 constexpr int kPrefillKeys = 32;     // keys per prefill tile (one page holds whole tiles)
-constexpr int kPrefillColumns = 16;  // (query row, head) columns per wave in prefill
+constexpr int kPrefillColumns = 64;  // (query row, head) columns per prefill workgroup (x2 at D=256)
 
 // Bytes of one pool element of the given type, 0 for an unknown type.
 int kv_elem_bytes(int kv_dtype);

@@ -8,26 +8,34 @@
 // page-table row.  A row at position p sees the keys lo .. p (lo = p + 1 - window with a
 // window): it is a decode token at length p + 1.
 //
-// One workgroup = row_tile consecutive prompt rows of one (request, KV head).  Each of its
-// four waves owns 16 MFMA columns: (16 / G) rows x the G query heads of the KV head.
-// Per 32-key tile (whole tiles inside one page: the page id is read once per tile):
+// One workgroup = row_tile consecutive prompt rows of one (request, KV head), as four
+// waves.  A column block of 32 MFMA columns = (32 / G) rows x the G query heads of the KV
+// head belongs to a pair of waves at head dim 512, which split the head dimension (256
+// dims each: each holds half of the columns' query operand and half of their output), and
+// to a single wave at head dim 256.  Per 32-key tile
+// (whole tiles inside one page: the page id is read once per tile):
 //   * the tile's stored rows are copied from the pool straight into LDS with 16-byte
-//     global->LDS loads (no registers involved); the next tile is requested as soon as
-//     its buffer is free, so it lands while the current one is used.  The 16-byte chunks
-//     of a row are XOR-swizzled inside each 256-byte group (chunk lc of row k sits at
-//     lc ^ (k & 15)), which keeps both LDS read patterns below free of bank conflicts
-//     without padding, so every 1-KB load instruction fills one contiguous kilobyte;
-//   * S^T = K Q^T on MFMA (keys as rows, (row, head) as columns).  The fp32 query, with
-//     scale * log2(e) folded in, is split into a high and a low bf16 part and both are
-//     multiplied against each K fragment, so the scores keep ~16 mantissa bits;
-//   * causal and window masks by select; online softmax in base 2 with the reference
-//     maximum moved only when a tile exceeds it by 2^8 (rare rescales);
-//   * O^T += V^T P^T on MFMA with the probabilities again as high and low bf16 parts,
-//     taken straight from the score registers; V^T is assembled from 16-byte LDS row
-//     reads with byte permutes.  V rows of keys no row of the workgroup may see are
-//     zeroed on the way, so padding (NaN or huge) never reaches the sums.
-// The fp32 output accumulators (128 per lane at head dim 512) live in the accumulation
-// registers, the split query operand (128) in the vector registers.
+//     global->LDS loads (no registers involved), one kilobyte of one row per
+//     instruction; the next tile is requested as soon as its buffer is free, so it lands
+//     while the current one is used.  Staged rows are 16 bytes apart beyond their length,
+//     which keeps every LDS read pattern below free of bank conflicts and lets every
+//     read address be a per-lane base plus a constant;
+//   * each wave forms the partial S^T = K Q^T over its half of the dims on the 32x32x16
+//     MFMA (keys as rows, (row, head) as columns); the fp32 query, with scale * log2(e)
+//     folded in, enters as a high and a low bf16 part, both multiplied against each K
+//     fragment, so the scores keep ~16 mantissa bits.  The two halves are added through
+//     LDS in a fixed order, so both waves of a pair hold the same scores bit for bit;
+//   * causal and window masks by select; online softmax in base 2;
+//   * O^T += V^T P^T on the same MFMA for the wave's half of the dims, the probabilities
+//     again as high and low bf16 parts taken straight from the score registers; V^T is
+//     assembled from LDS row reads with byte permutes.  V rows of keys no row of the
+//     workgroup may see are zeroed on the way, so padding (NaN or huge) never reaches
+//     the sums.
+// The hot loop never rescales the accumulators (that would move them through the vector
+// registers every tile): a column's reference maximum is fixed by its first tile with a
+// visible key, when nothing has been accumulated yet, and probabilities may then grow to
+// 2^kHeadroom.  A larger score only raises a flag, and the workgroup recomputes its rows in
+// a second loop that does rescale.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,15 +48,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units; probabilities stay below 2^8
-constexpr int kKeys = kPrefillKeys;    // keys per tile: two 16-key MFMA blocks
+constexpr float kRescaleSlack = 8.0f;  // slow path: log2 units a tile may exceed the reference
+constexpr int kKeys = kPrefillKeys;    // keys per tile: the 32 rows of one MFMA block
 // Without rescaling, probabilities may reach 2^kHeadroom (log2 units above a column's
 // reference): far inside fp32 and bf16 range, with room for any sum of them.
 constexpr float kHeadroom = 64.0f;
+constexpr int kCols = 32;              // MFMA columns of a pair of waves
 
 template <bool B>
 struct Flag {
@@ -75,13 +86,19 @@ struct PShape {
   static constexpr int ROT = FOLDED ? 128 : 0;
   static constexpr int COLS = FOLDED ? ROT + D : 2 * D;  // staged elements per row
   static constexpr int ROW_BYTES = 2 * COLS;
-  static constexpr int TILE_BYTES = kKeys * ROW_BYTES;
+  static constexpr int PITCH = ROW_BYTES + 16;            // staged row pitch in LDS
+  static constexpr int TILE_BYTES = kKeys * PITCH;
   static constexpr int TV = FOLDED ? ROT : D;            // staged column of V[0]
-  static constexpr int KSTEPS = D / 32;                  // 32-dim MFMA steps of QK
-  static constexpr int SLABS = D / 128;                  // 128-dim slabs of PV
-  static constexpr int LOADS = TILE_BYTES / (1024 * kWavesPerBlock);  // 1-KB loads per wave
-  static_assert(TILE_BYTES % (1024 * kWavesPerBlock) == 0, "whole 1-KB loads per wave");
-  static_assert(ROW_BYTES % 256 == 0, "rows are whole 256-byte swizzle groups");
+  static constexpr int PAIR = D == 512 ? 2 : 1;          // waves sharing a column block
+  static constexpr int HALF = D / PAIR;                  // dims per wave
+  static constexpr int KSTEPS = HALF / 16;               // 16-dim MFMA steps of QK
+  static constexpr int DPR = HALF / 32;                  // dims per lane per V row read
+  static constexpr int WAVES = 4;                               // waves per workgroup
+  static constexpr int ROWS_PER_WAVE = kKeys / WAVES;            // staged rows a wave loads
+  static constexpr int FULL_KB = ROW_BYTES / 1024;              // whole kilobytes of a row
+  static constexpr int TAIL = ROW_BYTES % 1024;                 // 0 or 256 bytes
+  static_assert(TAIL == 0 || TAIL == 256, "a row is whole kilobytes plus at most 256 bytes");
+  static_assert(DPR == 8 || DPR == 4, "V reads of 16 or 8 bytes");
 };
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
@@ -90,8 +107,10 @@ __device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-__device__ __forceinline__ floatx4 mma(u32x4 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+// D = A B + C on the 32x32x16 bf16 MFMA.  Lane l holds A[l % 32][8(l / 32) + j] and
+// B[8(l / 32) + j][l % 32] (j = 0..7); element r of D is D[8(r / 4) + 4(l / 32) + r % 4][l % 32].
+__device__ __forceinline__ floatx16 mma(u32x4 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
 // Page-table entry through the scalar cache (uniform index; the table is only read).
@@ -108,48 +127,56 @@ __device__ __forceinline__ int64_t piece_col(const PrefillArgs& a, int sb) {
   return sb < VG ? a.k_offset + 256 * sb : a.v_offset + 256 * (sb - VG);
 }
 
-// LDS byte offset of logical 16-byte chunk lc of staged row k.
-template <int ROW_BYTES>
-__device__ __forceinline__ int lds_off(int k, int lc) {
-  return k * ROW_BYTES + ((lc ^ (k & 15)) << 4);
-}
-
 // Request one tile into `lds`.  `base` is the pool address of the tile's first row (page,
-// KV head, slot).  Load instruction u = k * 4 + wave fills LDS bytes [1024u, 1024u + 1024):
-// lane l's 16 bytes land at 1024u + 16l, i.e. physical chunk pc of staged row k, which
-// holds logical chunk pc ^ (k & 15) of that row.  `lane` is passed through an opaque
-// move first, so the per-lane offsets are recomputed here rather than kept live.
+// KV head, slot).  Wave w stages rows w, w + WAVES, ...; each kilobyte of a row is one load
+// instruction whose lane l brings the row's 16-byte chunk 64k + l (lanes 0..15 for a
+// 256-byte tail), landing at M0 + 16l.  `off[k]` is this lane's byte offset of that chunk
+// in the stored row, fixed for the whole kernel.
 template <int D, bool FOLDED>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const char* base, char* lds,
-                                           int wave, int lane) {
+                                           int wave, int lane, const uint32_t (&off)[2]) {
   using S = PShape<D, FOLDED>;
-  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int k = 0; k < S::LOADS; ++k) {
-    const int u = k * kWavesPerBlock + wave;
-    const int o = u * 1024 + lane * 16;
-    const int row = o / S::ROW_BYTES;
-    const int lc = ((o % S::ROW_BYTES) >> 4) ^ (row & 15);
-    const uint32_t off = uint32_t(row * int32_t(a.row_stride)) +
-                         uint32_t(piece_col<D, FOLDED>(a, lc >> 4)) + uint32_t((lc & 15) << 4);
-    __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(lds + u * 1024), 16, 0, 0);
+  for (int i = 0; i < S::ROWS_PER_WAVE; ++i) {
+    const int row = i * S::WAVES + wave;
+    const char* rb = base + int64_t(row) * a.row_stride;
+    char* lb = lds + row * S::PITCH;
+#pragma unroll
+    for (int k = 0; k < S::FULL_KB; ++k)
+      __builtin_amdgcn_global_load_lds(rb + off[k], (lds_void*)(lb + 1024 * k), 16, 0, 0);
+    if constexpr (S::TAIL != 0) {
+      if (lane < 16)
+        __builtin_amdgcn_global_load_lds(rb + off[1], (lds_void*)(lb + 1024), 16, 0, 0);
+    }
   }
 }
 
+// Key (inside a tile) of k index 8 * hh + j of PV MFMA t: the scores of MFMA rows
+// 8(r / 4) + 4hh + r % 4 with r = 8t + j, as they sit in the score registers.
+__device__ __forceinline__ int pv_key(int t, int hh, int j) {
+  return 16 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
+}
+
 template <int D, int G, bool FOLDED>
-__global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   using S = PShape<D, FOLDED>;
-  constexpr int RB = S::ROW_BYTES;
-  constexpr int RPC = kPrefillColumns / G;     // rows per wave
-  constexpr int QT = RPC * kWavesPerBlock;     // rows per workgroup
-  static_assert(kPrefillColumns % G == 0, "a wave holds whole rows");
+  constexpr int P = S::PITCH;
+  constexpr int HALF = S::HALF;
+  constexpr int DPR = S::DPR;
+  constexpr int RPP = kCols / G;               // rows per column block
+  constexpr int W = S::WAVES;
+  constexpr int QT = W / S::PAIR * RPP;        // rows per workgroup
+  static_assert(kCols % G == 0, "a pair holds whole rows");
   __shared__ __attribute__((aligned(1024))) char buf0[S::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf1[S::TILE_BYTES];
+  __shared__ floatx4 xs[W][4][64];  // partial scores, one slot per wave
 
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15;   // MFMA column (row, head) / K row inside a 16-key block
-  const int qg = lane >> 4;  // lane group: k sub-range / output rows
+  const int n = lane & 31;   // MFMA column: (row, head) of the pair / key row of a K fragment
+  const int hh = lane >> 5;  // k half of the MFMA operands / row group of the results
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int pair = wave / S::PAIR;  // column block
+  const int half = wave % S::PAIR;  // dims [half * HALF, (half + 1) * HALF)
   const int g = blockIdx.y;
   const int r = blockIdx.z;
   const int tile = a.row_tiles - 1 - int(blockIdx.x);  // the longest rows start first
@@ -157,23 +184,23 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillA
   // Offsets the plan cannot serve are not followed: nothing is read or written.
   const int qs0 = a.q_starts[r];
   const int qs1 = a.q_starts[r + 1];
-  const int n = qs1 - qs0;
-  if (qs0 < 0 || n < 0 || n > a.max_rows || qs1 > a.total_rows) return;
+  const int nrows = qs1 - qs0;
+  if (qs0 < 0 || nrows < 0 || nrows > a.max_rows || qs1 > a.total_rows) return;
   const int row0 = tile * QT;
-  if (row0 >= n) return;
+  if (row0 >= nrows) return;
   const int L = a.seq_lens[r];
-  bool poison = L < n || int64_t(L) > int64_t(a.max_pages) * a.page_size;
+  bool poison = L < nrows || int64_t(L) > int64_t(a.max_pages) * a.page_size;
 
   // This lane's column: row qrow of the request, query head `head`; it sees keys lo_c .. pos.
-  const int qrow = row0 + wave * RPC + c / G;
-  const bool active = qrow < n;
-  const int head = g * G + c % G;
-  const int pos = (active && !poison) ? L - n + qrow : -1;
+  const int qrow = row0 + pair * RPP + n / G;
+  const bool active = qrow < nrows;
+  const int head = g * G + n % G;
+  const int pos = (active && !poison) ? L - nrows + qrow : -1;
   const int lo_c = a.window > 0 ? max(0, pos + 1 - a.window) : 0;
 
   // Keys of the workgroup: the first row's window start .. the last row's position.
-  const int pos_first = L - n + row0;
-  const int pos_last = L - n + min(row0 + QT, n) - 1;
+  const int pos_first = L - nrows + row0;
+  const int pos_last = L - nrows + min(row0 + QT, nrows) - 1;
   const int lo_first = a.window > 0 ? max(0, pos_first + 1 - a.window) : 0;
   const int start = lo_first & ~(kKeys - 1);
   int ntiles = poison ? 0 : (pos_last + 1 - start + kKeys - 1) / kKeys;
@@ -187,89 +214,120 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillA
     return head_base + int64_t(pid) * a.page_stride + int64_t(k0 % a.page_size) * a.row_stride;
   };
 
+  // This lane's chunk of each staged kilobyte: chunk 64k + lane of the row, i.e. piece
+  // 4k + lane / 16 (a tail of 256 bytes is piece 4 read by lanes 0..15).
+  uint32_t off[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    off[k] = uint32_t(piece_col<D, FOLDED>(a, 4 * k + (S::TAIL != 0 && k == 1 ? 0 : lane >> 4))) +
+             uint32_t((lane & 15) << 4);
+
   // Request the first tile, then prepare the query operand while it streams.
   if (ntiles > 0) {
     const char* b = tile_base(start);
     if (b) {
-      issue_tile<D, FOLDED>(a, b, buf0, wave, lane);
+      issue_tile<D, FOLDED>(a, b, buf0, wave, lane, off);
     } else {
       poison = true;
       ntiles = 0;
     }
   }
 
-  // Query operand (B of the QK MFMA): lane (c, qg), k-step j holds dims 32j + 8qg + [0, 8)
-  // of column c, as a high and a low bf16 part.
+  // Query operand (B of the QK MFMA): lane (n, hh), step s holds dims
+  // half * HALF + 16s + 8hh + [0, 8) of column n, as a high and a low bf16 part.
   bf16x8 qhi[S::KSTEPS], qlo[S::KSTEPS];
   {
     const float* qp = a.q + (int64_t(qs0) + (active ? qrow : 0)) * a.num_q_heads * D +
-                      int64_t(head) * D;
+                      int64_t(head) * D + half * HALF + 8 * hh;
 #pragma unroll
-    for (int j = 0; j < S::KSTEPS; ++j) {
-      const float qs = (FOLDED && 32 * j >= S::ROT) ? a.qscale_v : a.qscale_k;
+    for (int s = 0; s < S::KSTEPS; ++s) {
+      const float qs = (FOLDED && half * HALF + 16 * s >= S::ROT) ? a.qscale_v : a.qscale_k;
       floatx4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
       if (active) {
-        x0 = *reinterpret_cast<const floatx4*>(qp + 32 * j + 8 * qg);
-        x1 = *reinterpret_cast<const floatx4*>(qp + 32 * j + 8 * qg + 4);
+        x0 = *reinterpret_cast<const floatx4*>(qp + 16 * s);
+        x1 = *reinterpret_cast<const floatx4*>(qp + 16 * s + 4);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * qs;
         const __bf16 h = (__bf16)x;
-        qhi[j][e] = h;
-        qlo[j][e] = (__bf16)(x - (float)h);
+        qhi[s][e] = h;
+        qlo[s][e] = (__bf16)(x - (float)h);
       }
+      // Park the query operand in the accumulation registers, leaving the vector registers
+      // to the tile work (it is copied back next to each use).
+      asm volatile("" : "+a"(qhi[s]), "+a"(qlo[s]));
     }
   }
 
-  float m_run, l_run;
-  floatx4 acc[S::SLABS][8];  // slab b, step jj: lane (c, qg) rows 4qg + i <-> dims 128b + 8(4qg+i) + jj
-  bool overflow = false;     // a score exceeded the reference by more than kHeadroom
+  // LDS read bases of this lane: K fragments of row n at dims half*HALF + 8hh (+ the step),
+  // V of row 4hh at dims half*HALF + DPR*n (+ the key row).
+  const int kbase = n * P + 16 * hh;
+  const int vbase = 4 * hh * P + 2 * (S::TV + half * HALF + DPR * n);
+  // Interior tiles: all rows of the workgroup present and every key of the tile visible to
+  // all of them (at or after the last row's window start, at or before the first row).
+  const bool full_tile = row0 + QT <= nrows;
+  const int lo_last = a.window > 0 ? max(0, pos_last + 1 - a.window) : 0;
 
-  // One staged tile (keys k0 .. k0 + 31) for this wave's 16 columns.  Without RESCALE the
-  // reference maximum of a column is fixed by its first tile with a visible key (the
-  // accumulators are still zero then, so nothing is rescaled) and probabilities may grow
-  // to 2^kHeadroom; a larger score only raises `overflow`.  With RESCALE (the slow path
-  // for such workgroups) the reference follows the running maximum as in decode.
+  float m_run, l_run;
+  floatx16 acc[DPR];        // step jj: element r <-> dim half*HALF + DPR*(8(r/4) + 4hh + r%4) + jj
+  bool overflow = false;    // a score exceeded the reference by more than kHeadroom
+
+  // One staged tile (keys k0 .. k0 + 31) for this wave's half of its pair's 32 columns.
   auto compute = [&](const char* t, int k0, auto rescale) {
     constexpr bool RESCALE = decltype(rescale)::value;
-    // Scores: block kb holds keys k0 + 16kb + 4qg + i (lane (c, qg), i = 0..3) of column c.
-    // The K fragments of step j + 1 are read while step j multiplies.
-    floatx4 sh0 = {0.f, 0.f, 0.f, 0.f}, sl0 = sh0, sh1 = sh0, sl1 = sh0;
-    auto kfrag = [&](int j, int blk) {
-      const int kd = 32 * j + 8 * qg;
-      const int lc = ((FOLDED && kd >= S::ROT) ? S::TV + kd : kd) >> 3;
-      return *reinterpret_cast<const u32x4*>(t + lds_off<RB>(16 * blk + c, lc));
+    // Partial scores over this wave's dims; the K fragments of step s + 1 are read while
+    // step s multiplies.  Element e holds key 8(e/4) + 4hh + e%4 of column n.
+    floatx16 sp = {}, sq = {};  // high and low query parts: two independent chains
+    auto kfrag = [&](int s) {  // row n, dims half*HALF + 16s + 8hh .. + 8
+      const int kd = half * HALF + 16 * s;
+      const int col = (FOLDED && kd >= S::ROT) ? S::TV + kd : kd;
+      return *reinterpret_cast<const u32x4*>(t + kbase + 2 * col);
     };
-    u32x4 ka = kfrag(0, 0), kb = kfrag(0, 1);
+    constexpr int KA = 3;  // K fragments in flight ahead of the MFMAs
+    u32x4 kq[KA];
 #pragma unroll
-    for (int j = 0; j < S::KSTEPS; ++j) {
-      u32x4 na = ka, nb = kb;
-      if (j + 1 < S::KSTEPS) {
-        na = kfrag(j + 1, 0);
-        nb = kfrag(j + 1, 1);
-      }
+    for (int s = 0; s < KA; ++s) kq[s] = kfrag(s);
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+      const u32x4 kf = kq[s % KA];
+      if (s + KA < S::KSTEPS) kq[s % KA] = kfrag(s + KA);
       __builtin_amdgcn_sched_barrier(0);
-      sh0 = mma(ka, qhi[j], sh0);
-      sh1 = mma(kb, qhi[j], sh1);
-      sl0 = mma(ka, qlo[j], sl0);
-      sl1 = mma(kb, qlo[j], sl1);
+      sp = mma(kf, qhi[s], sp);
+      sq = mma(kf, qlo[s], sq);
       __builtin_amdgcn_sched_barrier(0);
-      ka = na;
-      kb = nb;
     }
-    const floatx4 s0 = sh0 + sl0, s1 = sh1 + sl1;
-
-    float sc[8];
+    sp += sq;
+    float sc[16];
+    if constexpr (S::PAIR == 2) {
+      // Add the pair's two halves in a fixed order (half 0 first): identical in both waves.
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[wave][e][lane] = floatx4{sp[4 * e], sp[4 * e + 1], sp[4 * e + 2], sp[4 * e + 3]};
+      __syncthreads();
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const floatx4 other = xs[wave ^ 1][e4][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[4 * e4 + i] = half == 0 ? sp[4 * e4 + i] + other[i] : other[i] + sp[4 * e4 + i];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = sp[e];
+    }
+    // Tiles whose every key every row of the workgroup sees need no mask (uniform branch).
+    if (!(full_tile && k0 >= lo_last && k0 + kKeys - 1 <= pos_first)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const bool vis = (key >= lo_c) & (key <= pos);
+        sc[e] = vis ? sc[e] : -INFINITY;
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = k0 + (e < 4 ? 4 * qg + e : 16 + 4 * qg + (e - 4));
-      const float v = e < 4 ? s0[e] : s1[e - 4];
-      sc[e] = (key >= lo_c && key <= pos) ? v : -INFINITY;
-      mx = fmaxf(mx, sc[e]);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
     mx = fmaxf(mx, shfl_xor(mx, 32));
     if constexpr (RESCALE) {
       const bool grow = mx > m_run + kRescaleSlack;
@@ -278,71 +336,82 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillA
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
         l_run *= alpha;
 #pragma unroll
-        for (int b = 0; b < S::SLABS; ++b)
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
+        for (int jj = 0; jj < DPR; ++jj) acc[jj] *= alpha;
         m_run = m_new;
       }
     } else {
       if (m_run == -INFINITY) m_run = mx;  // first visible tile: nothing accumulated yet
       overflow |= mx > m_run + kHeadroom;
     }
-    // Probabilities as the PV B operand: k index 8qg + e <-> key of sc[e].
-    bf16x8 phi, plo;
+    // Probabilities as the PV B operands: MFMA t takes elements 8t .. 8t + 7.
+    bf16x8 phi[2], plo[2];
     float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
       const float p = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[e] - m_run);
       psum += p;
       const __bf16 h = (__bf16)p;
-      phi[e] = h;
-      plo[e] = (__bf16)(p - (float)h);
+      phi[e >> 3][e & 7] = h;
+      plo[e >> 3][e & 7] = (__bf16)(p - (float)h);
     }
     l_run += psum;
 
-    // PV: A = V^T of slab b, step jj: lane (c, qg) dims 128b + 8c + jj, keys of sc[0..7].
-    // Each slab's eight 16-byte V row reads are issued before its MFMAs.
+    // PV: A of MFMA t, step jj = V^T: lane (n, hh) holds dim half*HALF + DPR*n + jj of the
+    // keys pv_key(t, hh, j).  Eight row reads of DPR dims, then byte permutes.
     const bool edge = k0 < lo_first || k0 + kKeys - 1 > pos_last;  // uniform
+    auto vrows = [&](int tt, u32x4 (&w)[8]) {
 #pragma unroll
-    for (int b = 0; b < S::SLABS; ++b) {
-      u32x4 w[8];
+      for (int j = 0; j < 8; ++j) {
+        const int o = (pv_key(tt, hh, j) - 4 * hh) * P;  // vbase: row 4hh, the lane's dims
+        if constexpr (DPR == 8) {
+          w[j] = *reinterpret_cast<const u32x4*>(t + vbase + o);
+        } else {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(t + vbase + o);
+          w[j] = u32x4{x[0], x[1], 0u, 0u};
+        }
+      }
+    };
+    // The V rows of MFMA 1 are read while MFMA 0's products run.
+    u32x4 wv[2][8];
+    vrows(0, wv[0]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kr = e < 4 ? 4 * qg + e : 16 + 4 * qg + (e - 4);
-        w[e] = *reinterpret_cast<const u32x4*>(t + lds_off<RB>(kr, (S::TV >> 3) + 16 * b + c));
-        if (__builtin_expect(edge, 0)) {
-          const int key = k0 + kr;
-          if (key < lo_first || key > pos_last) w[e] = u32x4{0u, 0u, 0u, 0u};
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt == 0) vrows(1, wv[1]);
+      u32x4 (&w)[8] = wv[tt];
+      if (__builtin_expect(edge, 0)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = k0 + pv_key(tt, hh, j);
+          const unsigned keep = ((key >= lo_first) & (key <= pos_last)) ? ~0u : 0u;
+          w[j] &= u32x4{keep, keep, keep, keep};
         }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
+      for (int dd = 0; dd < DPR / 2; ++dd) {
         u32x4 ev, od;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           ev[u] = perm(w[2 * u + 1][dd], w[2 * u][dd], 0x05040100u);
           od[u] = perm(w[2 * u + 1][dd], w[2 * u][dd], 0x07060302u);
         }
-        acc[b][2 * dd] = mma(ev, phi, acc[b][2 * dd]);
-        acc[b][2 * dd + 1] = mma(od, phi, acc[b][2 * dd + 1]);
-        acc[b][2 * dd] = mma(ev, plo, acc[b][2 * dd]);
-        acc[b][2 * dd + 1] = mma(od, plo, acc[b][2 * dd + 1]);
+        acc[2 * dd] = mma(ev, phi[tt], acc[2 * dd]);
+        acc[2 * dd + 1] = mma(od, phi[tt], acc[2 * dd + 1]);
+        acc[2 * dd] = mma(ev, plo[tt], acc[2 * dd]);
+        acc[2 * dd + 1] = mma(od, plo[tt], acc[2 * dd + 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // All tiles of the workgroup, double-buffered: wait for this tile's loads (own, then
-  // everyone's via the barrier, which also frees the other buffer), request the next tile
-  // into the other buffer, use this one.
+  // everyone's via the barrier, which also frees the other buffer and the score slots),
+  // request the next tile into the other buffer, use this one.
   auto run = [&](auto rescale) {
     m_run = -INFINITY;
     l_run = 0.0f;
 #pragma unroll
-    for (int b = 0; b < S::SLABS; ++b)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < DPR; ++jj) acc[jj] = floatx16{};
     int count = ntiles;
     auto step = [&](const char* cur, char* nxt, int it) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -351,7 +420,7 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillA
       if (it + 1 < count) {
         const char* b = tile_base(k0 + kKeys);
         if (b) {
-          issue_tile<D, FOLDED>(a, b, nxt, wave, lane);
+          issue_tile<D, FOLDED>(a, b, nxt, wave, lane, off);
         } else {
           poison = true;
           count = it + 1;
@@ -365,33 +434,39 @@ __global__ __launch_bounds__(256, D == 256 ? 2 : 1) void prefill_kernel(PrefillA
     }
   };
   run(Flag<false>{});
-  if (__syncthreads_or(overflow)) {  // uniform: every wave of the workgroup takes it
-    __syncthreads();                 // the last tile's buffer is no longer read
-    if (ntiles > 0) issue_tile<D, FOLDED>(a, tile_base(start), buf0, wave, lane);
+
+  // Workgroup-wide OR of the overflow flags through the score slots.
+  __syncthreads();
+  if (lane == 0) xs[wave][0][0][0] = __any(overflow) ? 1.0f : 0.0f;
+  __syncthreads();
+  bool any_overflow = false;
+#pragma unroll
+  for (int w = 0; w < W; ++w) any_overflow |= xs[w][0][0][0] != 0.0f;
+  if (any_overflow) {  // uniform: every wave of the workgroup takes it
+    __syncthreads();   // the flags have been read
+    if (ntiles > 0) issue_tile<D, FOLDED>(a, tile_base(start), buf0, wave, lane, off);
     run(Flag<true>{});
   }
 
   if (!active) return;
-  l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  float* o = a.out + (int64_t(qs0) + qrow) * a.num_q_heads * D + int64_t(head) * D;
+  float* o = a.out + (int64_t(qs0) + qrow) * a.num_q_heads * D + int64_t(head) * D + half * HALF;
   const float qnan = __builtin_nanf("");
 #pragma unroll
-  for (int b = 0; b < S::SLABS; ++b)
+  for (int e = 0; e < 16; ++e) {
+    const int mrow = 8 * (e >> 2) + 4 * hh + (e & 3);
+    float v[DPR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      floatx4 w0 = floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]} * a.vscale / l_run;
-      floatx4 w1 = floatx4{acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]} * a.vscale / l_run;
-      if (poison) w0 = w1 = floatx4{qnan, qnan, qnan, qnan};
-      float* dst = o + 128 * b + 32 * qg + 8 * i;
-      *reinterpret_cast<floatx4*>(dst) = w0;
-      *reinterpret_cast<floatx4*>(dst + 4) = w1;
-    }
+    for (int jj = 0; jj < DPR; ++jj) v[jj] = poison ? qnan : acc[jj][e] * a.vscale / l_run;
+    float* dst = o + DPR * mrow;
+    *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
+    if constexpr (DPR == 8) *reinterpret_cast<floatx4*>(dst + 4) = floatx4{v[4], v[5], v[6], v[7]};
+  }
 }
 
 template <int D, int G, bool FOLDED>
 void launch_prefill(const PrefillArgs& args, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s, args);
+  hipLaunchKernelGGL((prefill_kernel<D, G, FOLDED>), grid, dim3(256), 0, s, args);
 }
 
 }  // namespace

@@ -132,11 +132,17 @@ def test_page_permutation_and_layout_invariance():
     check(a[::5], oracle.prefill_attention(base, rows=range(0, 764, 5)), "permutation")
 
 
-def test_slow_path_on_a_dominant_key():
-    """A key planted at position 100 scores ~113 nat above every other key for the rows
-    after it: beyond the headroom of the no-rescale loop (the probabilities would overflow),
-    so the workgroups recompute with rescaling.  Rows before it are ordinary."""
-    wl = synth.make_workload([400], **synth.GLOBAL, seed=204, q_lens=[400], pad="nan")
+@pytest.mark.parametrize("shape", ["global", "sliding"])
+def test_slow_path_on_a_dominant_key(shape):
+    """A key planted at position 100 scores ~113 nat (global) / ~80 nat (sliding) above every
+    other key for the rows after it: beyond the headroom of the no-rescale loop (the
+    probabilities would overflow), so the workgroups recompute with rescaling.  Rows before
+    it are ordinary."""
+    if shape == "global":
+        wl = synth.make_workload([400], **synth.GLOBAL, seed=204, q_lens=[400], pad="nan")
+    else:
+        wl = synth.make_workload([400], **synth.SLIDING, seed=204, q_lens=[400], pad="nan",
+                                 max_pages=8)
     u = np.ascontiguousarray(wl.q[150, 0], dtype=np.float32)   # query head 0 of row 150
     wl.q[:, 0, :] = u                                          # every row of head 0 asks for u
     key = synth.f32_to_bf16_bits((5.0 * u).astype(np.float32))
@@ -144,9 +150,9 @@ def test_slow_path_on_a_dominant_key():
     pid = int(wl.table[0][j // wl.page_size])
     base = pid * wl.page_stride + (j % wl.page_size) * wl.row_stride + wl.k_offset  # KV head 0
     wl.pool[base:base + wl.head_dim] = key
-    _, got = run_case(wl, "dominant key")
+    _, got = run_case(wl, f"dominant key {shape}")
     ref = oracle.prefill_attention(wl)
-    check(got, ref, "dominant key")
+    check(got, ref, f"dominant key {shape}")
     v100 = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [j])))[1][0]
     assert np.max(np.abs(got[j:, 0] - v100)) <= 1e-5
 

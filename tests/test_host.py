@@ -313,7 +313,7 @@ def test_prefill_plan_tiles():
              page_stride=16 * 64 * 512, head_stride=64 * 512, row_stride=512, k_offset=0,
              v_offset=256)
     rc, p = prefill_status([4096, 30, 700], [0, 4096, 4096, 4196], **f)
-    assert rc == 0 and p.row_tile == 32 and p.max_rows == 4096 and p.grid_x == 128
+    assert rc == 0 and p.row_tile == 64 and p.max_rows == 4096 and p.grid_x == 64
     assert p.total_rows == 4196
 
 
