@@ -326,7 +326,9 @@ def main():
                 ("global-decode-163336-split-f16",
                  lambda: synth.global_decode(163336, seed=9, kv_dtype=synth.F16), 20),
                 ("sliding-hd256-16ragged-w1024-fp8e4m3",
-                 lambda: synth.sliding_batch(seed=4, kv_dtype=synth.FP8), 20)):
+                 lambda: synth.sliding_batch(seed=4, kv_dtype=synth.FP8), 20),
+                ("global-decode-163336-split-f32",
+                 lambda: synth.global_decode(163336, seed=10, kv_dtype=synth.F32), 20)):
             vwl = maker()
             vres = Resident(vwl)
             vt = time_steps(vres, n_steps, 3, flush=flush)

@@ -62,7 +62,8 @@ enum {
  * FP8 E4M3 as the OCP 8-bit floating point specification defines it (bias 7,
  * subnormals, no infinity, S.1111.111 = NaN), the FP8 encoding gfx950 converts
  * natively.  Every type is widened exactly to the MFMA operand type (bf16 for BF16
- * and FP8, f16 for F16); F32 is not yet served (ATTN_E_UNSUPPORTED). */
+ * and FP8, f16 for F16); F32 rows are multiplied in full fp32 (split rows and one query
+ * row only: folded F32 rows and F32 windows of several rows are ATTN_E_UNSUPPORTED). */
 enum {
   ATTN_KV_BF16 = 0,
   ATTN_KV_F16 = 1,

@@ -361,6 +361,56 @@ struct PageWalker {
   }
 };
 
+// (m, l, O) of the G heads of one wave's quarter of a chunk, parked in LDS for the
+// workgroup merge (m in log2 units, NaN for a poisoned quarter).
+template <int D, int G>
+struct QuarterState {
+  float m[G], l[G];
+  floatx4 o[G][D / 4];
+};
+
+// Workgroup merge of the four quarter states (fixed order) into the chunk's state,
+// head by head, 4 dims per thread; written in natural-log units with O times v_scale.
+template <int D, int G>
+__device__ __forceinline__ void write_chunk_state(const SplitArgs& a,
+                                                  const QuarterState<D, G>* const (&parked)[kWavesPerBlock],
+                                                  int r, int g, int chunk) {
+  const float qnan = __builtin_nanf("");
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 64 * kWavesPerBlock) {
+    const int h = idx / (D / 4);
+    const int d4 = idx % (D / 4);
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const float x = parked[w]->m[h];
+      nan |= x != x;
+      M = fmaxf(M, x);
+    }
+    float S = 0.0f;
+    floatx4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float x = parked[w]->m[h];
+        const float wt = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
+        S += wt * parked[w]->l[h];
+        O += wt * parked[w]->o[h][d4];
+      }
+    }
+    const int64_t st = (int64_t(r) * a.num_q_heads + g * G + h) * a.num_chunks + chunk;
+    if (nan) {
+      M = S = qnan;
+      O = floatx4{qnan, qnan, qnan, qnan};
+    }
+    if (d4 == 0) {
+      a.part_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
+      a.part_l[st] = S;
+    }
+    *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O * a.vscale;
+  }
+}
+
 template <int D, int G, bool FOLDED, int KV>
 __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   using S = Shape<D, FOLDED>;
@@ -470,11 +520,8 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 
   // Workgroup merge of the four quarters (fixed order) into the chunk's state.  Each
   // wave parks (m, l, O) of its G heads in its own LDS tile; after the barrier the
-  // workgroup folds them head by head, 4 dims per thread.
-  struct Parked {
-    float m[G], l[G];
-    floatx4 o[G][D / 4];
-  };
+  // workgroup folds them.
+  using Parked = QuarterState<D, G>;
   static_assert(sizeof(Parked) <= sizeof(RowTile<COLS>), "parked state must fit the tile");
   Parked* mine = reinterpret_cast<Parked*>(tile);
   const float qnan = __builtin_nanf("");
@@ -496,39 +543,193 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const Parked* parked[kWavesPerBlock];
 #pragma unroll
   for (int w = 0; w < kWavesPerBlock; ++w) parked[w] = reinterpret_cast<const Parked*>(tiles[w].v);
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 64 * kWavesPerBlock) {
-    const int h = idx / (D / 4);
-    const int d4 = idx % (D / 4);
-    float M = -INFINITY;
-    bool nan = false;
+  write_chunk_state<D, G>(a, parked, r, g, chunk);
+}
+
+// ---------------------------------------------------------------------------------------
+// FP32 pools (the KV type of the gem design note's "Fixed production shape"): products in
+// full fp32 on v_mfma_f32_16x16x4_f32, so nothing is split into parts.  A wave copies the
+// K half of a 16-key tile of whole rows into its own LDS region with 16-byte global->LDS
+// loads (no registers carry them), forms the scores, then copies the V half into the same
+// region.  Each wave works alone until the workgroup merge of the quarter states.
+//   A (16 x 4): lane l holds A[l % 16][l / 16];  B (4 x 16): B[l / 16][l % 16];
+//   C (16 x 16): element i of lane l is C[4(l / 16) + i][l % 16].
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ floatx4 mma_f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct F32Shape {
+  static constexpr int HALF_BYTES = 4 * D;        // the K or the V half of a row
+  static constexpr int PITCH = HALF_BYTES + 16;   // staged row pitch: conflict-free reads
+  static constexpr int REGION = kTile * PITCH;    // one wave's LDS region
+  static constexpr int LOADS = HALF_BYTES / 1024; // 1-KB load instructions per row half
+  static constexpr int QSTEPS = D / 16;           // 16-dim groups of QK (4 MFMA steps each)
+  static constexpr int VBLOCKS = D / 64;          // 64-dim blocks of PV
+  static_assert(HALF_BYTES % 1024 == 0, "whole kilobytes per row half");
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
+  using S = F32Shape<D>;
+  static_assert(G <= 16, "heads of a KV head fit the 16 MFMA columns");
+  static_assert(sizeof(QuarterState<D, G>) <= S::REGION, "parked state must fit the region");
+  __shared__ __attribute__((aligned(16))) char region[kWavesPerBlock][S::REGION];
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;   // MFMA column (head) / K row inside the tile
+  const int qg = lane >> 4;  // lane group: k index of the MFMA operands / output rows
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int chunk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int r = blockIdx.z;
+  char* lds = region[wave];
+
+  const int L = a.seq_lens[r];
+  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int start = lo & ~(kTile - 1);
+  const int64_t cap = int64_t(a.max_pages) * a.page_size;
+  bool poison = L < 1 || int64_t(L) > cap ||
+                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
+  const int quarter = a.chunk_len / kWavesPerBlock;
+  const int c0 = start + chunk * a.chunk_len + wave * quarter;
+  const int c1 = min(c0 + quarter, L);
+  const int end = (!poison && c0 < c1) ? c1 : c0;
+  const char* head_base = a.pool + int64_t(g) * a.head_stride;
+  PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
+
+  // Query operand: lane (c, qg), group s, step j holds q[head c][16s + 4qg + j] times
+  // scale * log2(e) * k_scale (zero for columns past the G heads).  Parked in the
+  // accumulation registers, so the vector registers hold the output accumulators.
+  floatx4 qv[S::QSTEPS];
+  {
+    const float* qrow = a.q + (int64_t(r) * a.num_q_heads + g * G + (c < G ? c : 0)) * D + 4 * qg;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      const float x = parked[w]->m[h];
-      nan |= x != x;
-      M = fmaxf(M, x);
+    for (int s = 0; s < S::QSTEPS; ++s) {
+      qv[s] = c < G ? *reinterpret_cast<const floatx4*>(qrow + 16 * s) * a.qscale_k
+                    : floatx4{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(qv[s]));
     }
-    float S = 0.0f;
-    floatx4 O = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        const float x = parked[w]->m[h];
-        const float wt = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
-        S += wt * parked[w]->l[h];
-        O += wt * parked[w]->o[h][d4];
-      }
-    }
-    const int64_t st = (int64_t(r) * a.num_q_heads + g * G + h) * a.num_chunks + chunk;
-    if (nan) {
-      M = S = qnan;
-      O = floatx4{qnan, qnan, qnan, qnan};
-    }
-    if (d4 == 0) {
-      a.part_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
-      a.part_l[st] = S;
-    }
-    *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O * a.vscale;
   }
+
+  // Copy the K (part 0) or V (part 1) half of the tile's 16 rows: instruction (row, k)
+  // brings one kilobyte of the row, lane l its 16-byte chunk 64k + l.
+  auto stage = [&](int32_t pid, int tok0, int part) {
+    const char* base = head_base + int64_t(pid) * a.page_stride +
+                       int64_t(tok0 % a.page_size) * a.row_stride + (part ? a.v_offset : a.k_offset) +
+                       16 * lane;
+#pragma unroll
+    for (int row = 0; row < kTile; ++row)
+#pragma unroll
+      for (int k = 0; k < S::LOADS; ++k)
+        __builtin_amdgcn_global_load_lds(base + int64_t(row) * a.row_stride + 1024 * k,
+                                         (lds_void*)(lds + row * S::PITCH + 1024 * k), 16, 0, 0);
+  };
+
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  floatx4 acc[S::VBLOCKS][4];  // block b, step jj: lane (c, qg) element i <-> dim 64b + 4(4qg+i) + jj
+#pragma unroll
+  for (int b = 0; b < S::VBLOCKS; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (c0 < end) pw.start(c0);
+  for (int tok0 = c0; tok0 < end; tok0 += kTile) {
+    const int32_t pid = pw.page_of(tok0);
+    if (pid < 0) {  // a table entry outside the pool poisons the quarter
+      poison = true;
+      break;
+    }
+    stage(pid, tok0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // Scores of keys tok0 + 4qg + i for head c: four independent chains (step j).
+    floatx4 sj[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                     {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < S::QSTEPS; ++s) {
+      const floatx4 kv = *reinterpret_cast<const floatx4*>(lds + c * S::PITCH + 64 * s + 16 * qg);
+      const floatx4 qq = qv[s];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sj[j] = mma_f32(kv[j], qq[j], sj[j]);
+    }
+    const floatx4 sc4 = (sj[0] + sj[1]) + (sj[2] + sj[3]);
+
+    // Online softmax (base 2), masked keys by select, lazy rescale as in the bf16 kernel.
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok0 + 4 * qg + i;
+      sc[i] = (t >= lo && t < L) ? sc4[i] : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_expect(__any(grow), 0)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < S::VBLOCKS; ++b)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[b][jj] *= alpha;
+      m_run = m_new;
+    }
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_run != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    }
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // V half into the same region (the K reads above have all returned: they fed the
+    // scores), then PV.  MFMA t takes keys 4qg + t, so lane (c, qg) supplies its own p[t]
+    // as B; A = V^T: lane (m, qg) holds dims 64b + 4m + jj of key 4qg + t.
+    stage(pid, tok0, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
+#pragma unroll
+    for (int b = 0; b < S::VBLOCKS; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kr = 4 * qg + t;
+        floatx4 vv = *reinterpret_cast<const floatx4*>(lds + kr * S::PITCH + 256 * b + 16 * c);
+        if (__builtin_expect(edge, 0)) {
+          const int key = tok0 + kr;
+          if (key < lo || key >= L) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[b][jj] = mma_f32(vv[jj], p[t], acc[b][jj]);
+      }
+  }
+
+  // Quarter state: sum l over the lane groups; park (m, l, O) for the workgroup merge.
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  using Parked = QuarterState<D, G>;
+  Parked* mine = reinterpret_cast<Parked*>(lds);
+  if (c < G) {
+    if (qg == 0) {
+      mine->m[c] = poison ? __builtin_nanf("") : m_run;
+      mine->l[c] = l_run;
+    }
+#pragma unroll
+    for (int b = 0; b < S::VBLOCKS; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mine->o[c][(64 * b + 16 * qg + 4 * i) / 4] =
+            floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+  }
+  __syncthreads();
+  const Parked* parked[kWavesPerBlock];
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) parked[w] = reinterpret_cast<const Parked*>(region[w]);
+  write_chunk_state<D, G>(a, parked, r, g, chunk);
 }
 
 // Write one query row's chunk state: low columns added onto the high ones, maximum in
@@ -848,6 +1049,12 @@ void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
 
 template <int D, int G, bool FOLDED>
 void launch_split_kv(int kv_dtype, const SplitArgs& args, dim3 grid, hipStream_t s) {
+  if constexpr (!FOLDED) {
+    if (kv_dtype == ATTN_KV_F32) {  // split rows, one query row (checked by the plan)
+      hipLaunchKernelGGL((f32_partial_kernel<D, G>), grid, dim3(64 * kWavesPerBlock), 0, s, args);
+      return;
+    }
+  }
   switch (kv_dtype) {
     case ATTN_KV_F16: launch_split<D, G, FOLDED, ATTN_KV_F16>(args, grid, s); break;
     case ATTN_KV_FP8_E4M3: launch_split<D, G, FOLDED, ATTN_KV_FP8_E4M3>(args, grid, s); break;

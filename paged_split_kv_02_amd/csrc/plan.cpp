@@ -48,11 +48,13 @@ int kv_elem_bytes(int kv_dtype) {
 }
 
 bool kv_dtype_served(int kv_dtype) {
-  return kv_dtype == ATTN_KV_BF16 || kv_dtype == ATTN_KV_F16 || kv_dtype == ATTN_KV_FP8_E4M3;
+  return kv_dtype == ATTN_KV_BF16 || kv_dtype == ATTN_KV_F16 || kv_dtype == ATTN_KV_FP8_E4M3 ||
+         kv_dtype == ATTN_KV_F32;
 }
 
 bool shape_supported(const attn_decode_desc& d) {
   if (!kv_dtype_served(d.kv_dtype)) return false;
+  if (d.kv_dtype == ATTN_KV_F32 && d.format != ATTN_KV_SPLIT) return false;  // split rows only
   const int g = d.num_q_heads / d.num_kv_heads;
   if (d.head_dim == 512 && g == 8) {
     if (d.format == ATTN_KV_SPLIT) return d.rot_cols == 0;
@@ -116,6 +118,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   // Query rows: 1 = ordinary decode; a window of n rows uses groups of four rows.
   const int64_t rows = d.num_rows < 1 ? 1 : d.num_rows;
   if (rows > kMaxRows) return ATTN_E_INVALID_ARG;
+  if (rows > 1 && d.kv_dtype == ATTN_KV_F32) return ATTN_E_UNSUPPORTED;  // one query row
   const int64_t groups = rows > 1 ? ceil_div(rows, kWavesPerBlock) : 1;
 
   // Lengths: rows <= L <= pages in a table row * page size.

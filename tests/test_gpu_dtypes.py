@@ -1,11 +1,13 @@
 """GPU parity for the pool element types other than bf16: f16 rows (multiplied on
-f16 MFMA), and FP8 E4M3 rows with K and V dequantisation factors (widened to bf16
-on their way into LDS), against the fp64 oracle at the same bar as bf16."""
+f16 MFMA), FP8 E4M3 rows with K and V dequantisation factors (widened to bf16
+on their way into LDS), and f32 rows (split rows, one query row; multiplied in full fp32
+on the fp32 MFMA), against the fp64 oracle at the same bar as bf16."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import paged_split_kv_02_amd as K
 import synth
 from tests.gpu_harness import Device, note
 from tests.test_gpu_parity import check, check_partials, run_case
@@ -13,11 +15,14 @@ from tests.test_gpu_parity import check, check_partials, run_case
 pytestmark = pytest.mark.gpu
 
 DTYPES = [synth.F16, synth.FP8]
+ALL_DTYPES = DTYPES + [synth.F32]   # f32: split rows and one query row only
 
 
 @pytest.mark.parametrize("fmt", ["split", "folded"])
-@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("dt", ALL_DTYPES)
 def test_global_ragged(dt, fmt):
+    if dt == synth.F32 and fmt == "folded":
+        pytest.skip("f32 pools hold split rows (the plan refuses folded f32)")
     wl = synth.make_workload([1000, 333, 17], **synth.GLOBAL, fmt=fmt, seed=70, kv_dtype=dt,
                              spare_pages=3, pad="nan")
     for n in (0, 9):
@@ -25,7 +30,7 @@ def test_global_ragged(dt, fmt):
         check(got, oracle.decode_attention(wl), f"{dt} {fmt} n={n}")
 
 
-@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("dt", ALL_DTYPES)
 def test_partials_per_chunk(dt):
     wl = synth.make_workload([1000, 333], **synth.GLOBAL, seed=71, kv_dtype=dt, spare_pages=2)
     dev, got = run_case(wl, f"{dt} partials n=9", num_chunks=9, merge_group=4)
@@ -33,7 +38,7 @@ def test_partials_per_chunk(dt):
     check(got, oracle.decode_attention(wl), f"{dt} partials")
 
 
-@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("dt", ALL_DTYPES)
 def test_hostile_padding_bit_identical(dt):
     """NaN, the largest finite value or zero in every slot no query sees: same bits."""
     outs = []
@@ -47,7 +52,7 @@ def test_hostile_padding_bit_identical(dt):
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
 
 
-@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("dt", ALL_DTYPES)
 def test_sliding_batch(dt):
     wl = synth.sliding_batch(seed=73, kv_dtype=dt, pad="nan")
     _, got = run_case(wl, f"{dt} sliding batch")
@@ -90,7 +95,7 @@ def test_fp8_widening_is_exact():
 
 
 @pytest.mark.parametrize("dt,fmt", [(synth.FP8, "split"), (synth.FP8, "folded"),
-                                    (synth.F16, "split")])
+                                    (synth.F16, "split"), (synth.F32, "split")])
 def test_full_length_163k(dt, fmt):
     note(f"[gpu] {dt} {fmt} L=163336: generating")
     wl = synth.global_decode(163336, seed=79, fmt=fmt, kv_dtype=dt)
@@ -99,3 +104,13 @@ def test_full_length_163k(dt, fmt):
     assert dev.guards_intact()
     note(f"[gpu] {dt} {fmt} L=163336: oracle (n={dev.plan.num_chunks})")
     check(got, oracle.decode_attention(wl), f"{dt} {fmt} 163K")
+
+
+def test_f32_refusals():
+    """f32 pools: folded rows and several query rows are refused by the plan."""
+    wl = synth.make_workload([100], **synth.GLOBAL, fmt="folded", seed=80, kv_dtype=synth.F32)
+    with pytest.raises(K.AttnDecodeError):
+        K.attn_decode_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens)
+    wl = synth.make_workload([100], **synth.GLOBAL, seed=80, kv_dtype=synth.F32, num_rows=2)
+    with pytest.raises(K.AttnDecodeError):
+        K.attn_decode_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens)

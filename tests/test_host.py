@@ -94,7 +94,8 @@ S = K.STATUS
     ([1024], dict(window=-1), "ATTN_E_INVALID_ARG"),
     ([1024], dict(kv_dtype=4), "ATTN_E_INVALID_ARG"),              # unknown element type
     ([1024], dict(kv_dtype=-1), "ATTN_E_INVALID_ARG"),
-    ([1024], dict(kv_dtype=3), "ATTN_E_UNSUPPORTED"),              # f32: no kernel yet
+    ([1024], dict(kv_dtype=3, format=1, rot_cols=128, v_offset=128), "ATTN_E_UNSUPPORTED"),  # f32: split rows only
+    ([1024], dict(kv_dtype=3, num_rows=2), "ATTN_E_UNSUPPORTED"),  # f32: one query row
     ([1024], dict(k_scale=0.0), "ATTN_E_INVALID_ARG"),
     ([1024], dict(v_scale=-0.5), "ATTN_E_INVALID_ARG"),
     ([1024], dict(k_scale=float("inf")), "ATTN_E_INVALID_ARG"),
@@ -110,7 +111,7 @@ def test_plan_refusals(lens, fields, status):
     assert rc == S[status], (rc, K.attn_decode_status_string(rc))
 
 
-@pytest.mark.parametrize("kv_dtype", [0, 1, 2])
+@pytest.mark.parametrize("kv_dtype", [0, 1, 2, 3])
 def test_plan_accepts_served_element_types(kv_dtype):
     rc, p = plan_status([1024], **global_desc(1024, kv_dtype=kv_dtype, k_scale=0.5, v_scale=3.0))
     assert rc == 0
@@ -119,7 +120,7 @@ def test_plan_accepts_served_element_types(kv_dtype):
     rc, _ = plan_status([1024], **global_desc(1024, kv_dtype=kv_dtype, v_offset=520,
                                               row_stride=1032, head_stride=256 * 1032,
                                               page_stride=4 * 256 * 1032))
-    assert rc == (0 if kv_dtype < 2 else S["ATTN_E_INVALID_ARG"])
+    assert rc == (0 if kv_dtype != 2 else S["ATTN_E_INVALID_ARG"])
 
 
 def test_plan_accepts_exact_capacity_and_refuses_one_past():
