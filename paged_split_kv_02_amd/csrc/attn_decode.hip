@@ -892,6 +892,39 @@ struct MergeArgs {
 __device__ __forceinline__ bool fold_states(const float* m, const float* l, const float* o,
                                             int64_t stride, int k0, int k1, float& M, float& S,
                                             floatx4& O) {
+  if (k1 - k0 <= 8) {
+    // Up to eight states: every load is issued before any arithmetic (one memory round
+    // trip); the same order of operations as below.
+    float mk[8], lk[8];
+    floatx4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u < k1) {
+        mk[u] = m[k0 + u];
+        lk[u] = l[k0 + u];
+        v[u] = *reinterpret_cast<const floatx4*>(o + int64_t(k0 + u) * stride);
+      }
+    }
+    M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < k1) {
+        nan |= mk[u] != mk[u];
+        M = fmaxf(M, mk[u]);
+      }
+    S = 0.0f;
+    O = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (nan || M == -INFINITY) return !nan;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < k1) {
+        const float w = mk[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mk[u] - M) * kLog2e);
+        S += w * lk[u];
+        O += w * v[u];
+      }
+    return true;
+  }
   M = -INFINITY;
   bool nan = false;
   for (int k = k0; k < k1; ++k) {
