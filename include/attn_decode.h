@@ -16,6 +16,10 @@
  *                      chooses the chunking and lays out the workspace.
  *   attn_decode_split  enqueues the partial kernel on a HIP stream.
  *   attn_decode_merge  enqueues the merge (level 1, level 2, O / S) on a stream.
+ * Around the step: attn_kv_write stores new tokens' K/V rows into the pages,
+ * attn_query_fold folds K's norm weight into the query for a folded pool, and
+ * attn_prefill_plan / attn_prefill run a request's prompt rows (causal, several rows
+ * per request) over the same pool and descriptor.
  *
  * Ownership: the caller owns every buffer (query, pool, page table, lengths,
  * workspace, output).  The library allocates nothing, keeps no mutable global
@@ -113,7 +117,7 @@ typedef struct attn_decode_desc {
                                  causally to the keys before L - n + i + 1 (drafted verify
                                  windows through the paged decode, TensorFold PR #1619, review
                                  thread); q and out are then [batch][n][num_q_heads][head_dim] */
-  int32_t kv_dtype;           /* ATTN_KV_BF16, ATTN_KV_F16 or ATTN_KV_FP8_E4M3 */
+  int32_t kv_dtype;           /* ATTN_KV_BF16, ATTN_KV_F16, ATTN_KV_FP8_E4M3 or ATTN_KV_F32 */
   float scale;                /* score = scale * q . k (1/sqrt(D) in the workloads) */
   float k_scale;              /* K = stored * k_scale; finite and > 0 */
   float v_scale;              /* V = stored * v_scale; finite and > 0 */
