@@ -12,21 +12,23 @@
 // waves.  A column block of 32 MFMA columns = (32 / G) rows x the G query heads of the KV
 // head belongs to a pair of waves at head dim 512, which split the head dimension (256
 // dims each: each holds half of the columns' query operand and half of their output), and
-// to a single wave at head dim 256.  Per 32-key tile
-// (whole tiles inside one page: the page id is read once per tile):
+// to a single wave at head dim 256.  Per 32-key tile (whole tiles inside one page: the
+// page id is read once per tile):
 //   * the tile's stored rows are copied from the pool straight into LDS with 16-byte
 //     global->LDS loads (no registers involved), one kilobyte of one row per
 //     instruction; the next tile is requested as soon as its buffer is free, so it lands
 //     while the current one is used.  Staged rows are 16 bytes apart beyond their length,
 //     which keeps every LDS read pattern below free of bank conflicts and lets every
 //     read address be a per-lane base plus a constant;
-//   * each wave forms the partial S^T = K Q^T over its half of the dims on the 32x32x16
-//     MFMA (keys as rows, (row, head) as columns); the fp32 query, with scale * log2(e)
-//     folded in, enters as a high and a low bf16 part, both multiplied against each K
-//     fragment, so the scores keep ~16 mantissa bits.  The two halves are added through
-//     LDS in a fixed order, so both waves of a pair hold the same scores bit for bit;
-//   * causal and window masks by select; online softmax in base 2;
-//   * O^T += V^T P^T on the same MFMA for the wave's half of the dims, the probabilities
+//   * each wave forms S^T = K Q^T over its dims on the 32x32x16 MFMA (keys as rows, (row,
+//     head) as columns), K fragments read three steps ahead; the fp32 query, with
+//     scale * log2(e) folded in, enters as a high and a low bf16 part, both multiplied
+//     against each K fragment, so the scores keep ~16 mantissa bits.  At head dim 512 the
+//     pair's two halves are added through LDS in a fixed order, so both waves of the pair
+//     hold the same scores bit for bit;
+//   * causal and window masks by select (skipped on interior tiles); online softmax in
+//     base 2;
+//   * O^T += V^T P^T on the same MFMA for the wave's dims, the probabilities
 //     again as high and low bf16 parts taken straight from the score registers; V^T is
 //     assembled from LDS row reads with byte permutes.  V rows of keys no row of the
 //     workgroup may see are zeroed on the way, so padding (NaN or huge) never reaches
@@ -332,8 +334,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     if constexpr (RESCALE) {
       const bool grow = mx > m_run + kRescaleSlack;
       if (__builtin_expect(__any(grow), 0)) {
+        // Columns of one wave see different key ranges: a column that keeps its maximum
+        // keeps its sums (exp2(-inf - -inf) would be NaN for one with no visible key yet).
         const float m_new = grow ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 from -inf
         l_run *= alpha;
 #pragma unroll
         for (int jj = 0; jj < DPR; ++jj) acc[jj] *= alpha;

@@ -157,6 +157,26 @@ def test_slow_path_on_a_dominant_key(shape):
     assert np.max(np.abs(got[j:, 0] - v100)) <= 1e-5
 
 
+def test_slow_path_with_rows_past_the_window():
+    """A dominant key at position 1100 of a 1400-row sliding prompt (window 1024): the
+    workgroups of rows 1088 and later recompute with rescaling, and their rows' windows
+    start at different tiles, so some columns of a wave have no visible key yet while
+    others move their maximum.  Those columns must come out unharmed."""
+    wl = synth.make_workload([1400], **synth.SLIDING, seed=207, q_lens=[1400], pad="nan",
+                             max_pages=24)
+    u = np.ascontiguousarray(wl.q[700, 0], dtype=np.float32)
+    wl.q[:, 0, :] = u
+    j = 1100
+    pid = int(wl.table[0][j // wl.page_size])
+    base = pid * wl.page_stride + (j % wl.page_size) * wl.row_stride + wl.k_offset
+    wl.pool[base:base + wl.head_dim] = synth.f32_to_bf16_bits((5.0 * u).astype(np.float32))
+    _, got = run_case(wl, "dominant key past the window")
+    rows = sorted(set(range(0, 1400, 9)) | set(range(1080, 1230)) | set(range(1380, 1400)))
+    check(got[rows], oracle.prefill_attention(wl, rows=rows), "dominant key past the window")
+    vj = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [j])))[1][0]
+    assert np.max(np.abs(got[j:, 0] - vj)) <= 1e-5
+
+
 def test_full_size_global_sampled():
     """The 10,602-token prompt of one request (pages of 256, shuffled), split and folded,
     at the launch configuration the bench times; sampled rows against the oracle: the first
