@@ -39,6 +39,8 @@ def parse_args():
     ap.add_argument("--num-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--variants", default="",
+                    help="comma-separated substrings: time only the variants whose names hold one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference kernel for counters)")
     return ap.parse_args()
@@ -313,6 +315,11 @@ def main():
 
         def flush():
             flush_buf.zero_()  # 1 GiB of writes evicts the 256 MB infinity cache
+
+        pick = [x for x in args.variants.split(",") if x]
+
+        def wanted(name):
+            return not pick or any(x in name for x in pick)
         for name, maker, n_steps in (
                 ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
@@ -329,6 +336,8 @@ def main():
                  lambda: synth.sliding_batch(seed=4, kv_dtype=synth.FP8), 20),
                 ("global-decode-163336-split-f32",
                  lambda: synth.global_decode(163336, seed=10, kv_dtype=synth.F32), 20)):
+            if not wanted(name):
+                continue
             vwl = maker()
             vres = Resident(vwl)
             vt = time_steps(vres, n_steps, 3, flush=flush)
@@ -350,6 +359,8 @@ def main():
         wres = Resident(wlw)
         gen = torch.Generator(device="cuda:0").manual_seed(5)
         for name, n in (("kv-write-prompt-10602-split", 10602), ("kv-write-append-1-split", 1)):
+            if not wanted(name):
+                continue
             kk = torch.randn(1, n, 4, 512, generator=gen, device="cuda:0")
             vv = torch.randn(1, n, 4, 512, generator=gen, device="cuda:0")
             start = torch.tensor([10602 - n], dtype=torch.int32, device="cuda:0")
@@ -377,6 +388,8 @@ def main():
                             ("global-prefill-10602-folded",
                              lambda: synth.global_prefill(10602, seed=11, fmt="folded")),
                             ("sliding-prefill-16ragged-w1024", lambda: synth.sliding_prefill(seed=12))):
+            if not wanted(name):
+                continue
             pwl = maker()
             t, plan = time_prefill(pwl, flush=flush)
             fl = prefill_flops(pwl)
