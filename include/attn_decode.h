@@ -276,7 +276,7 @@ typedef struct attn_prefill_plan_t {
   attn_decode_desc desc;
   int32_t group_size;  /* query heads per KV head */
   int32_t key_tile;    /* keys per tile (32) */
-  int32_t row_tile;    /* query rows per workgroup (8 at GQA 8, 32 at GQA 2) */
+  int32_t row_tile;    /* query rows per workgroup (8 at head dim 512 / GQA 8, 64 at head dim 256 / GQA 2) */
   int32_t total_rows;  /* q_starts[batch] */
   int32_t max_rows;    /* largest n_r */
   int32_t grid_x;      /* row tiles per (request, KV head): ceil(max_rows / row_tile) */

@@ -238,7 +238,11 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
   if (!mul_ok(uint64_t(total), uint64_t(d.num_q_heads) * uint64_t(d.head_dim), &elems) ||
       elems > (uint64_t(1) << 60))
     return ATTN_E_OVERFLOW;
-  if (tiles > INT32_MAX || d.batch > 65535 || d.num_kv_heads > 65535) return ATTN_E_OVERFLOW;
+  // One workgroup per (row tile, KV head, request), launched in whole rounds of 256.
+  uint64_t heads, items;
+  if (!mul_ok(uint64_t(d.num_kv_heads), uint64_t(d.batch), &heads) ||
+      !mul_ok(uint64_t(tiles), heads, &items) || items > uint64_t(INT32_MAX - 255))
+    return ATTN_E_OVERFLOW;
 
   attn_prefill_plan_t p;
   std::memset(&p, 0, sizeof(p));

@@ -78,6 +78,7 @@ struct PrefillArgs {
   // Pool strides and column offsets in bytes; num_pages in pages.
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_q_heads, page_size, max_pages, window, total_rows, max_rows, row_tiles;
+  int32_t num_kv_heads, items;  // work items: row_tiles per (request, KV head)
   float qscale_k;  // scale * log2(e) * k_scale: query dims that meet K columns
   float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
   float vscale;    // v_scale, applied to the output
@@ -179,9 +180,17 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int pair = wave / S::PAIR;  // column block
   const int half = wave % S::PAIR;  // dims [half * HALF, (half + 1) * HALF)
-  const int g = blockIdx.y;
-  const int r = blockIdx.z;
-  const int tile = a.row_tiles - 1 - int(blockIdx.x);  // the longest rows start first
+  // Launch slot -> work item.  Workgroups are handed to the eight XCDs in turn (slot w
+  // runs on XCD w % 8), so runs of 32 consecutive items, i.e. neighbouring row tiles of one
+  // (request, KV head) whose key ranges overlap, are given to one XCD and share its L2;
+  // successive runs rotate over the XCDs.  The launch is padded to whole rounds of 256.
+  const int w = blockIdx.x;
+  const int slot = w >> 3;
+  const int item = ((slot >> 5) * 8 + (w & 7)) * 32 + (slot & 31);
+  if (item >= a.items) return;
+  const int g = (item / a.row_tiles) % a.num_kv_heads;
+  const int r = item / a.row_tiles / a.num_kv_heads;
+  const int tile = a.row_tiles - 1 - item % a.row_tiles;  // the longest rows start first
 
   // Offsets the plan cannot serve are not followed: nothing is read or written.
   const int qs0 = a.q_starts[r];
@@ -508,11 +517,13 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
   args.total_rows = plan->total_rows;
   args.max_rows = plan->max_rows;
   args.row_tiles = plan->grid_x;
+  args.num_kv_heads = d.num_kv_heads;
+  args.items = plan->grid_x * d.num_kv_heads * d.batch;  // bounded by the plan
   args.qscale_k = d.scale * kLog2e * d.k_scale;
   args.qscale_v = d.scale * kLog2e * d.v_scale;
   args.vscale = d.v_scale;
 
-  const dim3 grid(plan->grid_x, d.num_kv_heads, d.batch);
+  const dim3 grid((args.items + 255) / 256 * 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
