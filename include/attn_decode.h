@@ -152,8 +152,10 @@ typedef struct attn_decode_plan_t {
   uint64_t magic;
   attn_decode_desc desc;
   int32_t group_size;    /* query heads per KV head */
-  int32_t tile;          /* keys per tile; chunk starts are multiples of it */
-  int32_t chunk_len;     /* keys per chunk, a multiple of 4 * tile (one quarter per wave) */
+  int32_t tile;          /* keys per tile (16; 32 for several query rows at head dim 512
+                            over bf16 pages); chunk starts are multiples of it */
+  int32_t chunk_len;     /* keys per chunk: a multiple of 4 * tile for one query row (one
+                            quarter per wave), of tile for several */
   int32_t num_chunks;    /* chunks per (request, KV head) */
   int32_t merge_group;   /* chunk partials folded per level-1 group */
   int32_t num_groups;    /* level-1 states per (request, query head), at most 8 */

@@ -1154,7 +1154,10 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   const dim3 grid(plan->grid_x, d.num_kv_heads, d.batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
+  if (rows_on_tiles(d, plan->num_rows))
+    launch_rows_tiles(*plan, q, kv_pool, page_table, seq_lens, args.part_m, args.part_l,
+                      args.part_o, stream);
+  else if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
     launch_split_kv<512, 8, false>(d.kv_dtype, args, grid, s);
   else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
     launch_split_kv<512, 8, true>(d.kv_dtype, args, grid, s);

@@ -121,6 +121,9 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   if (rows > 1 && d.kv_dtype == ATTN_KV_F32) return ATTN_E_UNSUPPORTED;  // one query row
   const int64_t groups = rows > 1 ? ceil_div(rows, kWavesPerBlock) : 1;
 
+  // Keys per tile of the partial kernel the shape runs on.
+  const int64_t T = rows_on_tiles(d, rows) ? kPrefillKeys : kTile;
+
   // Lengths: rows <= L <= pages in a table row * page size.
   const int64_t cap = int64_t(d.max_pages_per_seq) * d.page_size;
   int64_t max_span = 0;
@@ -130,17 +133,18 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
     if (L > cap) return ATTN_E_PAST_PAGES;
     const int64_t first_hi = L - rows + 1;  // keys the first row sees: [.., first_hi)
     const int64_t lo = d.window > 0 && first_hi > d.window ? first_hi - d.window : 0;
-    const int64_t start = lo / kTile * kTile;
+    const int64_t start = lo / T * T;
     if (L - start > max_span) max_span = L - start;
   }
   if (max_span > INT32_MAX) return ATTN_E_OVERFLOW;
 
   // Chunking.  One row: one chunk per workgroup, one quarter of it per wave, so that
   // every SIMD of the chip streams one quarter; a quarter is never shorter than a
-  // tile.  Several rows: the four waves share each tile (one row each), so a chunk is
-  // whole tiles.  An explicit count is honoured (trailing chunks may then be empty).
+  // tile.  Several rows: the four waves share each tile (one row each on the 16-key
+  // kernel, a quarter of the dims each on the 32-key one), so a chunk is whole tiles.
+  // An explicit count is honoured (trailing chunks may then be empty).
   const int64_t split = rows > 1 ? 1 : kWavesPerBlock;  // waves a chunk is cut into
-  const int64_t tiles = ceil_div(max_span, kTile);
+  const int64_t tiles = ceil_div(max_span, T);
   int64_t n = d.num_chunks;
   if (n == 0) {
     const int64_t units = int64_t(d.batch) * d.num_kv_heads * groups;
@@ -151,7 +155,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   }
   if (n > (int64_t(1) << 24)) return ATTN_E_OVERFLOW;
   const int64_t piece_tiles = ceil_div(tiles, n * split);
-  const int64_t chunk_len = piece_tiles * kTile * split;
+  const int64_t chunk_len = piece_tiles * T * split;
   if (d.num_chunks == 0) n = ceil_div(max_span, chunk_len);
   // Launch order of the multi-row kernel: row groups of a chunk 8 workgroups apart.
   const int64_t grid_x = groups > 1 ? ceil_div(n, 8) * 8 * groups : n;
@@ -174,7 +178,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   p.magic = kPlanMagic;
   p.desc = d;
   p.group_size = d.num_q_heads / d.num_kv_heads;
-  p.tile = kTile;
+  p.tile = int32_t(T);
   p.chunk_len = int32_t(chunk_len);
   p.num_chunks = int32_t(n);
   p.merge_group = int32_t(gm);
@@ -199,6 +203,19 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   return ATTN_OK;
 }
 
+// In-row byte offsets of a 32-key tile (rows and columns) fit 31 bits.
+bool tile_offsets_fit(const attn_decode_desc& d) {
+  const int64_t eb = kv_elem_bytes(d.kv_dtype);
+  uint64_t a, b;
+  return mul_ok(uint64_t(kPrefillKeys - 1), uint64_t(d.row_stride * eb), &a) &&
+         add_ok(a, uint64_t(row_extent(d) * eb), &b) && b <= uint64_t(INT32_MAX);
+}
+
+bool rows_on_tiles(const attn_decode_desc& d, int64_t rows) {
+  return rows > 1 && d.head_dim == 512 && d.kv_dtype == ATTN_KV_BF16 &&
+         d.page_size % kPrefillKeys == 0 && tile_offsets_fit(d);
+}
+
 bool prefill_shape_supported(const attn_decode_desc& d) {
   return shape_supported(d) && d.kv_dtype == ATTN_KV_BF16 && d.page_size % kPrefillKeys == 0;
 }
@@ -211,13 +228,7 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
   if (rc0 != ATTN_OK) return rc0;
   if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
   // A tile's rows are addressed with 32-bit byte offsets from its first row.
-  {
-    const int64_t eb = kv_elem_bytes(d.kv_dtype);
-    uint64_t a, b;
-    if (!mul_ok(uint64_t(kPrefillKeys - 1), uint64_t(d.row_stride * eb), &a) ||
-        !add_ok(a, uint64_t(row_extent(d) * eb), &b) || b > uint64_t(INT32_MAX))
-      return ATTN_E_OVERFLOW;
-  }
+  if (!tile_offsets_fit(d)) return ATTN_E_OVERFLOW;
 
   // Rows of request r are q_starts[r] .. q_starts[r + 1] (0 allowed); they are its last
   // positions, so there are at most L_r of them, and L_r fits the table row.

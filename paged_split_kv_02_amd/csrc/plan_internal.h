@@ -29,6 +29,13 @@ bool prefill_shape_supported(const attn_decode_desc& d);
 int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,
                       attn_prefill_plan_t* plan);
 int check_prefill_plan(const attn_prefill_plan_t* plan);
+// Decode windows of several rows at head dim 512 over bf16 pages of whole 32-key tiles
+// (with in-row offsets below 2^31 bytes) run on the 32-key MFMA tile kernel, in chunks
+// of whole 32-key tiles; other shapes on the 16-key rows kernel.
+bool rows_on_tiles(const attn_decode_desc& d, int64_t rows);
+void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* kv_pool,
+                       const int32_t* page_table, const int32_t* seq_lens, float* part_m,
+                       float* part_l, float* part_o, void* stream);
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 

@@ -56,12 +56,20 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // slow path: log2 units a tile may exceed the reference
 constexpr int kKeys = kPrefillKeys;    // keys per tile: the 32 rows of one MFMA block
 // Without rescaling, probabilities may reach 2^kHeadroom (log2 units above a column's
 // reference): far inside fp32 and bf16 range, with room for any sum of them.
 constexpr float kHeadroom = 64.0f;
-constexpr int kCols = 32;              // MFMA columns of a pair of waves
+constexpr int kCols = 32;              // MFMA columns of a column block
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts, and the
+// load's cache policy: non-temporal (bit 1 on gfx94x / gfx950).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kStreamLoad = 2;
+// Decode windows: tiles staged in registers ahead of the math.  Two keep the stream
+// going; a third spills registers and measured slower.
+constexpr int kStageSets = 2;
 
 template <bool B>
 struct Flag {
@@ -82,25 +90,37 @@ struct PrefillArgs {
   float qscale_k;  // scale * log2(e) * k_scale: query dims that meet K columns
   float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
   float vscale;    // v_scale, applied to the output
+  // Decode windows (chunked): chunk states [request, row, head, chunk] (m, l) and
+  // [.., D] (O), the chunking of the plan, rows per request, groups of four rows.
+  float* part_m;
+  float* part_l;
+  float* part_o;
+  int32_t chunk_len, num_chunks, num_rows, row_groups;
 };
 
+// Staged tile of kKeys stored rows (whole rows: K and V columns of the row format).
 template <int D, bool FOLDED>
-struct PShape {
+struct PStage {
   static constexpr int ROT = FOLDED ? 128 : 0;
   static constexpr int COLS = FOLDED ? ROT + D : 2 * D;  // staged elements per row
   static constexpr int ROW_BYTES = 2 * COLS;
   static constexpr int PITCH = ROW_BYTES + 16;            // staged row pitch in LDS
   static constexpr int TILE_BYTES = kKeys * PITCH;
   static constexpr int TV = FOLDED ? ROT : D;            // staged column of V[0]
-  static constexpr int PAIR = D == 512 ? 2 : 1;          // waves sharing a column block
-  static constexpr int HALF = D / PAIR;                  // dims per wave
-  static constexpr int KSTEPS = HALF / 16;               // 16-dim MFMA steps of QK
-  static constexpr int DPR = HALF / 32;                  // dims per lane per V row read
-  static constexpr int WAVES = 4;                               // waves per workgroup
-  static constexpr int ROWS_PER_WAVE = kKeys / WAVES;            // staged rows a wave loads
-  static constexpr int FULL_KB = ROW_BYTES / 1024;              // whole kilobytes of a row
-  static constexpr int TAIL = ROW_BYTES % 1024;                 // 0 or 256 bytes
+  static constexpr int WAVES = 4;                        // waves per workgroup
+  static constexpr int ROWS_PER_WAVE = kKeys / WAVES;    // staged rows a wave loads
+  static constexpr int FULL_KB = ROW_BYTES / 1024;       // whole kilobytes of a row
+  static constexpr int TAIL = ROW_BYTES % 1024;          // 0 or 256 bytes
   static_assert(TAIL == 0 || TAIL == 256, "a row is whole kilobytes plus at most 256 bytes");
+};
+
+// SPLIT waves share a column block, each holding D / SPLIT dims of its query operand,
+// accumulators and K / V reads.
+template <int D, bool FOLDED, int SPLIT>
+struct PShape : PStage<D, FOLDED> {
+  static constexpr int HALF = D / SPLIT;   // dims per wave
+  static constexpr int KSTEPS = HALF / 16;  // 16-dim MFMA steps of QK
+  static constexpr int DPR = HALF / 32;     // dims per lane per V row read
   static_assert(DPR == 8 || DPR == 4, "V reads of 16 or 8 bytes");
 };
 
@@ -138,7 +158,7 @@ __device__ __forceinline__ int64_t piece_col(const PrefillArgs& a, int sb) {
 template <int D, bool FOLDED>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const char* base, char* lds,
                                            int wave, int lane, const uint32_t (&off)[2]) {
-  using S = PShape<D, FOLDED>;
+  using S = PStage<D, FOLDED>;
 #pragma unroll
   for (int i = 0; i < S::ROWS_PER_WAVE; ++i) {
     const int row = i * S::WAVES + wave;
@@ -160,61 +180,103 @@ __device__ __forceinline__ int pv_key(int t, int hh, int j) {
   return 16 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
 }
 
-template <int D, int G, bool FOLDED>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
-  using S = PShape<D, FOLDED>;
+// Rows of one (request, KV head) against their keys, over the staged tiles.  Two uses:
+//   * prefill (CHUNKED false): a work item is row_tile consecutive prompt rows; its keys
+//     run from the first row's window start to the last row's position, and the
+//     normalised output is written;
+//   * a decode window of several rows (CHUNKED true, head dim 512): a work item is one key
+//     chunk of one group of four rows (32 columns = 4 rows x 8 heads, each of the four
+//     waves holding a quarter of the dims), and the chunk's unnormalised state (m in
+//     natural-log units, l, O) is written for the merge, as by the one-row decode kernels.
+template <int D, int G, bool FOLDED, bool CHUNKED>
+__global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
+  constexpr int SPLIT = CHUNKED ? 4 : (D == 512 ? 2 : 1);  // waves sharing a column block
+  using S = PShape<D, FOLDED, SPLIT>;
   constexpr int P = S::PITCH;
   constexpr int HALF = S::HALF;
   constexpr int DPR = S::DPR;
   constexpr int RPP = kCols / G;               // rows per column block
   constexpr int W = S::WAVES;
-  constexpr int QT = W / S::PAIR * RPP;        // rows per workgroup
-  static_assert(kCols % G == 0, "a pair holds whole rows");
+  constexpr int QT = W / SPLIT * RPP;          // rows per workgroup
+  static_assert(kCols % G == 0, "a column block holds whole rows");
+  static_assert(!CHUNKED || D == 512, "decode windows on tiles: head dim 512");
   __shared__ __attribute__((aligned(1024))) char buf0[S::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf1[S::TILE_BYTES];
   __shared__ floatx4 xs[W][4][64];  // partial scores, one slot per wave
 
   const int lane = threadIdx.x & 63;
-  const int n = lane & 31;   // MFMA column: (row, head) of the pair / key row of a K fragment
+  const int n = lane & 31;   // MFMA column: (row, head) of the block / key row of a K fragment
   const int hh = lane >> 5;  // k half of the MFMA operands / row group of the results
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int pair = wave / S::PAIR;  // column block
-  const int half = wave % S::PAIR;  // dims [half * HALF, (half + 1) * HALF)
-  // Launch slot -> work item.  Workgroups are handed to the eight XCDs in turn (slot w
-  // runs on XCD w % 8), so runs of 32 consecutive items, i.e. neighbouring row tiles of one
-  // (request, KV head) whose key ranges overlap, are given to one XCD and share its L2;
-  // successive runs rotate over the XCDs.  The launch is padded to whole rounds of 256.
-  const int w = blockIdx.x;
-  const int slot = w >> 3;
-  const int item = ((slot >> 5) * 8 + (w & 7)) * 32 + (slot & 31);
-  if (item >= a.items) return;
-  const int g = (item / a.row_tiles) % a.num_kv_heads;
-  const int r = item / a.row_tiles / a.num_kv_heads;
-  const int tile = a.row_tiles - 1 - item % a.row_tiles;  // the longest rows start first
+  const int block = wave / SPLIT;  // column block
+  const int half = wave % SPLIT;   // dims [half * HALF, (half + 1) * HALF)
 
-  // Offsets the plan cannot serve are not followed: nothing is read or written.
-  const int qs0 = a.q_starts[r];
-  const int qs1 = a.q_starts[r + 1];
-  const int nrows = qs1 - qs0;
-  if (qs0 < 0 || nrows < 0 || nrows > a.max_rows || qs1 > a.total_rows) return;
-  const int row0 = tile * QT;
-  if (row0 >= nrows) return;
+  int g, r, qs0, nrows, row0, chunk = 0;
+  if constexpr (CHUNKED) {
+    // Launch order of the decode plan: the row groups of a chunk 8 slots apart, i.e. on
+    // one XCD, so a later group finds the chunk's rows in that XCD's L2.
+    const int lo8 = blockIdx.x % 8;
+    const int hi8 = blockIdx.x / 8;
+    chunk = (hi8 / a.row_groups) * 8 + lo8;
+    if (chunk >= a.num_chunks) return;  // padding of the launch order (whole workgroup)
+    g = blockIdx.y;
+    r = blockIdx.z;
+    nrows = a.num_rows;
+    qs0 = r * nrows;
+    row0 = (hi8 % a.row_groups) * QT;
+  } else {
+    // Launch slot -> work item.  Workgroups are handed to the eight XCDs in turn (slot w
+    // runs on XCD w % 8), so runs of 32 consecutive items, i.e. neighbouring row tiles of
+    // one (request, KV head) whose key ranges overlap, are given to one XCD and share its
+    // L2; successive runs rotate over the XCDs.  The launch is padded to whole rounds of 256.
+    const int w = blockIdx.x;
+    const int slot = w >> 3;
+    const int item = ((slot >> 5) * 8 + (w & 7)) * 32 + (slot & 31);
+    if (item >= a.items) return;
+    g = (item / a.row_tiles) % a.num_kv_heads;
+    r = item / a.row_tiles / a.num_kv_heads;
+    const int tile = a.row_tiles - 1 - item % a.row_tiles;  // the longest rows start first
+    // Offsets the plan cannot serve are not followed: nothing is read or written.
+    qs0 = a.q_starts[r];
+    const int qs1 = a.q_starts[r + 1];
+    nrows = qs1 - qs0;
+    if (qs0 < 0 || nrows < 0 || nrows > a.max_rows || qs1 > a.total_rows) return;
+    row0 = tile * QT;
+    if (row0 >= nrows) return;
+  }
   const int L = a.seq_lens[r];
   bool poison = L < nrows || int64_t(L) > int64_t(a.max_pages) * a.page_size;
+  // Decode windows: chunks partition the keys from the request's first row's window start
+  // (rounded down to a tile); they must cover the keys up to L.
+  int64_t origin = 0;
+  if constexpr (CHUNKED) {
+    const int first_hi = L - nrows + 1;
+    origin = (a.window > 0 ? max(0, first_hi - a.window) : 0) & ~(kKeys - 1);
+    poison = poison || int64_t(L) - origin > int64_t(a.num_chunks) * a.chunk_len;
+  }
 
   // This lane's column: row qrow of the request, query head `head`; it sees keys lo_c .. pos.
-  const int qrow = row0 + pair * RPP + n / G;
+  const int qrow = row0 + block * RPP + n / G;
   const bool active = qrow < nrows;
   const int head = g * G + n % G;
   const int pos = (active && !poison) ? L - nrows + qrow : -1;
   const int lo_c = a.window > 0 ? max(0, pos + 1 - a.window) : 0;
 
-  // Keys of the workgroup: the first row's window start .. the last row's position.
+  // Keys of the workgroup: the first row's window start .. the last row's position (and,
+  // for a decode window, inside the chunk).
   const int pos_first = L - nrows + row0;
   const int pos_last = L - nrows + min(row0 + QT, nrows) - 1;
   const int lo_first = a.window > 0 ? max(0, pos_first + 1 - a.window) : 0;
-  const int start = lo_first & ~(kKeys - 1);
-  int ntiles = poison ? 0 : (pos_last + 1 - start + kKeys - 1) / kKeys;
+  int start, ntiles;
+  if constexpr (CHUNKED) {
+    const int64_t c0 = origin + int64_t(chunk) * a.chunk_len;
+    const int64_t c1 = min(c0 + a.chunk_len, int64_t(pos_last) + 1);
+    start = int(min(c0, int64_t(L)));
+    ntiles = (poison || c1 <= c0) ? 0 : int((c1 - c0 + kKeys - 1) / kKeys);
+  } else {
+    start = lo_first & ~(kKeys - 1);
+    ntiles = poison ? 0 : (pos_last + 1 - start + kKeys - 1) / kKeys;
+  }
 
   const int32_t* trow = a.table + int64_t(r) * a.max_pages;
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
@@ -233,34 +295,87 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     off[k] = uint32_t(piece_col<D, FOLDED>(a, 4 * k + (S::TAIL != 0 && k == 1 ? 0 : lane >> 4))) +
              uint32_t((lane & 15) << 4);
 
-  // Request the first tile, then prepare the query operand while it streams.
-  if (ntiles > 0) {
-    const char* b = tile_base(start);
-    if (b) {
-      issue_tile<D, FOLDED>(a, b, buf0, wave, lane, off);
-    } else {
-      poison = true;
-      ntiles = 0;
+  // Decode windows stage tiles through registers, kStageSets ahead of the math: each wave
+  // loads its rows of a tile (the same 16-byte chunks per lane as the direct loads below)
+  // and copies them into the tile's LDS buffer when its turn comes.  With the whole tile in
+  // two 66 KB buffers, direct loads could keep only one tile in flight per CU.
+  // The loads are buffer loads over the tile's rows, issued on every step whether or not
+  // the tile is wanted: a tile past the end (or on a page outside the pool) gets an empty
+  // range, so its loads return zeros without touching memory.  Every step then issues
+  // the same loads, and the compiler's wait before a copy keeps the newer tile in flight.
+  constexpr int RW = S::ROWS_PER_WAVE;
+  constexpr int NS = kStageSets;  // register sets: tiles in flight ahead of the math
+  u32x4 stg[NS][RW][2];
+  auto fetch = [&](u32x4 (&st)[RW][2], int k0, bool want) -> bool {  // false: bad page
+    const char* b = want ? tile_base(k0) : nullptr;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(b ? b : a.pool), 0, b ? 0x7fffffff : 0, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t ro = uint32_t(i * S::WAVES + wave) * uint32_t(a.row_stride);
+#pragma unroll
+      for (int k = 0; k < S::FULL_KB; ++k)
+        st[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off[k], 0, kStreamLoad);
+      if constexpr (S::TAIL != 0)  // lanes 16.. ask past the range: zeros, no access
+        st[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane < 16 ? ro + off[1] : 0x80000000u,
+                                                        0, kStreamLoad);
     }
-  }
+    return b || !want;
+  };
+  auto stash = [&](const u32x4 (&st)[RW][2], char* lds) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      char* lb = lds + (i * S::WAVES + wave) * P + 16 * lane;
+#pragma unroll
+      for (int k = 0; k < S::FULL_KB; ++k) *reinterpret_cast<u32x4*>(lb + 1024 * k) = st[i][k];
+      if constexpr (S::TAIL != 0) {
+        if (lane < 16) *reinterpret_cast<u32x4*>(lb + 1024) = st[i][1];
+      }
+    }
+  };
+  // The first tiles (prefill: one, by direct loads) are requested before the query
+  // operand is prepared, so they stream meanwhile.
+  int count0 = ntiles;  // tiles whose pages were found (a missing page poisons the rest)
+  auto prologue = [&]() {
+    if constexpr (CHUNKED) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (!fetch(stg[u], start + u * kKeys, count0 > u)) count0 = min(count0, u);
+    } else {
+      if (count0 > 0) {
+        const char* b = tile_base(start);
+        if (b)
+          issue_tile<D, FOLDED>(a, b, buf0, wave, lane, off);
+        else
+          count0 = 0;
+      }
+    }
+    if (count0 < ntiles) poison = true;
+  };
+  if constexpr (!CHUNKED) prologue();
 
   // Query operand (B of the QK MFMA): lane (n, hh), step s holds dims
   // half * HALF + 16s + 8hh + [0, 8) of column n, as a high and a low bf16 part.
   bf16x8 qhi[S::KSTEPS], qlo[S::KSTEPS];
   {
+    // Inactive columns read row 0 (always present) and use zeros.
     const float* qp = a.q + (int64_t(qs0) + (active ? qrow : 0)) * a.num_q_heads * D +
                       int64_t(head) * D + half * HALF + 8 * hh;
+    floatx4 xq[S::KSTEPS][2];
+#pragma unroll
+    for (int s = 0; s < S::KSTEPS; ++s) {
+      xq[s][0] = *reinterpret_cast<const floatx4*>(qp + 16 * s);
+      xq[s][1] = *reinterpret_cast<const floatx4*>(qp + 16 * s + 4);
+    }
+    // Decode windows request their first tiles after the query loads, so that waiting
+    // for the query leaves the tiles in flight.
+    if constexpr (CHUNKED) prologue();
 #pragma unroll
     for (int s = 0; s < S::KSTEPS; ++s) {
       const float qs = (FOLDED && half * HALF + 16 * s >= S::ROT) ? a.qscale_v : a.qscale_k;
-      floatx4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-      if (active) {
-        x0 = *reinterpret_cast<const floatx4*>(qp + 16 * s);
-        x1 = *reinterpret_cast<const floatx4*>(qp + 16 * s + 4);
-      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = (e < 4 ? x0[e & 3] : x1[e & 3]) * qs;
+        const float x = active ? xq[s][e >> 2][e & 3] * qs : 0.0f;
         const __bf16 h = (__bf16)x;
         qhi[s][e] = h;
         qlo[s][e] = (__bf16)(x - (float)h);
@@ -281,10 +396,11 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int lo_last = a.window > 0 ? max(0, pos_last + 1 - a.window) : 0;
 
   float m_run, l_run;
+  float m_top;              // decode windows: the largest score seen (the state's final m)
   floatx16 acc[DPR];        // step jj: element r <-> dim half*HALF + DPR*(8(r/4) + 4hh + r%4) + jj
   bool overflow = false;    // a score exceeded the reference by more than kHeadroom
 
-  // One staged tile (keys k0 .. k0 + 31) for this wave's half of its pair's 32 columns.
+  // One staged tile (keys k0 .. k0 + 31) for this wave's dims of its block's 32 columns.
   auto compute = [&](const char* t, int k0, auto rescale) {
     constexpr bool RESCALE = decltype(rescale)::value;
     // Partial scores over this wave's dims; the K fragments of step s + 1 are read while
@@ -310,7 +426,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     }
     sp += sq;
     float sc[16];
-    if constexpr (S::PAIR == 2) {
+    if constexpr (SPLIT == 2) {
       // Add the pair's two halves in a fixed order (half 0 first): identical in both waves.
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -322,6 +438,22 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sc[4 * e4 + i] = half == 0 ? sp[4 * e4 + i] + other[i] : other[i] + sp[4 * e4 + i];
+      }
+    } else if constexpr (SPLIT == 4) {
+      // Add the four quarters as (q0 + q1) + (q2 + q3), all read back from LDS: every wave
+      // of the block evaluates the same expression and holds the same scores bit for bit.
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[wave][e][lane] = floatx4{sp[4 * e], sp[4 * e + 1], sp[4 * e + 2], sp[4 * e + 3]};
+      __syncthreads();
+      const int w0 = block * SPLIT;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const floatx4 x0 = xs[w0][e4][lane], x1 = xs[w0 + 1][e4][lane];
+        const floatx4 x2 = xs[w0 + 2][e4][lane], x3 = xs[w0 + 3][e4][lane];
+        const floatx4 y = (x0 + x1) + (x2 + x3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = y[i];
       }
     } else {
 #pragma unroll
@@ -340,6 +472,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
     mx = fmaxf(mx, shfl_xor(mx, 32));
+    if constexpr (CHUNKED) m_top = fmaxf(m_top, mx);
     if constexpr (RESCALE) {
       const bool grow = mx > m_run + kRescaleSlack;
       if (__builtin_expect(__any(grow), 0)) {
@@ -417,33 +550,61 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // All tiles of the workgroup, double-buffered: wait for this tile's loads (own, then
-  // everyone's via the barrier, which also frees the other buffer and the score slots),
-  // request the next tile into the other buffer, use this one.
+  // All tiles of the work item through the two LDS buffers.
   auto run = [&](auto rescale) {
     m_run = -INFINITY;
+    m_top = -INFINITY;
     l_run = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < DPR; ++jj) acc[jj] = floatx16{};
-    int count = ntiles;
-    auto step = [&](const char* cur, char* nxt, int it) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      const int k0 = start + it * kKeys;
-      if (it + 1 < count) {
-        const char* b = tile_base(k0 + kKeys);
-        if (b) {
-          issue_tile<D, FOLDED>(a, b, nxt, wave, lane, off);
-        } else {
+    int count = count0;
+    if constexpr (CHUNKED) {
+      // Tile it sits in registers (fetched two steps earlier): copy it into its buffer
+      // (free: every wave passed the last barrier after using it two tiles ago), refill
+      // the registers with tile it + 2, wait for all waves' copies, use the buffer.
+      auto step = [&](u32x4 (&st)[RW][2], int it) {
+        char* cur = (it & 1) ? buf1 : buf0;
+        stash(st, cur);
+        if (!fetch(st, start + (it + NS) * kKeys, it + NS < count)) {
           poison = true;
-          count = it + 1;
+          count = it + NS;
         }
+        __syncthreads();
+        compute(cur, start + it * kKeys, rescale);
+      };
+      // Whole rounds in the loop (every pass refills all register sets, in order), the
+      // last tiles after it.
+      int it = 0;
+      for (; it + NS - 1 < count; it += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) step(stg[u], it + u);
       }
-      compute(cur, k0, rescale);
-    };
-    for (int it = 0; it < count; it += 2) {
-      step(buf0, buf1, it);
-      if (it + 1 < count) step(buf1, buf0, it + 1);
+#pragma unroll
+      for (int u = 0; u < NS - 1; ++u)
+        if (it + u < count) step(stg[u], it + u);
+    } else {
+      // Wait for this tile's loads (own, then everyone's via the barrier, which also frees
+      // the other buffer and the score slots), request the next tile into the other
+      // buffer, use this one.
+      auto step = [&](const char* cur, char* nxt, int it) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int k0 = start + it * kKeys;
+        if (it + 1 < count) {
+          const char* b = tile_base(k0 + kKeys);
+          if (b) {
+            issue_tile<D, FOLDED>(a, b, nxt, wave, lane, off);
+          } else {
+            poison = true;
+            count = it + 1;
+          }
+        }
+        compute(cur, k0, rescale);
+      };
+      for (int it = 0; it < count; it += 2) {
+        step(buf0, buf1, it);
+        if (it + 1 < count) step(buf1, buf0, it + 1);
+      }
     }
   };
   run(Flag<false>{});
@@ -457,29 +618,80 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   for (int w = 0; w < W; ++w) any_overflow |= xs[w][0][0][0] != 0.0f;
   if (any_overflow) {  // uniform: every wave of the workgroup takes it
     __syncthreads();   // the flags have been read
-    if (ntiles > 0) issue_tile<D, FOLDED>(a, tile_base(start), buf0, wave, lane, off);
+    count0 = ntiles;
+    prologue();
     run(Flag<true>{});
   }
 
   if (!active) return;
+  if constexpr (CHUNKED) {
+    // State relative to the chunk's largest score (the reference may lie below it).
+    if (m_top > m_run) {
+      const float al = __builtin_amdgcn_exp2f(m_run - m_top);
+      l_run *= al;
+#pragma unroll
+      for (int jj = 0; jj < DPR; ++jj) acc[jj] *= al;
+      m_run = m_top;
+    }
+  }
   l_run += shfl_xor(l_run, 32);
-  float* o = a.out + (int64_t(qs0) + qrow) * a.num_q_heads * D + int64_t(head) * D + half * HALF;
   const float qnan = __builtin_nanf("");
+  // Prefill: O / l into the row.  Decode window: the chunk state; an empty one is
+  // (-inf, 0, 0), a poisoned one NaN.
+  float* o;
+  float f;
+  if constexpr (CHUNKED) {
+    const int64_t st = ((int64_t(qs0) + qrow) * a.num_q_heads + head) * a.num_chunks + chunk;
+    if (half == 0 && hh == 0) {
+      a.part_m[st] = poison ? qnan : (m_run == -INFINITY ? -INFINITY : m_run * kLn2);
+      a.part_l[st] = poison ? qnan : l_run;
+    }
+    o = a.part_o + st * D + half * HALF;
+    f = a.vscale;
+  } else {
+    o = a.out + (int64_t(qs0) + qrow) * a.num_q_heads * D + int64_t(head) * D + half * HALF;
+    f = a.vscale / l_run;
+  }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int mrow = 8 * (e >> 2) + 4 * hh + (e & 3);
     float v[DPR];
 #pragma unroll
-    for (int jj = 0; jj < DPR; ++jj) v[jj] = poison ? qnan : acc[jj][e] * a.vscale / l_run;
+    for (int jj = 0; jj < DPR; ++jj) v[jj] = poison ? qnan : acc[jj][e] * f;
     float* dst = o + DPR * mrow;
     *reinterpret_cast<floatx4*>(dst) = floatx4{v[0], v[1], v[2], v[3]};
     if constexpr (DPR == 8) *reinterpret_cast<floatx4*>(dst + 4) = floatx4{v[4], v[5], v[6], v[7]};
   }
 }
 
-template <int D, int G, bool FOLDED>
-void launch_prefill(const PrefillArgs& args, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, G, FOLDED>), grid, dim3(256), 0, s, args);
+template <int D, int G, bool FOLDED, bool CHUNKED>
+void launch_rows_tile(const PrefillArgs& args, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED>), grid, dim3(256), 0, s, args);
+}
+
+// Pool geometry and query scaling shared by both uses.
+void fill_common(PrefillArgs& args, const attn_decode_desc& d, const float* q,
+                 const void* kv_pool, const int32_t* page_table, const int32_t* seq_lens) {
+  const int64_t eb = kv_elem_bytes(d.kv_dtype);
+  args = PrefillArgs{};
+  args.q = q;
+  args.pool = static_cast<const char*>(kv_pool);
+  args.table = page_table;
+  args.seq_lens = seq_lens;
+  args.page_stride = d.page_stride * eb;
+  args.head_stride = d.head_stride * eb;
+  args.row_stride = d.row_stride * eb;
+  args.k_offset = d.k_offset * eb;
+  args.v_offset = d.v_offset * eb;
+  args.num_pages = d.num_pages;
+  args.num_q_heads = d.num_q_heads;
+  args.num_kv_heads = d.num_kv_heads;
+  args.page_size = d.page_size;
+  args.max_pages = d.max_pages_per_seq;
+  args.window = d.window;
+  args.qscale_k = d.scale * kLog2e * d.k_scale;
+  args.qscale_v = d.scale * kLog2e * d.v_scale;
+  args.vscale = d.v_scale;
 }
 
 }  // namespace
@@ -496,41 +708,48 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
   if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
   if (plan->total_rows == 0) return ATTN_OK;
 
-  const int64_t eb = kv_elem_bytes(d.kv_dtype);
   PrefillArgs args;
-  args.q = q;
+  fill_common(args, d, q, kv_pool, page_table, seq_lens);
   args.out = out;
-  args.pool = static_cast<const char*>(kv_pool);
-  args.table = page_table;
-  args.seq_lens = seq_lens;
   args.q_starts = q_starts;
-  args.page_stride = d.page_stride * eb;
-  args.head_stride = d.head_stride * eb;
-  args.row_stride = d.row_stride * eb;
-  args.k_offset = d.k_offset * eb;
-  args.v_offset = d.v_offset * eb;
-  args.num_pages = d.num_pages;
-  args.num_q_heads = d.num_q_heads;
-  args.page_size = d.page_size;
-  args.max_pages = d.max_pages_per_seq;
-  args.window = d.window;
   args.total_rows = plan->total_rows;
   args.max_rows = plan->max_rows;
   args.row_tiles = plan->grid_x;
-  args.num_kv_heads = d.num_kv_heads;
   args.items = plan->grid_x * d.num_kv_heads * d.batch;  // bounded by the plan
-  args.qscale_k = d.scale * kLog2e * d.k_scale;
-  args.qscale_v = d.scale * kLog2e * d.v_scale;
-  args.vscale = d.v_scale;
 
   const dim3 grid((args.items + 255) / 256 * 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
-    launch_prefill<512, 8, false>(args, grid, s);
+    launch_rows_tile<512, 8, false, false>(args, grid, s);
   else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
-    launch_prefill<512, 8, true>(args, grid, s);
+    launch_rows_tile<512, 8, true, false>(args, grid, s);
   else
-    launch_prefill<256, 2, false>(args, grid, s);
+    launch_rows_tile<256, 2, false, false>(args, grid, s);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
+
+namespace attn {
+
+void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* kv_pool,
+                       const int32_t* page_table, const int32_t* seq_lens, float* part_m,
+                       float* part_l, float* part_o, void* stream) {
+  const attn_decode_desc& d = p.desc;
+  PrefillArgs args;
+  fill_common(args, d, q, kv_pool, page_table, seq_lens);
+  args.part_m = part_m;
+  args.part_l = part_l;
+  args.part_o = part_o;
+  args.chunk_len = p.chunk_len;
+  args.num_chunks = p.num_chunks;
+  args.num_rows = p.num_rows;
+  args.row_groups = p.row_groups;
+  const dim3 grid(p.grid_x, d.num_kv_heads, d.batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.format == ATTN_KV_FOLDED)
+    launch_rows_tile<512, 8, true, true>(args, grid, s);
+  else
+    launch_rows_tile<512, 8, false, true>(args, grid, s);
+}
+
+}  // namespace attn

@@ -277,6 +277,29 @@ def test_rows_plan():
     assert rc == S["ATTN_E_INVALID_ARG"]
 
 
+def test_rows_plan_tile_choice():
+    """Several rows at head dim 512 over bf16 pages of whole 32-key tiles: 32-key tiles
+    (chunk starts and lengths in whole tiles); one row, other element types or pages of
+    16 keep 16-key tiles."""
+    for fmt, rot, v_off, cols in ((0, 0, 512, 1024), (1, 128, 128, 640)):
+        f = global_desc(163336, num_rows=4, format=fmt, rot_cols=rot, v_offset=v_off,
+                        row_stride=cols, head_stride=256 * cols, page_stride=4 * 256 * cols)
+        rc, p = plan_status([163336], **f)
+        assert rc == 0 and p.tile == 32 and p.chunk_len % 32 == 0
+        assert p.num_chunks * p.chunk_len >= 163336 and p.grid_x == p.num_chunks
+    # a window: chunks start at the first row's window start rounded down to 32
+    rc, p = plan_status([5000], **global_desc(5000, num_rows=3, window=1024, num_chunks=3))
+    assert rc == 0 and p.tile == 32 and p.max_span == 5000 - (5000 - 3 + 1 - 1024) // 32 * 32
+    rc, p = plan_status([1000], **global_desc(1024, num_rows=1))
+    assert rc == 0 and p.tile == 16
+    rc, p = plan_status([1000], **global_desc(1024, num_rows=4, kv_dtype=1))
+    assert rc == 0 and p.tile == 16
+    rc, p = plan_status([1000], **global_desc(1024, num_rows=4, page_size=16,
+                                              max_pages_per_seq=64, page_stride=4 * 16 * 1024,
+                                              head_stride=16 * 1024, num_pages=70))
+    assert rc == 0 and p.tile == 16
+
+
 
 # ---------------------------------------------------------------------------- prefill plan
 
