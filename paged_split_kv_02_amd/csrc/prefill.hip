@@ -1,5 +1,7 @@
-// Paged prefill for gfx950 (MI355X): prompt rows attending causally to their request's
-// keys through the page table, the normalised output written directly.
+// Rows on 32-key MFMA tiles for gfx950 (MI355X): paged prefill (prompt rows attending
+// causally to their request's keys through the page table, the normalised output written
+// directly), and, in a chunked mode, decode windows of several rows at head dim 512 (each
+// workgroup one key chunk of four rows, writing chunk states for the decode merge).
 //
 // pegainfer PR #1055 ("Description") runs the global family's prompt rows through a
 // prefill over the split or folded pool; pegainfer PR #1057 ("Description") runs the
@@ -12,20 +14,21 @@
 // waves.  A column block of 32 MFMA columns = (32 / G) rows x the G query heads of the KV
 // head belongs to a pair of waves at head dim 512, which split the head dimension (256
 // dims each: each holds half of the columns' query operand and half of their output), and
-// to a single wave at head dim 256.  Per 32-key tile (whole tiles inside one page: the
+// to a single wave at head dim 256 (decode windows: to all four waves, 128 dims each).  Per 32-key tile (whole tiles inside one page: the
 // page id is read once per tile):
 //   * the tile's stored rows are copied from the pool straight into LDS with 16-byte
 //     global->LDS loads (no registers involved), one kilobyte of one row per
 //     instruction; the next tile is requested as soon as its buffer is free, so it lands
-//     while the current one is used.  Staged rows are 16 bytes apart beyond their length,
+//     while the current one is used (decode windows stage through registers instead,
+//     two tiles ahead).  Staged rows are 16 bytes apart beyond their length,
 //     which keeps every LDS read pattern below free of bank conflicts and lets every
 //     read address be a per-lane base plus a constant;
 //   * each wave forms S^T = K Q^T over its dims on the 32x32x16 MFMA (keys as rows, (row,
 //     head) as columns), K fragments read three steps ahead; the fp32 query, with
 //     scale * log2(e) folded in, enters as a high and a low bf16 part, both multiplied
-//     against each K fragment, so the scores keep ~16 mantissa bits.  At head dim 512 the
-//     pair's two halves are added through LDS in a fixed order, so both waves of the pair
-//     hold the same scores bit for bit;
+//     against each K fragment, so the scores keep ~16 mantissa bits.  Where waves split
+//     the dims, their partial scores are added through LDS in a fixed order, so all waves
+//     of a block hold the same scores bit for bit;
 //   * causal and window masks by select (skipped on interior tiles); online softmax in
 //     base 2;
 //   * O^T += V^T P^T on the same MFMA for the wave's dims, the probabilities
