@@ -120,9 +120,9 @@ struct Elem<ATTN_KV_F16> : Elem<ATTN_KV_BF16> {
   static constexpr bool kF16 = true;  // operand type: f16
 };
 
-// FP8 E4M3 (OCP): v_cvt_pk_f32_fp8 widens two codes to f32 exactly (every code,
-// NaN and subnormals included); an E4M3 value has 3 mantissa bits, so the upper half
-// of its f32 pattern is the same value in bf16, and one byte permute packs two.
+// FP8 E4M3 (OCP): every E4M3 value (subnormals included) is exactly a bf16 value, and
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes straight to a
+// packed bf16 pair.
 template <>
 struct Elem<ATTN_KV_FP8_E4M3> {
   static constexpr int kBytes = 1;
@@ -136,12 +136,10 @@ struct Elem<ATTN_KV_FP8_E4M3> {
     u32x4 out;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const floatx2 a = __builtin_amdgcn_cvt_pk_f32_fp8(int(r[i]), false);  // bytes 0, 1
-      const floatx2 b = __builtin_amdgcn_cvt_pk_f32_fp8(int(r[i]), true);   // bytes 2, 3
-      // (__float_as_uint, not __builtin_bit_cast: on a vector element subscript this
-      // hipcc bit-casts element 0 whatever the index.)
-      out[2 * i] = perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-      out[2 * i + 1] = perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+      out[2 * i] = __builtin_bit_cast(                                       // bytes 0, 1
+          unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[i], 1.0f, false));
+      out[2 * i + 1] = __builtin_bit_cast(                                   // bytes 2, 3
+          unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[i], 1.0f, true));
     }
     return out;
   }

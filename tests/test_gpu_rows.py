@@ -31,6 +31,18 @@ def test_rows_sliding_window(rows):
     check(got, oracle.decode_attention(wl), f"sliding rows={rows}")
 
 
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_rows_global_with_window(fmt):
+    """Head dim 512 with a window (the 32-key tile kernel): every row's window starts at a
+    different key, chunks start at the first row's window start rounded to a tile, and
+    windows cross chunk and tile boundaries; plus a request shorter than the window."""
+    wl = synth.make_workload([3000, 1400, 300], **dict(synth.GLOBAL, window=700), fmt=fmt,
+                             seed=63, num_rows=6, pad="nan")
+    dev, got = run_case(wl, f"rows=6 window=700 {fmt}", num_chunks=7)
+    assert dev.plan.tile == 32
+    check(got, oracle.decode_attention(wl), f"rows=6 window {fmt}")
+
+
 def test_rows_minimal_lengths_and_explicit_chunks():
     """L == rows (the first row sees one key: exactly v_0), and more chunks than tiles."""
     wl = synth.make_workload([4, 4], **synth.GLOBAL, seed=60, num_rows=4, pad="big")
