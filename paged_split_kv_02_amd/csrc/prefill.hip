@@ -435,13 +435,14 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e)
         xs[wave][e][lane] = floatx4{sp[4 * e], sp[4 * e + 1], sp[4 * e + 2], sp[4 * e + 3]};
       __syncthreads();
+      floatx4 other[4];  // all reads issued before the first add
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const floatx4 other = xs[wave ^ 1][e4][lane];
+      for (int e4 = 0; e4 < 4; ++e4) other[e4] = xs[wave ^ 1][e4][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[4 * e4 + i] = half == 0 ? sp[4 * e4 + i] + other[i] : other[i] + sp[4 * e4 + i];
-      }
+      for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)  // (IEEE addition commutes: the same sum in both waves)
+          sc[4 * e4 + i] = sp[4 * e4 + i] + other[e4][i];
     } else if constexpr (SPLIT == 4) {
       // Add the four quarters as (q0 + q1) + (q2 + q3), all read back from LDS: every wave
       // of the block evaluates the same expression and holds the same scores bit for bit.
@@ -450,11 +451,14 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
         xs[wave][e][lane] = floatx4{sp[4 * e], sp[4 * e + 1], sp[4 * e + 2], sp[4 * e + 3]};
       __syncthreads();
       const int w0 = block * SPLIT;
+      floatx4 x[4][4];  // all reads issued before the first add
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u][e4] = xs[w0 + u][e4][lane];
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const floatx4 x0 = xs[w0][e4][lane], x1 = xs[w0 + 1][e4][lane];
-        const floatx4 x2 = xs[w0 + 2][e4][lane], x3 = xs[w0 + 3][e4][lane];
-        const floatx4 y = (x0 + x1) + (x2 + x3);
+        const floatx4 y = (x[0][e4] + x[1][e4]) + (x[2][e4] + x[3][e4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = y[i];
       }
@@ -493,11 +497,14 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
       overflow |= mx > m_run + kHeadroom;
     }
     // Probabilities as the PV B operands: MFMA t takes elements 8t .. 8t + 7.
+    // A reference still unset means every score of the column so far is -inf: any finite
+    // stand-in gives the zero probabilities.
     bf16x8 phi[2], plo[2];
     float psum = 0.0f;
+    const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[e] - m_run);
+      const float p = __builtin_amdgcn_exp2f(sc[e] - m_ref);
       psum += p;
       const __bf16 h = (__bf16)p;
       phi[e >> 3][e & 7] = h;
