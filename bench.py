@@ -321,6 +321,9 @@ def main():
         def wanted(name):
             return not pick or any(x in name for x in pick)
         for name, maker, n_steps in (
+                ("global-decode-10602-split", lambda: synth.global_decode(10602, seed=13), 20),
+                ("global-decode-40002-split", lambda: synth.global_decode(40002, seed=14), 20),
+                ("global-decode-81653-split", lambda: synth.global_decode(81653, seed=15), 20),
                 ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
                 ("global-decode-163336-split-4rows",
@@ -346,8 +349,11 @@ def main():
             variants[name] = {"us_per_step": round(vms * 1e3, 2), "query_rows": vwl.num_rows,
                               "kv_dtype": vwl.kv_dtype,
                               "partial_kernel_us": round(vsplit * 1e3, 2),
+                              "merge_us": round((vms - vsplit) * 1e3, 2),
                               "kv_bytes": vwl.kv_bytes(),
                               "effective_gbs": round(vwl.kv_bytes() / (vms * 1e-3) / 1e9, 1),
+                              "pct_hbm_peak": round(100 * vwl.kv_bytes() / (vms * 1e-3) / 1e9
+                                                    / HBM_PEAK_GBS, 2),
                               "partial_kernel_gbs": round(vres.kernel_bytes() / (vsplit * 1e-3) / 1e9, 1),
                               "num_chunks": vres.plan.num_chunks, "timing": "median, cache flushed"}
             print(f"# {name}: {vms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
