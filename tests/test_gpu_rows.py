@@ -43,6 +43,33 @@ def test_rows_global_with_window(fmt):
     check(got, oracle.decode_attention(wl), f"rows=6 window {fmt}")
 
 
+@pytest.mark.parametrize("shape", ["split", "folded", "sliding"])
+def test_rows_bad_page_and_device_lengths(shape):
+    """Forced from the host (every kernel exits normally): a table entry outside the pool,
+    a device length below the row count, and one at the table's capacity (past the plan's
+    chunks, or onto empty table entries) each turn only that request's rows into NaN; the
+    other request matches the oracle.  Head dim 512 runs the 32-key tile kernel, 256 the
+    16-key rows kernel."""
+    if shape == "sliding":
+        wl = synth.make_workload([1300, 900], **synth.SLIDING, seed=64, num_rows=4, max_pages=40)
+    else:
+        wl = synth.make_workload([1300, 900], **synth.GLOBAL, fmt=shape, seed=64, num_rows=4)
+    ref0 = oracle.decode_attention(wl)[:1]
+    good = int(wl.table[1][1])
+    wl.table[1][1] = wl.num_pages + 100
+    _, got = run_case(wl, f"{shape} rows=4 bad page id")
+    assert np.all(np.isnan(got[1]))
+    check(got[:1], ref0, f"{shape} healthy request beside a bad page")
+    wl.table[1][1] = good
+    for lens in ([1300, 3], [1300, wl.max_pages * wl.page_size]):
+        note(f"[gpu] {shape} rows=4 device lengths {lens}")
+        dev = Device(wl, seq_lens_dev=lens)
+        got = dev.run()
+        assert dev.guards_intact()
+        assert np.all(np.isnan(got[1])), lens
+        check(got[:1], ref0, f"{shape} request 0 beside device lengths {lens}")
+
+
 def test_rows_minimal_lengths_and_explicit_chunks():
     """L == rows (the first row sees one key: exactly v_0), and more chunks than tiles."""
     wl = synth.make_workload([4, 4], **synth.GLOBAL, seed=60, num_rows=4, pad="big")
