@@ -25,6 +25,8 @@
  * workspace, output).  The library allocates nothing, keeps no mutable global
  * state and is reentrant.  Launches are asynchronous; buffers must stay alive
  * until the stream has run them.  A plan is plain old data and may be copied.
+ * The enqueuing calls neither synchronise nor allocate nor record memsets, and a
+ * plan fixes their grids, so they can be captured into a HIP graph and replayed.
  *
  * Errors: every check runs before any launch, so a refused call enqueues
  * nothing.  Kernels write only the plan's workspace extent and `out`.
