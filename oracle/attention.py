@@ -194,22 +194,45 @@ def dense_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -
     return (e @ V) / z
 
 
+def window_row_positions(L: int, n: int, i: int, window: int, mask: int | None) -> np.ndarray:
+    """Key positions row i of an n-row window over L keys attends to, ascending.
+
+    Causal (mask None): the positions before L - n + i + 1, and with a sliding window
+    not older than W keys back from there.  Tree attention (TensorFold PR #1619 names
+    the paged tree-attention decode kernels of its drafted verify windows, body and
+    review thread; the mask is our reading): the same keys before the window, L - n,
+    and of the window's own keys L - n + j those whose bit j is set in the row's mask,
+    again not older than the window's lower bound.  Causal is the mask of bits 0 .. i.
+    """
+    lo, hi = visible_range(L - n + 1 + i, window)
+    if mask is None:
+        return np.arange(lo, hi)
+    start = L - n
+    own = [start + j for j in range(n) if (mask >> j) & 1 and start + j >= lo]
+    return np.concatenate([np.arange(lo, start), np.array(own, dtype=np.int64)]).astype(np.int64)
+
+
 def decode_attention(wl) -> np.ndarray:
     """fp64 output of one decode step over the paged pool: [B][Hq][D], or
     [B][rows][Hq][D] when the workload has a window of several query rows.
 
     Query row i of a window of n rows sits at position L - n + i and attends causally:
     to the keys at positions before L - n + i + 1 (and, with a sliding window, not older
-    than W keys back from there).  One row is ordinary decode.
+    than W keys back from there), or, given tree masks, as `window_row_positions`
+    describes.  One row is ordinary decode.  A row that sees no key gets NaN (0 / 0).
     """
     G = wl.num_q_heads // wl.num_kv_heads
     n = getattr(wl, "num_rows", 1)
+    masks = getattr(wl, "row_masks", None)
     q = wl.q if n > 1 else wl.q[:, None]
     out = np.empty((wl.batch, n, wl.num_q_heads, wl.head_dim), dtype=np.float64)
     for r in range(wl.batch):
         for i in range(n):
-            lo, L = visible_range(int(wl.seq_lens[r]) - n + 1 + i, wl.window)
-            pos = np.arange(lo, L)
+            mask = None if masks is None else int(masks[r][i])
+            pos = window_row_positions(int(wl.seq_lens[r]), n, i, wl.window, mask)
+            if pos.size == 0:
+                out[r, i] = np.nan
+                continue
             for g in range(wl.num_kv_heads):
                 K, V = keys_values(wl, _stored_rows(wl, r, g, pos))
                 heads = slice(g * G, (g + 1) * G)

@@ -98,6 +98,11 @@ class Workload:
     kv_dtype: str = BF16     # element type of the pool
     k_scale: float = 1.0     # K = stored value * k_scale
     v_scale: float = 1.0     # V = stored value * v_scale
+    # Tree attention over a window of several rows: parent window row of each row (-1:
+    # hangs directly off the keys before the window) and its encoding as the kernels
+    # take it, bit j of row_masks[r][i] set when row i sees window row j.
+    tree_parents: Optional[np.ndarray] = None   # int32 [B][rows]
+    row_masks: Optional[np.ndarray] = None      # uint64 [B][rows]
 
     @property
     def group_size(self) -> int:
@@ -387,3 +392,43 @@ def sliding_batch(seed: int = 4, batch: int = 16, max_len: int = 4096, **kw) -> 
     lens = (torch.randint(1, max_len + 1, (batch,), generator=g)).tolist()
     kw.setdefault("max_pages", max_len // SLIDING["page_size"])
     return make_workload(lens, **SLIDING, seed=seed, **kw)
+
+
+def tree_masks(parents: np.ndarray) -> np.ndarray:
+    """uint64 [B][rows] masks of a forest of window rows given by parent indices
+    (parents[r][i] < i, or -1): bit j of row i is set when j is i or one of its
+    ancestors.  Rows are at most 64."""
+    parents = np.asarray(parents, dtype=np.int64)
+    B, n = parents.shape
+    if n > 64:
+        raise ValueError("at most 64 window rows")
+    masks = np.zeros((B, n), dtype=np.uint64)
+    for r in range(B):
+        for i in range(n):
+            p = int(parents[r, i])
+            if not -1 <= p < i:
+                raise ValueError("a parent must be an earlier row or -1")
+            masks[r, i] = np.uint64(1 << i) | (masks[r, p] if p >= 0 else np.uint64(0))
+    return masks
+
+
+def random_parents(batch: int, rows: int, seed: int) -> np.ndarray:
+    """Seeded random forests: row 0 hangs off the prefix, row i > 0 off a uniformly
+    drawn earlier row (or, one time in eight, off the prefix as a new root)."""
+    rng = np.random.default_rng(seed)
+    parents = np.full((batch, rows), -1, dtype=np.int32)
+    for r in range(batch):
+        for i in range(1, rows):
+            parents[r, i] = -1 if rng.random() < 0.125 else int(rng.integers(0, i))
+    return parents
+
+
+def set_tree(wl: Workload, parents: np.ndarray) -> Workload:
+    """Attach a tree (parent indices per request) and its masks to a multi-row workload."""
+    parents = np.asarray(parents, dtype=np.int32)
+    if parents.shape != (wl.batch, wl.num_rows):
+        raise ValueError("parents must be [batch][rows]")
+    wl.tree_parents = parents
+    wl.row_masks = tree_masks(parents)
+    return wl
+

@@ -595,10 +595,77 @@ def pin_prefill_causality():
     assert not np.array_equal(moved[p + 1:], base[p + 1:])
 
 
+def brute_force_tree(wl) -> np.ndarray:
+    """Tree attention by brute force: window row i sees the keys before the window that
+    a causal row i sees, and the window rows on its path to the root, found by walking
+    the parent indices (never the masks); pure-Python scores and sums."""
+    D, G, n = wl.head_dim, wl.num_q_heads // wl.num_kv_heads, wl.num_rows
+    out = np.zeros((wl.batch, n, wl.num_q_heads, D))
+    elem = _ELEMENT[wl.kv_dtype]
+    for r in range(wl.batch):
+        L = int(wl.seq_lens[r])
+        for i in range(n):
+            path, j = set(), i
+            while j >= 0:
+                path.add(j)
+                j = int(wl.tree_parents[r][j])
+            here = L - n + i + 1                   # a causal row i's length
+            lo = here - wl.window if (wl.window and here > wl.window) else 0
+            positions = [t for t in range(lo, L) if t < L - n or (t - (L - n)) in path]
+            for g in range(wl.num_kv_heads):
+                keys, vals = [], []
+                for t in positions:
+                    pg = int(wl.table[r][t // wl.page_size])
+                    base = pg * wl.page_stride + g * wl.head_stride + (t % wl.page_size) * wl.row_stride
+                    row = [elem(wl.pool[base + c]) for c in range(wl.row_cols)]
+                    v = row[wl.v_offset:wl.v_offset + D]
+                    k = (row[wl.k_offset:wl.k_offset + D] if wl.fmt == "split" else
+                         row[wl.k_offset:wl.k_offset + wl.rot_cols] + v[wl.rot_cols:])
+                    keys.append(k)
+                    vals.append(v)
+                for h in range(g * G, (g + 1) * G):
+                    qh = [float(x) for x in wl.q[r, i, h]]
+                    w = [math.exp(wl.scale * math.fsum(qh[d] * k[d] for d in range(D))) for k in keys]
+                    z = math.fsum(w)
+                    out[r, i, h] = [math.fsum(w[t] * vals[t][d] for t in range(len(keys))) / z
+                                    for d in range(D)]
+    return out
+
+
+def pin_tree_brute_force():
+    """Tree attention on random forests (whole context and a window, split and folded)
+    against the parent-walking brute force; a chain of rows is the causal window bit for
+    bit; a row whose mask shows no key (no keys before the window) is NaN, the others
+    unaffected."""
+    for W, fmt, seed in ((0, "split", 40), (5, "split", 41), (0, "folded", 42)):
+        D = 17 if fmt == "split" else 512
+        wl = synth.make_workload([11, 7, 9], num_q_heads=4, num_kv_heads=2, head_dim=D,
+                                 page_size=4, window=W, fmt=fmt, seed=seed, num_rows=6,
+                                 pad="big", spare_pages=2)
+        synth.set_tree(wl, synth.random_parents(3, 6, seed))
+        _assert_close(oracle.decode_attention(wl), brute_force_tree(wl), 1e-13,
+                      f"tree W={W} {fmt}")
+    wl = synth.make_workload([40, 33], num_q_heads=8, num_kv_heads=1, head_dim=64, page_size=8,
+                             seed=43, num_rows=5)
+    causal = oracle.decode_attention(wl)
+    synth.set_tree(wl, np.tile(np.arange(-1, 4), (2, 1)))
+    assert np.array_equal(oracle.decode_attention(wl), causal)
+    wl = synth.make_workload([4], num_q_heads=2, num_kv_heads=1, head_dim=8, page_size=4,
+                             seed=44, num_rows=4)
+    synth.set_tree(wl, np.array([[-1, 0, 0, 1]]))
+    masks = wl.row_masks.copy()
+    wl.row_masks[0, 2] = np.uint64(0)
+    got = oracle.decode_attention(wl)
+    assert np.all(np.isnan(got[0, 2]))
+    wl.row_masks = masks
+    ref = oracle.decode_attention(wl)
+    assert np.array_equal(np.delete(got, 2, axis=1), np.delete(ref, 2, axis=1))
+
+
 ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, pin_needle,
             pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
             pin_empty_merge_identity, pin_merge_identity_values, pin_window,
             pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed,
             pin_query_rows, pin_dtype_brute_force, pin_e4m3_codes, pin_f16_f32_codes,
             pin_dequant_factors, pin_prefill_brute_force, pin_prefill_rows_are_decode,
-            pin_prefill_causality]
+            pin_prefill_causality, pin_tree_brute_force]

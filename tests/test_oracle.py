@@ -172,6 +172,16 @@ def _prefill_excludes_own_key(wl, rows=None):
             out[k, hs] = OA.dense_attention(wl.q[t, hs], K, V, wl.scale)
     return out
 
+def _tree_masks_read_by_index(L, n, i, window, mask):
+    # reads the mask as "the first popcount(mask) rows" instead of the rows it names
+    if mask is not None:
+        mask = (1 << bin(mask).count("1")) - 1
+    return _window_row_positions(L, n, i, window, mask)
+
+
+_window_row_positions = OA.window_row_positions
+
+
 MUTANTS = {
     "rows_see_one_key_too_many": ("decode_attention", _rows_off_by_one),
     "k_v_swapped": ("keys_values", _kv_swapped),
@@ -190,6 +200,7 @@ MUTANTS = {
     "e4m3_subnormal_as_normal": ("e4m3_bits_to_f64", _e4m3_subnormal_as_normal),
     "prefill_rows_from_zero": ("prefill_row_index", _prefill_rows_from_zero),
     "prefill_excludes_own_key": ("prefill_attention", _prefill_excludes_own_key),
+    "tree_masks_read_by_index": ("window_row_positions", _tree_masks_read_by_index),
 }
 
 
