@@ -16,6 +16,7 @@
  *                      chooses the chunking and lays out the workspace.
  *   attn_decode_split  enqueues the partial kernel on a HIP stream.
  *   attn_decode_merge  enqueues the merge (level 1, level 2, O / S) on a stream.
+ *   attn_decode_split_tree  the split step for a window of rows forming a tree.
  * Around the step: attn_kv_write stores new tokens' K/V rows into the pages,
  * attn_query_fold folds K's norm weight into the query for a folded pool, and
  * attn_prefill_plan / attn_prefill run a request's prompt rows (causal, several rows
@@ -207,6 +208,25 @@ int attn_decode_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
 int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
                       const int32_t* page_table, const int32_t* seq_lens, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_split for a window of several query rows whose rows form a tree
+ * (speculative decoding's tree attention; TensorFold PR #1619, body and review thread,
+ * names paged tree-attention decode kernels for its drafted verify windows, without
+ * fixing a mask).  Row i of request r sees the keys before the window, L_r - num_rows,
+ * that a causal row i sees, and of the window's own keys the key of row j exactly when
+ * bit j of row_masks[r * num_rows + i] is set (a tree: row i and its ancestors; causal
+ * rows are the masks 2^(i+1) - 1, which give attn_decode_split's result).  A window
+ * lower bound applies to every key as for the causal row.  Bits at or past num_rows are
+ * ignored; a row that sees no key gets NaN from the merge (0 / 0).
+ *   row_masks  device, uint64 [batch][num_rows]
+ * Other arguments and returns as attn_decode_split; ATTN_E_INVALID_ARG also for a null
+ * row_masks or a plan of one query row.
+ */
+int attn_decode_split_tree(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                           const int32_t* page_table, const int32_t* seq_lens,
+                           const uint64_t* row_masks, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * Enqueue the two-level merge as one kernel: level 1 folds each run of

@@ -66,7 +66,8 @@ import numpy as np
 __all__ = [
     "InvalidState", "State", "bf16_bits_to_f64", "f16_bits_to_f64", "e4m3_bits_to_f64",
     "f32_bits_to_f64", "stored_to_f64", "visible_range", "row_view", "gather_rows",
-    "keys_values", "dense_attention", "decode_attention", "partial_state", "empty_state",
+    "keys_values", "dense_attention", "decode_attention", "window_row_positions",
+    "partial_state", "empty_state",
     "merge", "finalize", "split_kv_attention", "paged_partials", "validate",
     "prefill_attention", "prefill_row_index",
 ]

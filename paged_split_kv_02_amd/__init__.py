@@ -14,7 +14,8 @@ import os
 from . import build as _build
 
 __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_plan",
-           "attn_decode_split", "attn_decode_merge", "attn_decode_status_string", "make_desc",
+           "attn_decode_split", "attn_decode_split_tree", "attn_decode_merge",
+           "attn_decode_status_string", "make_desc",
            "attn_kv_write", "attn_query_fold", "AttnPrefillPlan", "attn_prefill_plan",
            "attn_prefill",
            "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "ATTN_KV_BF16", "ATTN_KV_F16", "ATTN_KV_FP8_E4M3",
@@ -29,7 +30,7 @@ ATTN_KV_F32 = 3
 STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
           "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
-SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_merge",
+SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_split_tree", "attn_decode_merge",
            "attn_decode_status_string", "attn_kv_write", "attn_query_fold",
            "attn_prefill_plan", "attn_prefill")
 LIB_PATH = _build.LIB
@@ -82,6 +83,9 @@ def _load() -> ctypes.CDLL:
     lib.attn_decode_plan.restype = ctypes.c_int
     lib.attn_decode_split.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P, P, ctypes.c_size_t, P]
     lib.attn_decode_split.restype = ctypes.c_int
+    lib.attn_decode_split_tree.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P, P, P,
+                                           ctypes.c_size_t, P]
+    lib.attn_decode_split_tree.restype = ctypes.c_int
     lib.attn_decode_merge.argtypes = [ctypes.POINTER(AttnDecodePlan), P, ctypes.c_size_t, P, P]
     lib.attn_decode_merge.restype = ctypes.c_int
     lib.attn_kv_write.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, ctypes.c_int32, P, P, P, P, P]
@@ -162,6 +166,18 @@ def attn_decode_split(plan: AttnDecodePlan, q, kv_pool, page_table, seq_lens, wo
                                 _ptr(seq_lens), _ptr(workspace), nbytes, _stream(stream))
     if rc != 0:
         raise AttnDecodeError("attn_decode_split", rc)
+
+
+def attn_decode_split_tree(plan: AttnDecodePlan, q, kv_pool, page_table, seq_lens, row_masks,
+                           workspace, workspace_bytes=None, stream=None) -> None:
+    """attn_decode_split for a window of rows forming a tree: row_masks is a device
+    uint64 [batch][rows] (int64 tensors are taken as the same bits)."""
+    nbytes = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    rc = _lib.attn_decode_split_tree(ctypes.byref(plan), _ptr(q), _ptr(kv_pool),
+                                     _ptr(page_table), _ptr(seq_lens), _ptr(row_masks),
+                                     _ptr(workspace), nbytes, _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_decode_split_tree", rc)
 
 
 def attn_decode_merge(plan: AttnDecodePlan, workspace, out, workspace_bytes=None,

@@ -61,6 +61,9 @@ struct SplitArgs {
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_q_heads, page_size, max_pages, window, chunk_len, num_chunks;
   int32_t num_rows, row_groups;  // query rows per request; groups of 4 rows (multi-row kernel)
+  // Several rows: bit j of row_masks[r * num_rows + i] lets row i see the key of window
+  // row j (tree attention); null means causal rows.
+  const uint64_t* row_masks;
   float qscale_k;  // scale * log2(e) * k_scale: the query dims that meet K columns
   float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
   float vscale;    // v_scale, applied to the written numerators
@@ -230,13 +233,15 @@ __device__ __forceinline__ void make_query_operand(const float* qrow_heads, int 
 }
 
 // One staged tile of 16 keys for one query row: QK^T on MFMA, online softmax over the
-// keys tok0 + 4qg + i visible to the row (lo <= key < hi), PV on MFMA.  The caller has
-// zeroed the V rows of keys no row may see.
-template <int D, int G, bool FOLDED, bool F16>
+// keys tok0 + 4qg + i visible to the row (lo <= key < hi, and with MASKED, a key at or
+// past wstart, i.e. a key of the row window, only if its bit key - wstart of `mask` is
+// set), PV on MFMA.  The caller has zeroed the V rows of keys no row may see.
+template <int D, int G, bool FOLDED, bool F16, bool MASKED = false>
 __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo, int hi,
                                           const typename Ops<F16>::T8 (&qop)[D / 32], int c,
                                           int qg, float& m_run, float& l_run,
-                                          floatx4 (&acc)[D / 128][8]) {
+                                          floatx4 (&acc)[D / 128][8], int wstart = 0,
+                                          uint64_t mask = 0) {
   using S = Shape<D, FOLDED>;
   using O = Ops<F16>;
   using T = typename O::T;
@@ -259,7 +264,9 @@ __device__ __forceinline__ void tile_math(const uint16_t* tile, int tok0, int lo
   for (int i = 0; i < 4; ++i) {
     const float full = s[i] + partner<G>(s[i]);
     const int t = tok0 + 4 * qg + i;
-    sc[i] = (t >= lo && t < hi) ? full : -INFINITY;
+    bool vis = t >= lo && t < hi;
+    if constexpr (MASKED) vis = vis && (t < wstart || ((mask >> ((t - wstart) & 63)) & 1));
+    sc[i] = vis ? full : -INFINITY;
     mx = fmaxf(mx, sc[i]);
   }
   mx = fmaxf(mx, shfl_xor(mx, 16));
@@ -765,7 +772,8 @@ __device__ __forceinline__ void write_row_state(const SplitArgs& a, int64_t st, 
 }
 
 // Several query rows per request (a verify window): row i sits at position
-// L - rows + i and attends causally.  One workgroup = one key chunk of one (request,
+// L - rows + i and attends causally, or with row masks (tree attention) to the keys before
+// the window and the window rows its mask names.  One workgroup = one key chunk of one (request,
 // KV head, group of up to four rows); wave w serves row 4*group + w.  The four waves
 // fetch each tile together (wave w the rows 4qg + w) into a double-buffered LDS tile,
 // so every K/V byte is read once for all the rows of the group.  Workgroups of the
@@ -797,8 +805,12 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
   const int L = a.seq_lens[r];
   const int first_hi = L - rows + 1;  // keys the first row sees: [.., first_hi)
   const int lo_all = (a.window > 0 && first_hi > a.window) ? first_hi - a.window : 0;
-  const int hi = L - rows + row + 1;  // this wave's row
+  const int hi = L - rows + row + 1;  // a causal row's keys: [lo, hi)
   const int lo = (a.window > 0 && hi > a.window) ? hi - a.window : 0;
+  // Keys of the window [L - rows, L) this row sees: its mask, or (causal) rows 0 .. row.
+  const uint64_t mask = !row_active ? 0
+                        : a.row_masks ? a.row_masks[int64_t(r) * rows + row]
+                        : (row >= 63 ? ~uint64_t(0) : (uint64_t(2) << row) - 1);
   const int start = lo_all & ~(kTile - 1);
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
   bool poison = L < rows || int64_t(L) > cap ||
@@ -858,7 +870,8 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
       zero_dead_rows<D, FOLDED>(tile, tok0, lo_all, L, c, qg, wave, wave + 1);
     __syncthreads();  // the tile is complete; the other buffer is free again
     if (row_active)
-      tile_math<D, G, FOLDED, E::kF16>(tile, tok0, lo, hi, qop, c, qg, m_run, l_run, acc);
+      tile_math<D, G, FOLDED, E::kF16, true>(tile, tok0, lo, L, qop, c, qg, m_run, l_run, acc,
+                                             L - rows, mask);
     buf ^= 1;
   };
   for (int tok0 = c0; tok0 < end; tok0 += kAhead * kTile) {
@@ -1109,10 +1122,14 @@ int launch_status() {
 }  // namespace
 }  // namespace attn
 
-extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
-                                 const int32_t* page_table, const int32_t* seq_lens, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  using namespace attn;
+namespace attn {
+namespace {
+
+// The split launch of attn_decode_split (row_masks null: causal rows) and
+// attn_decode_split_tree.
+int split_launch(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                 const int32_t* page_table, const int32_t* seq_lens, const uint64_t* row_masks,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!q || !kv_pool || !page_table || !seq_lens) return ATTN_E_INVALID_ARG;
@@ -1145,6 +1162,7 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   args.num_chunks = plan->num_chunks;
   args.num_rows = plan->num_rows;
   args.row_groups = plan->row_groups;
+  args.row_masks = row_masks;
   args.qscale_k = d.scale * kLog2e * d.k_scale;
   args.qscale_v = d.scale * kLog2e * d.v_scale;
   args.vscale = d.v_scale;
@@ -1153,8 +1171,8 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (rows_on_tiles(d, plan->num_rows))
-    launch_rows_tiles(*plan, q, kv_pool, page_table, seq_lens, args.part_m, args.part_l,
-                      args.part_o, stream);
+    launch_rows_tiles(*plan, q, kv_pool, page_table, seq_lens, row_masks, args.part_m,
+                      args.part_l, args.part_o, stream);
   else if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
     launch_split_kv<512, 8, false>(d.kv_dtype, args, grid, s);
   else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
@@ -1162,6 +1180,27 @@ extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q,
   else
     launch_split_kv<256, 2, false>(d.kv_dtype, args, grid, s);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_decode_split(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                                 const int32_t* page_table, const int32_t* seq_lens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return attn::split_launch(plan, q, kv_pool, page_table, seq_lens, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+extern "C" int attn_decode_split_tree(const attn_decode_plan_t* plan, const float* q,
+                                      const void* kv_pool, const int32_t* page_table,
+                                      const int32_t* seq_lens, const uint64_t* row_masks,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = attn::check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (!row_masks || plan->num_rows < 2) return ATTN_E_INVALID_ARG;
+  return attn::split_launch(plan, q, kv_pool, page_table, seq_lens, row_masks, workspace,
+                            workspace_bytes, stream);
 }
 
 extern "C" int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace,

@@ -33,9 +33,11 @@ int check_prefill_plan(const attn_prefill_plan_t* plan);
 // (with in-row offsets below 2^31 bytes) run on the 32-key MFMA tile kernel, in chunks
 // of whole 32-key tiles; other shapes on the 16-key rows kernel.
 bool rows_on_tiles(const attn_decode_desc& d, int64_t rows);
+// row_masks: null for causal rows, else one 64-bit mask per (request, row) (tree attention).
 void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* kv_pool,
-                       const int32_t* page_table, const int32_t* seq_lens, float* part_m,
-                       float* part_l, float* part_o, void* stream);
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const uint64_t* row_masks, float* part_m, float* part_l, float* part_o,
+                       void* stream);
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 

@@ -99,6 +99,7 @@ struct PrefillArgs {
   float* part_l;
   float* part_o;
   int32_t chunk_len, num_chunks, num_rows, row_groups;
+  const uint64_t* row_masks;  // decode windows: per (request, row) window masks, or null
 };
 
 // Staged tile of kKeys stored rows (whole rows: K and V columns of the row format).
@@ -258,17 +259,28 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
     poison = poison || int64_t(L) - origin > int64_t(a.num_chunks) * a.chunk_len;
   }
 
-  // This lane's column: row qrow of the request, query head `head`; it sees keys lo_c .. pos.
+  // This lane's column: row qrow of the request, query head `head`; it sees keys lo_c .. pos
+  // (none for an idle or poisoned column).  Decode windows: of the window's own keys
+  // [wstart, L), only those whose bit key - wstart is set in the row's mask (causal rows:
+  // bits 0 .. qrow, the same keys).
   const int qrow = row0 + block * RPP + n / G;
   const bool active = qrow < nrows;
   const int head = g * G + n % G;
   const int pos = (active && !poison) ? L - nrows + qrow : -1;
-  const int lo_c = a.window > 0 ? max(0, pos + 1 - a.window) : 0;
+  const int lo_c = pos < 0 ? INT32_MAX : a.window > 0 ? max(0, pos + 1 - a.window) : 0;
+  const int wstart = L - nrows;
+  uint64_t mask = 0;
+  if constexpr (CHUNKED) {
+    if (active)
+      mask = a.row_masks ? a.row_masks[int64_t(qs0) + qrow]
+                         : (qrow >= 63 ? ~uint64_t(0) : (uint64_t(2) << qrow) - 1);
+  }
 
-  // Keys of the workgroup: the first row's window start .. the last row's position (and,
-  // for a decode window, inside the chunk).
+  // Keys of the workgroup: the first row's window start .. the last row's position (a
+  // decode window with masks: .. the last key; and inside the chunk).
   const int pos_first = L - nrows + row0;
-  const int pos_last = L - nrows + min(row0 + QT, nrows) - 1;
+  const int pos_last =
+      (CHUNKED && a.row_masks) ? L - 1 : L - nrows + min(row0 + QT, nrows) - 1;
   const int lo_first = a.window > 0 ? max(0, pos_first + 1 - a.window) : 0;
   int start, ntiles;
   if constexpr (CHUNKED) {
@@ -394,8 +406,10 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   const int kbase = n * P + 16 * hh;
   const int vbase = 4 * hh * P + 2 * (S::TV + half * HALF + DPR * n);
   // Interior tiles: all rows of the workgroup present and every key of the tile visible to
-  // all of them (at or after the last row's window start, at or before the first row).
+  // all of them (at or after the last row's window start, at or before the first row;
+  // decode windows: before the window's own keys).
   const bool full_tile = row0 + QT <= nrows;
+  const int vis_end = CHUNKED ? wstart - 1 : pos_first;
   const int lo_last = a.window > 0 ? max(0, pos_last + 1 - a.window) : 0;
 
   float m_run, l_run;
@@ -467,11 +481,16 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
       for (int e = 0; e < 16; ++e) sc[e] = sp[e];
     }
     // Tiles whose every key every row of the workgroup sees need no mask (uniform branch).
-    if (!(full_tile && k0 >= lo_last && k0 + kKeys - 1 <= pos_first)) {
+    if (!(full_tile && k0 >= lo_last && k0 + kKeys - 1 <= vis_end)) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const bool vis = (key >= lo_c) & (key <= pos);
+        bool vis;
+        if constexpr (CHUNKED)
+          vis = (key >= lo_c) & (key < L) &
+                ((key < wstart) | bool((mask >> ((key - wstart) & 63)) & 1));
+        else
+          vis = (key >= lo_c) & (key <= pos);
         sc[e] = vis ? sc[e] : -INFINITY;
       }
     }
@@ -742,11 +761,13 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
 namespace attn {
 
 void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* kv_pool,
-                       const int32_t* page_table, const int32_t* seq_lens, float* part_m,
-                       float* part_l, float* part_o, void* stream) {
+                       const int32_t* page_table, const int32_t* seq_lens,
+                       const uint64_t* row_masks, float* part_m, float* part_l, float* part_o,
+                       void* stream) {
   const attn_decode_desc& d = p.desc;
   PrefillArgs args;
   fill_common(args, d, q, kv_pool, page_table, seq_lens);
+  args.row_masks = row_masks;
   args.part_m = part_m;
   args.part_l = part_l;
   args.part_o = part_o;

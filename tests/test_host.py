@@ -252,6 +252,25 @@ def test_split_and_merge_refuse_before_any_launch():
     assert L.attn_query_fold(ctypes.byref(bad), fake, fake, fake, None) == S["ATTN_E_PLAN"]
 
 
+def test_tree_split_refuses_before_any_launch():
+    """The tree entry point: a bad plan, a plan of one query row, null masks and the
+    ordinary argument checks are all refused before a launch."""
+    rc, p4 = plan_status([1024], **global_desc(num_rows=4))
+    rc1, p1 = plan_status([1024], **global_desc())
+    assert rc == 0 and rc1 == 0
+    fake = 1 << 20  # never dereferenced
+    ws = p4.workspace_bytes
+    bad = K.AttnDecodePlan.from_buffer_copy(p4)
+    bad.magic = 0
+    T = K._lib.attn_decode_split_tree
+    assert T(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_PLAN"]
+    assert T(None, fake, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert T(ctypes.byref(p1), fake, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert T(ctypes.byref(p4), fake, fake, fake, fake, None, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert T(ctypes.byref(p4), None, fake, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert T(ctypes.byref(p4), fake, fake, fake, fake, fake, fake, ws - 1, None) == S["ATTN_E_WORKSPACE"]
+
+
 def test_status_strings():
     for name, code in S.items():
         s = K.attn_decode_status_string(code)
