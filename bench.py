@@ -92,8 +92,15 @@ class Resident:
         self.ws = torch.empty(int(self.plan.workspace_bytes), dtype=torch.uint8, device=dev)
         self.out = torch.empty(wl.batch * wl.num_rows, wl.num_q_heads, wl.head_dim,
                                dtype=torch.float32, device=dev)
+        self.masks = None
+        if getattr(wl, "row_masks", None) is not None:   # tree attention over the rows
+            self.masks = torch.from_numpy(np.ascontiguousarray(wl.row_masks).view(np.int64)).to(dev)
 
     def split(self):
+        if self.masks is not None:
+            self.K.attn_decode_split_tree(self.plan, self.q, self.pool, self.table, self.lens,
+                                          self.masks, self.ws)
+            return
         self.K.attn_decode_split(self.plan, self.q, self.pool, self.table, self.lens, self.ws)
 
     def merge(self):
@@ -248,6 +255,7 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported here "
               "(the decode step shards across GPUs without this process).", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     import synth
     if not torch.cuda.is_available():
@@ -329,6 +337,10 @@ def main():
                 ("global-decode-163336-split-4rows",
                  lambda: synth.make_workload([163336], **synth.GLOBAL, seed=6, num_rows=4,
                                              spare_pages=1), 20),
+                ("global-decode-163336-split-4rows-tree",
+                 lambda: synth.set_tree(synth.make_workload([163336], **synth.GLOBAL, seed=6,
+                                                            num_rows=4, spare_pages=1),
+                                        np.array([[-1, 0, 0, 1]], dtype=np.int32)), 20),
                 ("global-decode-163336-split-fp8e4m3",
                  lambda: synth.global_decode(163336, seed=7, kv_dtype=synth.FP8), 20),
                 ("global-decode-163336-folded-fp8e4m3",
