@@ -133,11 +133,12 @@ typedef struct attn_decode_desc {
 } attn_decode_desc;
 
 /*
- * A validated plan (host-only POD).  Chunk c of request r covers key positions
- *   [start_r + c * chunk_len, start_r + (c + 1) * chunk_len)  intersected with the keys
- * a query row sees, where lo_r = max(0, L_r - rows + 1 - window) (0 without a window)
- * is the oldest key any row of the request sees and start_r = lo_r rounded down to a
- * multiple of `tile`.  A chunk with no visible key yields the empty partial (-inf, 0, 0).
+ * A validated plan (host-only POD).  Chunk c of request r covers the chunk_len (c even)
+ * or chunk_len_odd (c odd) key positions from
+ *   start_r + (c / 2) * (chunk_len + chunk_len_odd) + (c % 2) * chunk_len
+ * intersected with the keys a query row sees, where
+ * lo_r = max(0, L_r - rows + 1 - window) (0 without a window) is the oldest key any row
+ * of the request sees and start_r = lo_r rounded down to a multiple of `tile`.  A chunk with no visible key yields the empty partial (-inf, 0, 0).
  *
  * Workspace layout (byte offsets from the workspace base, each region 256-byte
  * aligned, all float32, partition-major and contiguous in the output dimension;
@@ -157,8 +158,11 @@ typedef struct attn_decode_plan_t {
   int32_t group_size;    /* query heads per KV head */
   int32_t tile;          /* keys per tile (16; 32 for several query rows at head dim 512
                             over bf16 pages); chunk starts are multiples of it */
-  int32_t chunk_len;     /* keys per chunk: a multiple of 4 * tile for one query row (one
-                            quarter per wave), of tile for several */
+  int32_t chunk_len;     /* keys per even-numbered chunk: a multiple of 4 * tile for one
+                            query row (one quarter per wave), of tile for several */
+  int32_t chunk_len_odd; /* keys per odd-numbered chunk (the same multiple); equal to
+                            chunk_len except for one query row with an automatic chunk
+                            count, where even chunks run on the faster XCDs */
   int32_t num_chunks;    /* chunks per (request, KV head) */
   int32_t merge_group;   /* chunk partials folded per level-1 group */
   int32_t num_groups;    /* level-1 states per (request, query head), at most 8 */

@@ -53,7 +53,8 @@ class AttnDecodeDesc(ctypes.Structure):
 class AttnDecodePlan(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint64), ("desc", AttnDecodeDesc),
                 ("group_size", ctypes.c_int32), ("tile", ctypes.c_int32),
-                ("chunk_len", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32), ("chunk_len_odd", ctypes.c_int32),
+                ("num_chunks", ctypes.c_int32),
                 ("merge_group", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("max_span", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("row_groups", ctypes.c_int32), ("grid_x", ctypes.c_int32),

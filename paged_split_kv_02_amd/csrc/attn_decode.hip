@@ -60,6 +60,7 @@ struct SplitArgs {
   // Pool strides and column offsets in bytes.
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_q_heads, page_size, max_pages, window, chunk_len, num_chunks;
+  int32_t chunk_len_odd;  // keys of odd-numbered chunks (one row; else == chunk_len)
   int32_t num_rows, row_groups;  // query rows per request; groups of 4 rows (multi-row kernel)
   // Several rows: bit j of row_masks[r * num_rows + i] lets row i see the key of window
   // row j (tree attention); null means causal rows.
@@ -68,6 +69,11 @@ struct SplitArgs {
   float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
   float vscale;    // v_scale, applied to the written numerators
 };
+
+// Keys covered by the first c chunks (even chunks chunk_len, odd ones chunk_len_odd).
+__device__ __forceinline__ int64_t chunk_cover(const SplitArgs& a, int c) {
+  return int64_t(c >> 1) * (a.chunk_len + a.chunk_len_odd) + (c & 1) * int64_t(a.chunk_len);
+}
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
@@ -443,9 +449,9 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   const int start = lo & ~(kTile - 1);
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
   bool poison = L < 1 || int64_t(L) > cap ||
-                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
-  const int quarter = a.chunk_len / kWavesPerBlock;
-  const int c0 = start + chunk * a.chunk_len + wave * quarter;
+                int64_t(L) - start > chunk_cover(a, a.num_chunks);
+  const int quarter = ((chunk & 1) ? a.chunk_len_odd : a.chunk_len) / kWavesPerBlock;
+  const int c0 = start + int(chunk_cover(a, chunk)) + wave * quarter;
   const int c1 = min(c0 + quarter, L);
   int end = (!poison && c0 < c1) ? c1 : c0;  // tiles from `end` on are not processed
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
@@ -597,9 +603,9 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   const int start = lo & ~(kTile - 1);
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
   bool poison = L < 1 || int64_t(L) > cap ||
-                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
-  const int quarter = a.chunk_len / kWavesPerBlock;
-  const int c0 = start + chunk * a.chunk_len + wave * quarter;
+                int64_t(L) - start > chunk_cover(a, a.num_chunks);
+  const int quarter = ((chunk & 1) ? a.chunk_len_odd : a.chunk_len) / kWavesPerBlock;
+  const int c0 = start + int(chunk_cover(a, chunk)) + wave * quarter;
   const int c1 = min(c0 + quarter, L);
   const int end = (!poison && c0 < c1) ? c1 : c0;
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
@@ -814,9 +820,9 @@ __global__ __launch_bounds__(256, 1) void rows_partial_kernel(SplitArgs a) {
   const int start = lo_all & ~(kTile - 1);
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
   bool poison = L < rows || int64_t(L) > cap ||
-                int64_t(L) - start > int64_t(a.num_chunks) * a.chunk_len;
-  const int c0 = start + chunk * a.chunk_len;
-  const int c1 = min(c0 + a.chunk_len, L);
+                int64_t(L) - start > chunk_cover(a, a.num_chunks);
+  const int c0 = start + int(chunk_cover(a, chunk));
+  const int c1 = min(c0 + ((chunk & 1) ? a.chunk_len_odd : a.chunk_len), L);
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
 
   PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
@@ -1159,6 +1165,7 @@ int split_launch(const attn_decode_plan_t* plan, const float* q, const void* kv_
   args.max_pages = d.max_pages_per_seq;
   args.window = d.window;
   args.chunk_len = plan->chunk_len;
+  args.chunk_len_odd = plan->chunk_len_odd;
   args.num_chunks = plan->num_chunks;
   args.num_rows = plan->num_rows;
   args.row_groups = plan->row_groups;

@@ -155,8 +155,25 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   }
   if (n > (int64_t(1) << 24)) return ATTN_E_OVERFLOW;
   const int64_t piece_tiles = ceil_div(tiles, n * split);
-  const int64_t chunk_len = piece_tiles * T * split;
+  int64_t chunk_len = piece_tiles * T * split;
+  int64_t chunk_len_odd = chunk_len;
   if (d.num_chunks == 0) n = ceil_div(max_span, chunk_len);
+  // XCD balance (one row, the plan's own chunking): a launch hands workgroups to the
+  // eight XCDs in turn, so with an even number of chunks (the grid's width) chunk c runs
+  // on an XCD of c's parity.  On MI355X the odd XCDs stream HBM ~7-10 % slower (per-wave
+  // timestamps on several parts, whatever the page placement), so even-numbered chunks
+  // take ~5 % more keys and odd-numbered ones as many fewer, and all finish together.
+  if (rows == 1 && d.num_chunks == 0) {
+    const int64_t skew = piece_tiles / kXcdSkewDiv;
+    const int64_t le = (piece_tiles + skew) * T * split, lo = (piece_tiles - skew) * T * split;
+    const int64_t pairs = max_span / (le + lo), rest = max_span - pairs * (le + lo);
+    const int64_t m = 2 * pairs + (rest > 0) + (rest > le);
+    if (skew > 0 && m % 2 == 0) {
+      chunk_len = le;
+      chunk_len_odd = lo;
+      n = m;
+    }
+  }
   // Launch order of the multi-row kernel: row groups of a chunk 8 workgroups apart.
   const int64_t grid_x = groups > 1 ? ceil_div(n, 8) * 8 * groups : n;
 
@@ -180,6 +197,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   p.group_size = d.num_q_heads / d.num_kv_heads;
   p.tile = int32_t(T);
   p.chunk_len = int32_t(chunk_len);
+  p.chunk_len_odd = int32_t(chunk_len_odd);
   p.num_chunks = int32_t(n);
   p.merge_group = int32_t(gm);
   p.num_groups = int32_t(ng);

@@ -10,6 +10,7 @@ namespace attn {
 constexpr uint64_t kPlanMagic = 0x5041474544534b56ull;  // "PAGEDSKV"
 constexpr int kTile = 16;            // keys per tile = rows of one 16x16 MFMA block
 constexpr int kWavesPerBlock = 4;    // one chunk per workgroup, one quarter per wave
+constexpr int64_t kXcdSkewDiv = 20;    // even/odd chunks: +-1/20 of a quarter's tiles
 constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
 constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)

@@ -99,6 +99,7 @@ struct PrefillArgs {
   float* part_l;
   float* part_o;
   int32_t chunk_len, num_chunks, num_rows, row_groups;
+  int32_t chunk_len_odd;      // keys of odd-numbered chunks
   const uint64_t* row_masks;  // decode windows: per (request, row) window masks, or null
 };
 
@@ -256,7 +257,10 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   if constexpr (CHUNKED) {
     const int first_hi = L - nrows + 1;
     origin = (a.window > 0 ? max(0, first_hi - a.window) : 0) & ~(kKeys - 1);
-    poison = poison || int64_t(L) - origin > int64_t(a.num_chunks) * a.chunk_len;
+    const int64_t pair = int64_t(a.chunk_len) + a.chunk_len_odd;
+    const int64_t cover =
+        int64_t(a.num_chunks >> 1) * pair + (a.num_chunks & 1) * int64_t(a.chunk_len);
+    poison = poison || int64_t(L) - origin > cover;
   }
 
   // This lane's column: row qrow of the request, query head `head`; it sees keys lo_c .. pos
@@ -284,8 +288,10 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   const int lo_first = a.window > 0 ? max(0, pos_first + 1 - a.window) : 0;
   int start, ntiles;
   if constexpr (CHUNKED) {
-    const int64_t c0 = origin + int64_t(chunk) * a.chunk_len;
-    const int64_t c1 = min(c0 + a.chunk_len, int64_t(pos_last) + 1);
+    const int64_t c0 = origin + int64_t(chunk >> 1) * (int64_t(a.chunk_len) + a.chunk_len_odd) +
+                       (chunk & 1) * int64_t(a.chunk_len);
+    const int64_t c1 =
+        min(c0 + ((chunk & 1) ? a.chunk_len_odd : a.chunk_len), int64_t(pos_last) + 1);
     start = int(min(c0, int64_t(L)));
     ntiles = (poison || c1 <= c0) ? 0 : int((c1 - c0 + kKeys - 1) / kKeys);
   } else {
@@ -772,6 +778,7 @@ void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* 
   args.part_l = part_l;
   args.part_o = part_o;
   args.chunk_len = p.chunk_len;
+  args.chunk_len_odd = p.chunk_len_odd;
   args.num_chunks = p.num_chunks;
   args.num_rows = p.num_rows;
   args.row_groups = p.row_groups;

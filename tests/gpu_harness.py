@@ -90,7 +90,18 @@ class Device:
         first_hi = L - self.wl.num_rows + 1
         lo = max(0, first_hi - p.desc.window) if p.desc.window > 0 else 0
         start = lo // p.tile * p.tile
-        return [(start + c * p.chunk_len, start + (c + 1) * p.chunk_len) for c in range(p.num_chunks)]
+        return plan_chunk_ranges(p, start)
+
+
+def plan_chunk_ranges(p, start: int) -> list:
+    """[a, b) of every chunk of a plan from a request's start: even-numbered chunks hold
+    chunk_len keys, odd-numbered ones chunk_len_odd (the header's chunk layout)."""
+    out, a = [], start
+    for c in range(p.num_chunks):
+        n = p.chunk_len if c % 2 == 0 else p.chunk_len_odd
+        out.append((a, a + n))
+        a += n
+    return out
 
 
 def compare(got: np.ndarray, ref: np.ndarray) -> dict:

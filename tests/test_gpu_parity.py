@@ -79,6 +79,21 @@ def test_partials_match_oracle_per_chunk():
     check(got, oracle.decode_attention(wl), "partials case")
 
 
+def test_xcd_balanced_chunks_per_chunk():
+    """The automatic plan of a long context gives even-numbered chunks more keys than
+    odd-numbered ones (they run on the faster XCDs); every chunk state covers exactly the
+    range the header's layout gives it."""
+    wl = synth.global_decode(81653, seed=8)
+    note("[gpu] XCD-balanced chunks at 81,653")
+    dev = Device(wl)
+    p = dev.plan
+    assert p.num_chunks % 2 == 0 and p.chunk_len > p.chunk_len_odd, (p.chunk_len, p.chunk_len_odd)
+    got = dev.run()
+    assert dev.guards_intact()
+    check_partials(dev, wl)
+    check(got, oracle.decode_attention(wl), "XCD-balanced 81,653")
+
+
 def test_repeat_runs_bit_identical():
     wl = synth.global_decode(10602, seed=1)
     note("[gpu] repeat x10 L=10602")

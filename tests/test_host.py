@@ -184,20 +184,26 @@ def test_merge_group_bounds():
 
 
 def chunk_ranges(p, L):
+    """Chunks as the header lays them out: even-numbered ones chunk_len keys, odd-numbered
+    ones chunk_len_odd, from the request's start, cut to the visible keys."""
     lo = max(0, L - p.desc.window) if p.desc.window > 0 else 0
-    start = lo // p.tile * p.tile
+    a = lo // p.tile * p.tile
     out = []
     for c in range(p.num_chunks):
-        a = start + c * p.chunk_len
-        out.append((max(a, lo), min(a + p.chunk_len, L)))
+        n = p.chunk_len if c % 2 == 0 else p.chunk_len_odd
+        out.append((max(a, lo), min(a + n, L)))
+        a += n
     return lo, out
 
 
 @pytest.mark.parametrize("lens,fields,expect", [
-    ([1024], dict(num_chunks=8), dict(num_chunks=8, chunk_len=128)),
-    ([163336], dict(), dict(num_chunks=64, chunk_len=2560)),
-    ([10602], dict(), dict(num_chunks=56, chunk_len=192)),
-    ([100], dict(num_chunks=16), dict(num_chunks=16, chunk_len=64)),
+    ([1024], dict(num_chunks=8), dict(num_chunks=8, chunk_len=128, chunk_len_odd=128)),
+    # automatic chunking of a long context: even-numbered chunks (on the even XCDs) take
+    # 42 tiles per quarter, odd ones 38, instead of 40 each
+    ([163336], dict(), dict(num_chunks=64, chunk_len=2688, chunk_len_odd=2432)),
+    ([81653], dict(), dict(num_chunks=64, chunk_len=1344, chunk_len_odd=1216)),
+    ([10602], dict(), dict(num_chunks=56, chunk_len=192, chunk_len_odd=192)),
+    ([100], dict(num_chunks=16), dict(num_chunks=16, chunk_len=64, chunk_len_odd=64)),
 ])
 def test_chunking(lens, fields, expect):
     L = lens[0]
@@ -206,7 +212,9 @@ def test_chunking(lens, fields, expect):
     assert rc == 0
     for k, v in expect.items():
         assert getattr(p, k) == v, (k, getattr(p, k))
-    assert p.chunk_len % (4 * p.tile) == 0 and p.tile == 16
+    assert p.chunk_len % (4 * p.tile) == 0 and p.chunk_len_odd % (4 * p.tile) == 0
+    assert p.tile == 16
+    assert p.chunk_len_odd == p.chunk_len or p.num_chunks % 2 == 0  # skew: even chunk count
     lo, ranges = chunk_ranges(p, L)
     covered = [x for a, b in ranges for x in range(a, b)]
     assert covered == list(range(lo, L)), "chunks must tile [lo, L) in order"
@@ -281,7 +289,9 @@ def test_status_strings():
 def test_rows_plan():
     rc, p = plan_status([1000, 2000], **global_desc(2048, batch=2, num_rows=4))
     assert rc == 0 and p.num_rows == 4 and p.row_groups == 1 and p.grid_x == p.num_chunks
-    assert p.chunk_len % 16 == 0
+    assert p.chunk_len % 16 == 0 and p.chunk_len_odd == p.chunk_len  # rows: uniform chunks
+    rc, p = plan_status([163336], **global_desc(163336, num_rows=4))
+    assert rc == 0 and p.chunk_len_odd == p.chunk_len
     rc, p = plan_status([1000], **global_desc(1024, num_rows=8))
     assert rc == 0 and p.row_groups == 2 and p.grid_x == -(-p.num_chunks // 8) * 8 * 2
     # workspace counts request x row states
