@@ -51,6 +51,18 @@ def test_tree_global(rows, fmt):
     check(got, oracle.decode_attention(wl), f"tree rows={rows} {fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_tree_global_with_window(fmt):
+    """The tile kernel with tree masks and a window lower bound (700 keys): the bound
+    applies to the window's own keys too, rows' bounds differ, chunks are explicit."""
+    wl = synth.make_workload([3000, 1400, 300], **dict(synth.GLOBAL, window=700), fmt=fmt,
+                             seed=125, num_rows=8, pad="nan")
+    synth.set_tree(wl, synth.random_parents(3, 8, 125))
+    dev, got = run_tree(wl, f"rows=8 window=700 {fmt}", num_chunks=7)
+    assert dev.plan.tile == 32
+    check(got, oracle.decode_attention(wl), f"tree window {fmt}")
+
+
 @pytest.mark.parametrize("shape", ["sliding", "global-f16", "global-fp8"])
 def test_tree_on_the_rows_kernel(shape):
     if shape == "sliding":
