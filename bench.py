@@ -400,11 +400,14 @@ def main():
                               "timing": "median of 20, cache flushed"}
             print(f"# {name}: {t * 1e3:.1f} us", file=sys.stderr, flush=True)
         del wres
-        # paged prefill: a 10,602-token global prompt (split and folded rows) and the
-        # sliding layers' 16 ragged prompts; compute-bound (MFMA), reported in TFLOP/s
+        # paged prefill: a 10,602-token global prompt (split and folded rows, and split rows
+        # over an FP8 pool) and the sliding layers' 16 ragged prompts; compute-bound (MFMA),
+        # reported in TFLOP/s
         for name, maker in (("global-prefill-10602-split", lambda: synth.global_prefill(10602, seed=11)),
                             ("global-prefill-10602-folded",
                              lambda: synth.global_prefill(10602, seed=11, fmt="folded")),
+                            ("global-prefill-10602-split-fp8",
+                             lambda: synth.global_prefill(10602, seed=11, kv_dtype=synth.FP8)),
                             ("sliding-prefill-16ragged-w1024", lambda: synth.sliding_prefill(seed=12))):
             if not wanted(name):
                 continue

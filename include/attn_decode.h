@@ -157,7 +157,7 @@ typedef struct attn_decode_plan_t {
   attn_decode_desc desc;
   int32_t group_size;    /* query heads per KV head */
   int32_t tile;          /* keys per tile (16; 32 for several query rows at head dim 512
-                            over bf16 pages); chunk starts are multiples of it */
+                            over bf16 or FP8 pages); chunk starts are multiples of it */
   int32_t chunk_len;     /* keys per even-numbered chunk: a multiple of 4 * tile for one
                             query row (one quarter per wave), of tile for several */
   int32_t chunk_len_odd; /* keys per odd-numbered chunk (the same multiple); equal to
@@ -294,7 +294,9 @@ int attn_query_fold(const attn_decode_plan_t* plan, const float* q, const float*
  * window and max(0, p + 1 - window) with one: each row is a decode token at length
  * p + 1 (n_r < L_r is a continuation after L_r - n_r earlier keys).
  * The descriptor is the decode descriptor (num_chunks, merge_group and num_rows are not
- * used).  Supported: the decode shapes, bf16 pools, page_size a multiple of 32.
+ * used).  Supported: the decode shapes, bf16 and FP8 E4M3 pools (FP8 codes are widened
+ * to bf16 on their way on chip and the dequantisation factors applied as in decode),
+ * page_size a multiple of 32.
  * The output is written directly (no workspace, no merge): one workgroup owns
  * row_tile consecutive rows of one (request, KV head) and walks their keys in
  * key_tile-key tiles, staged once in on-chip memory for all its rows and heads.
@@ -314,8 +316,8 @@ typedef struct attn_prefill_plan_t {
  * Validate `desc`, the host lengths seq_lens_host[batch] and the host row offsets
  * q_starts_host[batch + 1], and fill `plan`.  No device call is made.
  * Refusals as attn_decode_plan for the descriptor (ATTN_E_INVALID_ARG,
- * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); an element type other than bf16 or a page size
- * not a multiple of 32 (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
+ * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); an f16 or f32 pool or a page size not a
+ * multiple of 32 (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
  * more rows than keys in a request (ATTN_E_INVALID_ARG); a length above
  * max_pages_per_seq * page_size (ATTN_E_PAST_PAGES).
  */
@@ -325,7 +327,7 @@ int attn_prefill_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host
 /*
  * Enqueue the prefill kernel.
  *   q          device, float32 [total_rows][num_q_heads][head_dim] (FOLDED: folded q')
- *   kv_pool    device, bf16 pool laid out as described for attn_decode_desc
+ *   kv_pool    device, bf16 or FP8 E4M3 pool laid out as described for attn_decode_desc
  *   page_table device, int32 [batch][max_pages_per_seq]
  *   seq_lens   device, int32 [batch]; q_starts device, int32 [batch + 1]; both must equal
  *              what the plan was given.  A request whose device offsets the plan cannot

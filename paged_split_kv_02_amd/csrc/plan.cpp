@@ -229,13 +229,18 @@ bool tile_offsets_fit(const attn_decode_desc& d) {
          add_ok(a, uint64_t(row_extent(d) * eb), &b) && b <= uint64_t(INT32_MAX);
 }
 
+// Element types the 32-key tile kernel stages: bf16 as stored, FP8 E4M3 widened to bf16.
+bool tile_dtype(const attn_decode_desc& d) {
+  return d.kv_dtype == ATTN_KV_BF16 || d.kv_dtype == ATTN_KV_FP8_E4M3;
+}
+
 bool rows_on_tiles(const attn_decode_desc& d, int64_t rows) {
-  return rows > 1 && d.head_dim == 512 && d.kv_dtype == ATTN_KV_BF16 &&
-         d.page_size % kPrefillKeys == 0 && tile_offsets_fit(d);
+  return rows > 1 && d.head_dim == 512 && tile_dtype(d) && d.page_size % kPrefillKeys == 0 &&
+         tile_offsets_fit(d);
 }
 
 bool prefill_shape_supported(const attn_decode_desc& d) {
-  return shape_supported(d) && d.kv_dtype == ATTN_KV_BF16 && d.page_size % kPrefillKeys == 0;
+  return shape_supported(d) && tile_dtype(d) && d.page_size % kPrefillKeys == 0;
 }
 
 int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,

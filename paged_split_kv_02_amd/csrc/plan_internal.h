@@ -30,7 +30,7 @@ bool prefill_shape_supported(const attn_decode_desc& d);
 int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,
                       attn_prefill_plan_t* plan);
 int check_prefill_plan(const attn_prefill_plan_t* plan);
-// Decode windows of several rows at head dim 512 over bf16 pages of whole 32-key tiles
+// Decode windows of several rows at head dim 512 over bf16 or FP8 pages of whole 32-key tiles
 // (with in-row offsets below 2^31 bytes) run on the 32-key MFMA tile kernel, in chunks
 // of whole 32-key tiles; other shapes on the 16-key rows kernel.
 bool rows_on_tiles(const attn_decode_desc& d, int64_t rows);

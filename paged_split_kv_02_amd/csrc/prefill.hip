@@ -141,6 +141,13 @@ __device__ __forceinline__ floatx16 mma(u32x4 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
+// Two E4M3 codes (bytes 2HI, 2HI + 1 of w) to a packed bf16 pair: exact, since every E4M3
+// value is a bf16 value.
+template <int HI>
+__device__ __forceinline__ unsigned widen8(unsigned w) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI != 0));
+}
+
 // Page-table entry through the scalar cache (uniform index; the table is only read).
 __device__ __forceinline__ int32_t table_entry(const int32_t* row, int idx) {
   typedef const int32_t __attribute__((address_space(4))) cint;
@@ -193,9 +200,12 @@ __device__ __forceinline__ int pv_key(int t, int hh, int j) {
 //     chunk of one group of four rows (32 columns = 4 rows x 8 heads, each of the four
 //     waves holding a quarter of the dims), and the chunk's unnormalised state (m in
 //     natural-log units, l, O) is written for the merge, as by the one-row decode kernels.
-template <int D, int G, bool FOLDED, bool CHUNKED>
+template <int D, int G, bool FOLDED, bool CHUNKED, bool FP8>
 __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   constexpr int SPLIT = CHUNKED ? 4 : (D == 512 ? 2 : 1);  // waves sharing a column block
+  // Staged through registers: decode windows (to keep tiles in flight) and FP8 pools (to
+  // widen the codes to bf16 on their way into LDS).  Prefill keeps one tile ahead.
+  constexpr bool REGS = CHUNKED || FP8;
   using S = PShape<D, FOLDED, SPLIT>;
   constexpr int P = S::PITCH;
   constexpr int HALF = S::HALF;
@@ -324,8 +334,15 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   // the tile is wanted: a tile past the end (or on a page outside the pool) gets an empty
   // range, so its loads return zeros without touching memory.  Every step then issues
   // the same loads, and the compiler's wait before a copy keeps the newer tile in flight.
+  // FP8 rows: lane l < COLS / 16 holds stored codes 16l .. 16l + 15 of the staged row (K
+  // or rotated K columns first, then V), widened to the bf16 of staged columns 16l ..
   constexpr int RW = S::ROWS_PER_WAVE;
-  constexpr int NS = kStageSets;  // register sets: tiles in flight ahead of the math
+  constexpr int NS = CHUNKED ? kStageSets : 1;  // register sets: tiles ahead of the math
+  constexpr int KC = FOLDED ? S::ROT : D;        // staged K columns
+  constexpr int FP8_LANES = S::COLS / 16;
+  const uint32_t off8 = lane >= FP8_LANES ? 0x80000000u  // past the range: zeros, no access
+                        : 16 * lane < KC ? uint32_t(a.k_offset) + 16 * lane
+                                         : uint32_t(a.v_offset) + 16 * lane - KC;
   u32x4 stg[NS][RW][2];
   auto fetch = [&](u32x4 (&st)[RW][2], int k0, bool want) -> bool {  // false: bad page
     const char* b = want ? tile_base(k0) : nullptr;
@@ -334,6 +351,11 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const uint32_t ro = uint32_t(i * S::WAVES + wave) * uint32_t(a.row_stride);
+      if constexpr (FP8) {
+        st[i][0] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, lane < FP8_LANES ? ro + off8 : 0x80000000u, 0, kStreamLoad);
+        continue;
+      }
 #pragma unroll
       for (int k = 0; k < S::FULL_KB; ++k)
         st[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off[k], 0, kStreamLoad);
@@ -346,6 +368,17 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   auto stash = [&](const u32x4 (&st)[RW][2], char* lds) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
+      if constexpr (FP8) {
+        if (lane < FP8_LANES) {
+          char* lb = lds + (i * S::WAVES + wave) * P + 32 * lane;
+          const u32x4 x = st[i][0];
+          *reinterpret_cast<u32x4*>(lb) =
+              u32x4{widen8<0>(x[0]), widen8<1>(x[0]), widen8<0>(x[1]), widen8<1>(x[1])};
+          *reinterpret_cast<u32x4*>(lb + 16) =
+              u32x4{widen8<0>(x[2]), widen8<1>(x[2]), widen8<0>(x[3]), widen8<1>(x[3])};
+        }
+        continue;
+      }
       char* lb = lds + (i * S::WAVES + wave) * P + 16 * lane;
 #pragma unroll
       for (int k = 0; k < S::FULL_KB; ++k) *reinterpret_cast<u32x4*>(lb + 1024 * k) = st[i][k];
@@ -358,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   // operand is prepared, so they stream meanwhile.
   int count0 = ntiles;  // tiles whose pages were found (a missing page poisons the rest)
   auto prologue = [&]() {
-    if constexpr (CHUNKED) {
+    if constexpr (REGS) {
 #pragma unroll
       for (int u = 0; u < NS; ++u)
         if (!fetch(stg[u], start + u * kKeys, count0 > u)) count0 = min(count0, u);
@@ -593,7 +626,7 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 #pragma unroll
     for (int jj = 0; jj < DPR; ++jj) acc[jj] = floatx16{};
     int count = count0;
-    if constexpr (CHUNKED) {
+    if constexpr (REGS) {
       // Tile it sits in registers (fetched two steps earlier): copy it into its buffer
       // (free: every wave passed the last barrier after using it two tiles ago), refill
       // the registers with tile it + 2, wait for all waves' copies, use the buffer.
@@ -644,9 +677,11 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   };
   run(Flag<false>{});
 
-  // Workgroup-wide OR of the overflow flags through the score slots.
+  // Workgroup-wide OR of the overflow flags through the score slots.  The wave's vote is
+  // taken with every lane active, before lane 0 stores it.
+  const bool wave_overflow = __any(overflow);
   __syncthreads();
-  if (lane == 0) xs[wave][0][0][0] = __any(overflow) ? 1.0f : 0.0f;
+  if (lane == 0) xs[wave][0][0][0] = wave_overflow ? 1.0f : 0.0f;
   __syncthreads();
   bool any_overflow = false;
 #pragma unroll
@@ -700,8 +735,11 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 }
 
 template <int D, int G, bool FOLDED, bool CHUNKED>
-void launch_rows_tile(const PrefillArgs& args, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED>), grid, dim3(256), 0, s, args);
+void launch_rows_tile(const PrefillArgs& args, int kv_dtype, dim3 grid, hipStream_t s) {
+  if (kv_dtype == ATTN_KV_FP8_E4M3)
+    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, true>), grid, dim3(256), 0, s, args);
+  else
+    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, false>), grid, dim3(256), 0, s, args);
 }
 
 // Pool geometry and query scaling shared by both uses.
@@ -756,11 +794,11 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (d.head_dim == 512 && d.format == ATTN_KV_SPLIT)
-    launch_rows_tile<512, 8, false, false>(args, grid, s);
+    launch_rows_tile<512, 8, false, false>(args, d.kv_dtype, grid, s);
   else if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
-    launch_rows_tile<512, 8, true, false>(args, grid, s);
+    launch_rows_tile<512, 8, true, false>(args, d.kv_dtype, grid, s);
   else
-    launch_rows_tile<256, 2, false, false>(args, grid, s);
+    launch_rows_tile<256, 2, false, false>(args, d.kv_dtype, grid, s);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
@@ -785,9 +823,9 @@ void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* 
   const dim3 grid(p.grid_x, d.num_kv_heads, d.batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.format == ATTN_KV_FOLDED)
-    launch_rows_tile<512, 8, true, true>(args, grid, s);
+    launch_rows_tile<512, 8, true, true>(args, d.kv_dtype, grid, s);
   else
-    launch_rows_tile<512, 8, false, true>(args, grid, s);
+    launch_rows_tile<512, 8, false, true>(args, d.kv_dtype, grid, s);
 }
 
 }  // namespace attn

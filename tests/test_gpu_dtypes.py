@@ -72,11 +72,13 @@ def test_rows(dt, rows):
     check(got, oracle.decode_attention(ws), f"{dt} sliding rows={rows}")
 
 
-def test_fp8_widening_is_exact():
+@pytest.mark.parametrize("rows", [1, 4])
+def test_fp8_widening_is_exact(rows):
     """FP8 codes with unit factors and the bf16 pool of the same values (E4M3 is a subset
-    of bf16) give identical bits: the kernel multiplies the same bf16 operands."""
+    of bf16) give identical bits: the kernel multiplies the same bf16 operands.  One row
+    runs the split kernel, four rows the 32-key tile kernel."""
     wl8 = synth.make_workload([3000, 700], **synth.GLOBAL, seed=78, kv_dtype=synth.FP8,
-                              k_scale=1.0, v_scale=1.0, pad="nan")
+                              k_scale=1.0, v_scale=1.0, pad="nan", num_rows=rows)
     # make sure every class of code is present in live rows: subnormals, +-448, +-0
     live = np.flatnonzero(oracle.e4m3_bits_to_f64(wl8.pool) == oracle.e4m3_bits_to_f64(wl8.pool))
     rng = np.random.default_rng(78)
@@ -84,11 +86,12 @@ def test_fp8_widening_is_exact():
     wl8.pool[pick] = rng.choice(np.array([0x01, 0x81, 0x07, 0x87, 0x08, 0x7E, 0xFE, 0x00, 0x80],
                                          dtype=np.uint8), size=pick.size)
     bf = torch.from_numpy(wl8.pool.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16)
-    wl16 = synth.make_workload([3000, 700], **synth.GLOBAL, seed=78, pad="nan")
+    wl16 = synth.make_workload([3000, 700], **synth.GLOBAL, seed=78, pad="nan", num_rows=rows)
     wl16.pool = bf.view(torch.int16).numpy().view(np.uint16)
     wl16.table = wl8.table
-    _, got8 = run_case(wl8, "fp8 with extreme codes")
-    _, got16 = run_case(wl16, "bf16 of the same values")
+    dev8, got8 = run_case(wl8, f"fp8 with extreme codes rows={rows}")
+    _, got16 = run_case(wl16, f"bf16 of the same values rows={rows}")
+    assert dev8.plan.tile == (32 if rows > 1 else 16)
     assert np.array_equal(got8.view(np.uint32), got16.view(np.uint32))
     # the absolute bar is stated for N(0, 1) values; here V reaches 448, so it scales by that
     check(got8, oracle.decode_attention(wl8), "fp8 extreme codes", tol=2e-3 * 448)

@@ -132,29 +132,33 @@ def test_page_permutation_and_layout_invariance():
     check(a[::5], oracle.prefill_attention(base, rows=range(0, 764, 5)), "permutation")
 
 
+@pytest.mark.parametrize("head", [0, 5])
 @pytest.mark.parametrize("shape", ["global", "sliding"])
-def test_slow_path_on_a_dominant_key(shape):
+def test_slow_path_on_a_dominant_key(shape, head):
     """A key planted at position 100 scores ~113 nat (global) / ~80 nat (sliding) above every
     other key for the rows after it: beyond the headroom of the no-rescale loop (the
     probabilities would overflow), so the workgroups recompute with rescaling.  Rows before
-    it are ordinary."""
+    it are ordinary.  With query head 5 no column that overflows sits on a wave's first
+    lane: the workgroup's vote must still see it."""
     if shape == "global":
         wl = synth.make_workload([400], **synth.GLOBAL, seed=204, q_lens=[400], pad="nan")
     else:
         wl = synth.make_workload([400], **synth.SLIDING, seed=204, q_lens=[400], pad="nan",
                                  max_pages=8)
-    u = np.ascontiguousarray(wl.q[150, 0], dtype=np.float32)   # query head 0 of row 150
-    wl.q[:, 0, :] = u                                          # every row of head 0 asks for u
+    u = np.ascontiguousarray(wl.q[150, head], dtype=np.float32)  # the head's query at row 150
+    wl.q[:, head, :] = u                                         # every row of it asks for u
     key = synth.f32_to_bf16_bits((5.0 * u).astype(np.float32))
     j = 100
+    g = head // (wl.num_q_heads // wl.num_kv_heads)               # the head's KV head
     pid = int(wl.table[0][j // wl.page_size])
-    base = pid * wl.page_stride + (j % wl.page_size) * wl.row_stride + wl.k_offset  # KV head 0
+    base = (pid * wl.page_stride + g * wl.head_stride + (j % wl.page_size) * wl.row_stride
+            + wl.k_offset)
     wl.pool[base:base + wl.head_dim] = key
-    _, got = run_case(wl, f"dominant key {shape}")
+    _, got = run_case(wl, f"dominant key {shape} head {head}")
     ref = oracle.prefill_attention(wl)
-    check(got, ref, f"dominant key {shape}")
-    v100 = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [j])))[1][0]
-    assert np.max(np.abs(got[j:, 0] - v100)) <= 1e-5
+    check(got, ref, f"dominant key {shape} head {head}")
+    v100 = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, g, [j])))[1][0]
+    assert np.max(np.abs(got[j:, head] - v100)) <= 1e-5
 
 
 def test_slow_path_with_rows_past_the_window():
@@ -205,6 +209,56 @@ def test_full_size_sliding_sampled():
         a, b = int(starts[r]), int(starts[r + 1])
         rows += sorted(set([a, b - 1] + rng.integers(a, b, 3).tolist()))
     check(got[rows], oracle.prefill_attention(wl, rows=rows), "sliding 16 sampled")
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_fp8_global_ragged(fmt):
+    """FP8 E4M3 pools (factors 0.0175 / 0.0225): the codes are widened to bf16 on their
+    way into LDS; ragged prompts, a continuation, a one-row and a zero-row request."""
+    wl = synth.make_workload([300, 610, 1, 45, 257], **synth.GLOBAL, fmt=fmt, seed=210,
+                             q_lens=[300, 37, 1, 0, 257], spare_pages=3, pad="nan",
+                             kv_dtype=synth.FP8)
+    _, got = run_case(wl, f"fp8 global {fmt} ragged")
+    check(got, oracle.prefill_attention(wl), f"fp8 global {fmt} ragged")
+
+
+def test_fp8_sliding_window_cases():
+    wl = synth.make_workload([1300, 1500, 70, 1], **synth.SLIDING, seed=211, kv_dtype=synth.FP8,
+                             q_lens=[1300, 150, 70, 1], max_pages=40, pad="nan")
+    _, got = run_case(wl, "fp8 sliding window cases")
+    rows = list(range(0, 1300, 7)) + list(range(1300, 1521))
+    check(got[rows], oracle.prefill_attention(wl, rows=rows), "fp8 sliding window cases")
+
+
+@pytest.mark.parametrize("shape", ["global-split", "global-folded", "sliding"])
+def test_fp8_prefill_equals_bf16_of_the_same_values(shape):
+    """With unit factors an FP8 pool and the bf16 pool of the same values (every E4M3
+    value is a bf16 value) give identical output bits: the widening is exact and the
+    kernel multiplies the same operands.  Extreme codes (+-448, subnormals, +-0) are
+    planted among the live keys."""
+    if shape == "sliding":
+        kw = dict(synth.SLIDING)
+        mk = dict(max_pages=20, q_lens=[200, 90])
+        lens = [200, 1100]
+    else:
+        kw = dict(synth.GLOBAL)
+        mk = dict(fmt=shape.split("-")[1], q_lens=[300, 64])
+        lens = [300, 700]
+    wl8 = synth.make_workload(lens, **kw, seed=212, kv_dtype=synth.FP8, k_scale=1.0, v_scale=1.0,
+                              pad="nan", **mk)
+    live = np.flatnonzero(oracle.e4m3_bits_to_f64(wl8.pool) == oracle.e4m3_bits_to_f64(wl8.pool))
+    rng = np.random.default_rng(212)
+    pick = rng.choice(live, size=3000, replace=False)
+    wl8.pool[pick] = rng.choice(np.array([0x01, 0x81, 0x07, 0x87, 0x08, 0x7E, 0xFE, 0x00, 0x80],
+                                         dtype=np.uint8), size=pick.size)
+    wl16 = synth.make_workload(lens, **kw, seed=212, pad="nan", **mk)
+    bf = torch.from_numpy(wl8.pool.copy()).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    wl16.pool = bf.view(torch.int16).numpy().view(np.uint16)
+    wl16.table = wl8.table
+    _, got8 = run_case(wl8, f"fp8 {shape} extreme codes")
+    _, got16 = run_case(wl16, f"bf16 {shape} of the same values")
+    assert np.array_equal(got8.view(np.uint32), got16.view(np.uint32))
+    check(got8, oracle.prefill_attention(wl8), f"fp8 {shape} extreme codes", tol=2e-3 * 448)
 
 
 def test_device_mismatches_fail_closed():

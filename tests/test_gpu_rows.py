@@ -43,6 +43,33 @@ def test_rows_global_with_window(fmt):
     check(got, oracle.decode_attention(wl), f"rows=6 window {fmt}")
 
 
+@pytest.mark.parametrize("head", [0, 5])
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_rows_dominant_key(fmt, head):
+    """A key at position 100 scores ~160 log2 units above the rest for every row of one
+    query head: beyond the headroom of the tile kernel's no-rescale loop, so the workgroups
+    of that chunk recompute with rescaling.  With query head 5 no overflowing column sits on
+    a wave's first lane; the workgroup's vote must still see it."""
+    wl = synth.make_workload([900, 300], **synth.GLOBAL, fmt=fmt, seed=65, num_rows=4, pad="nan")
+    u = np.ascontiguousarray(wl.q[0, 2, head], dtype=np.float32)
+    wl.q[0, :, head, :] = u
+    j = 100
+    pid = int(wl.table[0][j // wl.page_size])
+    base = pid * wl.page_stride + (j % wl.page_size) * wl.row_stride + wl.k_offset  # KV head 0
+    wl.pool[base:base + wl.rot_cols if fmt == "folded" else base + wl.head_dim] = \
+        synth.f32_to_bf16_bits((5.0 * (u[:wl.rot_cols] if fmt == "folded" else u)).astype(np.float32))
+    if fmt == "folded":   # the unrotated dims score against the V columns: scale those too
+        vb = base - wl.k_offset + wl.v_offset + wl.rot_cols
+        vals = 5.0 * u[wl.rot_cols:] / wl.fold_w
+        wl.pool[vb:vb + wl.head_dim - wl.rot_cols] = synth.f32_to_bf16_bits(vals.astype(np.float32))
+    dev, got = run_case(wl, f"rows=4 {fmt} dominant key head {head}", num_chunks=3)
+    assert dev.plan.tile == 32
+    ref = oracle.decode_attention(wl)
+    check(got, ref, f"rows=4 {fmt} dominant key head {head}")
+    vj = oracle.keys_values(wl, oracle.stored_to_f64(oracle.gather_rows(wl, 0, 0, [j])))[1][0]
+    assert np.max(np.abs(got[0, :, head] - vj)) <= 1e-5
+
+
 @pytest.mark.parametrize("shape", ["split", "folded", "sliding"])
 def test_rows_bad_page_and_device_lengths(shape):
     """Forced from the host (every kernel exits normally): a table entry outside the pool,

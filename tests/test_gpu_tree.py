@@ -1,7 +1,7 @@
 """GPU parity of tree attention over a window of query rows (attn_decode_split_tree +
 attn_decode_merge through the C ABI) against the fp64 oracle: seeded random forests on
-both multi-row kernels (head dim 512 over bf16 pages: the 32-key tile kernel; head dim
-256 and other element types: the 16-key rows kernel), a chain of rows equal to the
+both multi-row kernels (head dim 512 over bf16 or FP8 pages: the 32-key tile kernel; head
+dim 256 and f16 pools: the 16-key rows kernel), a chain of rows equal to the
 causal window bit for bit, a row that sees no key, per-chunk partials and the full
 163,336-token length.  Bar as for decode: max |GPU - oracle| <= 2e-3, NMSE <= 1e-4."""
 import math
@@ -64,7 +64,9 @@ def test_tree_global_with_window(fmt):
 
 
 @pytest.mark.parametrize("shape", ["sliding", "global-f16", "global-fp8"])
-def test_tree_on_the_rows_kernel(shape):
+def test_tree_on_other_shapes(shape):
+    """Head dim 256 and f16 pools on the 16-key rows kernel; FP8 pools at head dim 512 on
+    the 32-key tile kernel (codes widened to bf16 on their way into LDS)."""
     if shape == "sliding":
         wl = synth.make_workload([1030, 1500, 40, 3000], **synth.SLIDING, seed=130, num_rows=7,
                                  pad="nan", max_pages=64)
@@ -74,7 +76,7 @@ def test_tree_on_the_rows_kernel(shape):
                                  pad="nan")
     synth.set_tree(wl, synth.random_parents(wl.batch, wl.num_rows, 132))
     dev, got = run_tree(wl, shape)
-    assert dev.plan.tile == 16
+    assert dev.plan.tile == (32 if shape == "global-fp8" else 16)
     check(got, oracle.decode_attention(wl), f"tree {shape}")
 
 

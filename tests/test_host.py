@@ -322,7 +322,9 @@ def test_rows_plan_tile_choice():
     rc, p = plan_status([1000], **global_desc(1024, num_rows=1))
     assert rc == 0 and p.tile == 16
     rc, p = plan_status([1000], **global_desc(1024, num_rows=4, kv_dtype=1))
-    assert rc == 0 and p.tile == 16
+    assert rc == 0 and p.tile == 16                    # f16: the 16-key rows kernel
+    rc, p = plan_status([1000], **global_desc(1024, num_rows=4, kv_dtype=2))
+    assert rc == 0 and p.tile == 32                    # FP8: widened on the 32-key kernel
     rc, p = plan_status([1000], **global_desc(1024, num_rows=4, page_size=16,
                                               max_pages_per_seq=64, page_stride=4 * 16 * 1024,
                                               head_stride=16 * 1024, num_pages=70))
@@ -357,6 +359,11 @@ def test_prefill_plan_layout_matches_header(tmp_path):
     assert vals[1:] == [getattr(K.AttnPrefillPlan, f).offset for f in pfields]
 
 
+def test_prefill_plan_accepts_fp8():
+    rc, p = prefill_status([1024], [0, 1000], **global_desc(kv_dtype=2, k_scale=0.02, v_scale=0.03))
+    assert rc == 0 and p.row_tile == 8 and p.desc.kv_dtype == 2
+
+
 def test_prefill_plan_tiles():
     rc, p = prefill_status([1024], [0, 1000], **global_desc())
     assert rc == 0 and p.row_tile == 8 and p.key_tile == 32 and p.total_rows == 1000
@@ -375,7 +382,6 @@ def test_prefill_plan_tiles():
     ([1024], [0, 1025], dict(), "ATTN_E_INVALID_ARG"),            # more rows than keys
     ([10, 10], [0, 5, 4], dict(batch=2), "ATTN_E_INVALID_ARG"),   # decreasing offsets
     ([1025], [0, 1], dict(), "ATTN_E_PAST_PAGES"),
-    ([1024], [0, 8], dict(kv_dtype=2), "ATTN_E_UNSUPPORTED"),     # FP8: decode only
     ([1024], [0, 8], dict(kv_dtype=1), "ATTN_E_UNSUPPORTED"),     # f16: decode only
     ([1024], [0, 8], dict(page_size=16, max_pages_per_seq=64), "ATTN_E_UNSUPPORTED"),
     ([1024], [0, 8], dict(head_dim=128), "ATTN_E_UNSUPPORTED"),
