@@ -333,6 +333,7 @@ def main():
                 ("global-decode-40002-split", lambda: synth.global_decode(40002, seed=14), 20),
                 ("global-decode-81653-split", lambda: synth.global_decode(81653, seed=15), 20),
                 ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
+                ("global-decode-4streams-9k-split", lambda: synth.global_streams(seed=16), 20),
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
                 ("global-decode-163336-split-4rows",
                  lambda: synth.make_workload([163336], **synth.GLOBAL, seed=6, num_rows=4,

@@ -370,6 +370,17 @@ def global_decode(L: int, seed: int = 1, fmt: str = SPLIT, **kw) -> Workload:
     return make_workload([L], **GLOBAL, fmt=fmt, seed=seed, **kw)
 
 
+def global_streams(seed: int = 16, streams: int = 4, prompt: int = 9000, spread: int = 640,
+                   fmt: str = SPLIT, **kw) -> Workload:
+    """Global-layer decode of several concurrent streams: ``streams`` requests whose
+    contexts are a ``prompt``-token prompt plus 0 .. spread - 1 decoded tokens (seeded),
+    the four-stream, 9k-prompt serving case."""
+    g = _gen(seed + 77)
+    lens = (prompt + torch.randint(0, spread, (streams,), generator=g)).tolist()
+    kw.setdefault("spare_pages", 1)
+    return make_workload(lens, **GLOBAL, fmt=fmt, seed=seed, **kw)
+
+
 def global_prefill(n: int, context: int = 0, seed: int = 11, fmt: str = SPLIT, **kw) -> Workload:
     """Global-layer prefill: a prompt of n new rows after ``context`` earlier tokens,
     one request (10,602 rows: the prompt length the pages measure)."""

@@ -150,6 +150,16 @@ def test_global_lengths_auto_chunks(L):
     check(got, oracle.decode_attention(wl), f"L={L}")
 
 
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_four_streams_9k(fmt):
+    """Four concurrent requests of a 9k-token prompt plus some decoded tokens (ragged
+    lengths, automatic chunking over the batch)."""
+    wl = synth.global_streams(seed=16, fmt=fmt)
+    dev, got = run_case(wl, f"4 streams {fmt} lens={wl.seq_lens.tolist()}")
+    assert dev.plan.num_chunks > 1
+    check(got, oracle.decode_attention(wl), f"4 streams {fmt}")
+
+
 @pytest.mark.parametrize("n", [16, 32, 64])
 def test_global_10602_chunk_counts(n):
     wl = synth.global_decode(10602, seed=1)
