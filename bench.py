@@ -142,16 +142,18 @@ def time_steps(res, steps, warmup, flush=None):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         total_ms = first.elapsed_time(last)
-        ev = [(E(), E()) for _ in range(steps)]
-        for a, b in ev:
+        ev = [(E(), E(), E()) for _ in range(steps)]
+        for a, b, c in ev:
             a.record(stream)
             res.split()
             b.record(stream)
             res.merge()
+            c.record(stream)
         torch.cuda.synchronize()
-        split_ms = [a.elapsed_time(b) for a, b in ev]
+        split_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        each_step_ms = [a.elapsed_time(c) for a, _, c in ev]
         return dict(total_ms=total_ms, wall_s=wall, split_ms=split_ms,
-                    step_ms=[total_ms / steps] * steps)
+                    step_ms=[total_ms / steps] * steps, each_step_ms=each_step_ms)
     step_ms, split_ms = [], []
     for _ in range(steps):
         flush()
@@ -165,6 +167,26 @@ def time_steps(res, steps, warmup, flush=None):
         step_ms.append(a.elapsed_time(c))
         split_ms.append(a.elapsed_time(b))
     return dict(total_ms=sum(step_ms), wall_s=None, split_ms=split_ms, step_ms=step_ms)
+
+
+def time_stream_read(buf, nbytes: int, reps: int = 20) -> float:
+    """Median duration (ms) of the plain streaming read over the first ``nbytes`` of buf:
+    the practical read ceiling beside a decode step over the same bytes."""
+    import torch
+    import paged_split_kv_02_amd as K
+    part = torch.empty(K.STREAM_READ_GROUPS * 4, dtype=torch.int32, device=buf.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        K.attn_stream_read(buf, nbytes, part)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        K.attn_stream_read(buf, nbytes, part)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return median(times)
 
 
 def prefill_flops(wl) -> int:
@@ -210,6 +232,14 @@ def median(xs):
     s = sorted(xs)
     n = len(s)
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def percentile(xs, p):
+    """Linear interpolation between the closest ranks."""
+    s = sorted(xs)
+    x = (len(s) - 1) * p / 100.0
+    i = int(x)
+    return s[i] if i + 1 >= len(s) else s[i] + (s[i + 1] - s[i]) * (x - i)
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -278,6 +308,9 @@ def main():
         del a, b
 
     t = time_steps(res, args.steps, args.warmup)
+    # the plain streaming read over the step's own K/V bytes (the pool's leading pages)
+    read_bytes = wl.kv_bytes() // 16 * 16
+    read_ms = time_stream_read(res.pool, read_bytes)
     ms_per_step = t["total_ms"] / args.steps
     kv = wl.kv_bytes()
     gbs = kv / (ms_per_step * 1e-3) / 1e9
@@ -312,6 +345,15 @@ def main():
                      "traffic": traffic, "kernel": "split_partial_kernel",
                      "kernel_us": round(split_avg_ms * 1e3, 2), "algorithmic_bytes": kb},
         "merge_us": round((ms_per_step - split_avg_ms) * 1e3, 2),
+        "kernel_us_p10_p90": [round(percentile(t["split_ms"], 10) * 1e3, 2),
+                              round(percentile(t["split_ms"], 90) * 1e3, 2)],
+        "step_us_p10_p90": [round(percentile(t["each_step_ms"], 10) * 1e3, 2),
+                            round(percentile(t["each_step_ms"], 90) * 1e3, 2)],
+        "read_ceiling": {"kernel": "attn_stream_read", "bytes": read_bytes,
+                         "us": round(read_ms * 1e3, 2),
+                         "gbs": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
+                         "step_pct_of_ceiling": round(100 * (read_ms / ms_per_step), 2),
+                         "kernel_pct_of_ceiling": round(100 * (read_ms / split_avg_ms), 2)},
     }
     print(f"# step {ms_per_step * 1e3:.1f} us, partial kernel {split_avg_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)

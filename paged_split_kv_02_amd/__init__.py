@@ -17,7 +17,7 @@ __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_p
            "attn_decode_split", "attn_decode_split_tree", "attn_decode_merge",
            "attn_decode_status_string", "make_desc",
            "attn_kv_write", "attn_query_fold", "AttnPrefillPlan", "attn_prefill_plan",
-           "attn_prefill",
+           "attn_prefill", "attn_stream_read", "STREAM_READ_GROUPS",
            "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "ATTN_KV_BF16", "ATTN_KV_F16", "ATTN_KV_FP8_E4M3",
            "ATTN_KV_F32", "STATUS", "LIB_PATH", "SYMBOLS"]
 
@@ -32,7 +32,8 @@ STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
 SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_split_tree", "attn_decode_merge",
            "attn_decode_status_string", "attn_kv_write", "attn_query_fold",
-           "attn_prefill_plan", "attn_prefill")
+           "attn_prefill_plan", "attn_prefill", "attn_stream_read")
+STREAM_READ_GROUPS = 2048  # ATTN_STREAM_READ_GROUPS
 LIB_PATH = _build.LIB
 
 
@@ -98,6 +99,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_prefill_plan.restype = ctypes.c_int
     lib.attn_prefill.argtypes = [ctypes.POINTER(AttnPrefillPlan), P, P, P, P, P, P, P]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.attn_stream_read.restype = ctypes.c_int
     lib.attn_decode_status_string.argtypes = [ctypes.c_int]
     lib.attn_decode_status_string.restype = ctypes.c_char_p
     return lib
@@ -219,6 +222,15 @@ def attn_prefill(plan: AttnPrefillPlan, q, kv_pool, page_table, seq_lens, q_star
                            _ptr(seq_lens), _ptr(q_starts), _ptr(out), _stream(stream))
     if rc != 0:
         raise AttnDecodeError("attn_prefill", rc)
+
+
+def attn_stream_read(buf, nbytes: int, partial, stream=None) -> None:
+    """Measurement aid: read ``nbytes`` of ``buf`` once (the read ceiling a decode step is
+    compared against); ``partial`` (uint32 [STREAM_READ_GROUPS][4]) receives per-workgroup
+    XORs of the 16-byte words read."""
+    rc = _lib.attn_stream_read(_ptr(buf), int(nbytes), _ptr(partial), _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_stream_read", rc)
 
 
 def attn_query_fold(plan: AttnDecodePlan, q, norm_w, q_out, stream=None) -> None:

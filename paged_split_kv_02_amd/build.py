@@ -18,6 +18,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # tile.  The prefill kernel keeps its larger accumulator set in the AGPRs.
 UNITS = [("attn_decode.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
          ("prefill.hip", []),
+         ("stream_read.hip", []),
          ("plan.cpp", [])]
 SOURCES = [os.path.join(CSRC, name) for name, _ in UNITS]
 

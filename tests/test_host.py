@@ -17,7 +17,8 @@ HEADER = os.path.join(ROOT, "include", "attn_decode.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(ROOT, "include", f)).read()
+                   for f in sorted(os.listdir(os.path.join(ROOT, "include"))) if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
 
 
@@ -235,6 +236,18 @@ def test_sliding_chunking_covers_every_window():
         covered = [x for a, b in ranges for x in range(a, b)]
         assert covered == list(range(lo, int(L)))
         assert int(L) - lo == min(int(L), 1024)
+
+
+def test_stream_read_refuses_before_any_launch():
+    fake = 1 << 20  # never dereferenced: every refusal below returns before a launch
+    L = K._lib
+    assert L.attn_stream_read(None, 1024, fake, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_stream_read(fake, 1024, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_stream_read(fake, 1000, fake, None) == S["ATTN_E_INVALID_ARG"]   # not whole words
+    assert L.attn_stream_read(fake + 8, 1024, fake, None) == S["ATTN_E_INVALID_ARG"]  # misaligned
+    assert L.attn_stream_read(fake, 1024, fake + 4, None) == S["ATTN_E_INVALID_ARG"]
+    text = open(os.path.join(ROOT, "include", "attn_measure.h")).read()
+    assert int(re.search(r"#define ATTN_STREAM_READ_GROUPS (\d+)", text).group(1)) == K.STREAM_READ_GROUPS
 
 
 def test_split_and_merge_refuse_before_any_launch():
