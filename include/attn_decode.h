@@ -186,7 +186,8 @@ typedef struct attn_decode_plan_t {
  * above max_pages_per_seq * page_size
  * (ATTN_E_PAST_PAGES, TensorFold PR #1619, body: rows past a slot's pages are
  * refused); a merge_group below ceil(chunks / 8) (ATTN_E_UNSUPPORTED); any size
- * product that overflows, or a grid beyond the launch limits (ATTN_E_OVERFLOW;
+ * product that overflows, a grid beyond the launch limits, or chunks that would end
+ * within 1024 positions of 2^31 (the kernels' key positions are 32-bit) (ATTN_E_OVERFLOW;
  * gem design note, "Candidate ownership and storage": all scratch products are
  * overflow-checked).
  */
@@ -319,7 +320,8 @@ typedef struct attn_prefill_plan_t {
  * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); an f16 or f32 pool or a page size not a
  * multiple of 32 (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
  * more rows than keys in a request (ATTN_E_INVALID_ARG); a length above
- * max_pages_per_seq * page_size (ATTN_E_PAST_PAGES).
+ * max_pages_per_seq * page_size (ATTN_E_PAST_PAGES); a length within 1024 of 2^31, or
+ * more work items than one launch takes (ATTN_E_OVERFLOW).
  */
 int attn_prefill_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host,
                       const int32_t* q_starts_host, attn_prefill_plan_t* plan);

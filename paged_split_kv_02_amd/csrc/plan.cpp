@@ -126,7 +126,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
 
   // Lengths: rows <= L <= pages in a table row * page size.
   const int64_t cap = int64_t(d.max_pages_per_seq) * d.page_size;
-  int64_t max_span = 0;
+  int64_t max_span = 0, max_start = 0;
   for (int r = 0; r < d.batch; ++r) {
     const int64_t L = lens[r];
     if (L < 1 || L < rows) return ATTN_E_INVALID_ARG;
@@ -135,6 +135,7 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
     const int64_t lo = d.window > 0 && first_hi > d.window ? first_hi - d.window : 0;
     const int64_t start = lo / T * T;
     if (L - start > max_span) max_span = L - start;
+    if (start > max_start) max_start = start;
   }
   if (max_span > INT32_MAX) return ATTN_E_OVERFLOW;
 
@@ -174,6 +175,10 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
       n = m;
     }
   }
+  // The kernels address chunk positions in 32 bits: every chunk must end a margin below
+  // 2^31 (chunks are whole tiles, so near that size the rounding alone could cross it).
+  const int64_t cover = (n / 2) * (chunk_len + chunk_len_odd) + (n % 2) * chunk_len;
+  if (max_start + cover > INT32_MAX - kPosMargin) return ATTN_E_OVERFLOW;
   // Launch order of the multi-row kernel: row groups of a chunk 8 workgroups apart.
   const int64_t grid_x = groups > 1 ? ceil_div(n, 8) * 8 * groups : n;
 
@@ -263,6 +268,7 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
     const int64_t L = lens[r];
     if (n < 0 || L < n) return ATTN_E_INVALID_ARG;
     if (L > cap) return ATTN_E_PAST_PAGES;
+    if (L > INT32_MAX - kPosMargin) return ATTN_E_OVERFLOW;  // 32-bit positions in the kernel
     if (n > max_rows) max_rows = n;
   }
   const int64_t total = q_starts[d.batch];

@@ -14,6 +14,9 @@ constexpr int64_t kXcdSkewDiv = 20;    // even/odd chunks: +-1/20 of a quarter's
 constexpr int64_t kTargetWaves = 1024;  // 256 CUs x 4 SIMDs: one chunk-wave per SIMD
 constexpr int kMergeGroups = 8;      // level-1 groups per (request, head) in the merge
 constexpr int64_t kMaxRows = 64;     // query rows per request (multi-row windows)
+// Key positions are 32-bit in the kernels, which add tile and lookahead offsets (at most a
+// few hundred) to them: every position a plan admits stays this far below 2^31.
+constexpr int64_t kPosMargin = 1024;
 constexpr uint64_t kPrefillMagic = 0x4c4c494645525050ull;  // "PPREFILL"
 constexpr int kPrefillKeys = 32;     // keys per prefill tile (one page holds whole tiles)
 constexpr int kPrefillColumns = 64;  // (query row, head) columns per prefill workgroup (x2 at D=256)

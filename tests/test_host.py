@@ -131,6 +131,45 @@ def test_plan_accepts_exact_capacity_and_refuses_one_past():
     assert rc == S["ATTN_E_PAST_PAGES"]
 
 
+def test_positions_near_two_to_the_31_refused():
+    """Key positions are 32-bit in the kernels: a plan whose chunks would end within 1024
+    positions of 2^31 (lengths near it round up to whole tiles) is refused; one a little
+    shorter is accepted and its chunks end below that bound."""
+    big = dict(global_desc(), max_pages_per_seq=(1 << 23) + 4, num_pages=(1 << 23) + 8)
+    for L in (2**31 - 1, 2**31 - 1024):
+        rc, _ = plan_status([L], **big)
+        assert rc == S["ATTN_E_OVERFLOW"], L
+        rc, _ = prefill_status([L], [0, 1], **big)
+        assert rc == S["ATTN_E_OVERFLOW"], L
+    L = 2**31 - 70000
+    rc, p = plan_status([L], **big)
+    assert rc == 0
+    pair = p.chunk_len + p.chunk_len_odd
+    cover = (p.num_chunks // 2) * pair + (p.num_chunks % 2) * p.chunk_len
+    assert L <= cover <= 2**31 - 1 - 1024
+    rc, _ = prefill_status([L], [0, 1], **big)
+    assert rc == 0
+
+
+def test_plan_fuzz_under_sanitizers(tmp_path):
+    """Host-side fuzz of the planning calls built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (g++, host code only): 200,000 seeded descriptors from
+    valid shapes with up to two hostile fields, invariants of every accepted plan."""
+    exe = tmp_path / "plan_fuzz"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+                    os.path.join(ROOT, "paged_split_kv_02_amd", "csrc", "plan.cpp"),
+                    os.path.join(ROOT, "tests", "host", "plan_fuzz.cpp"), "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr, res.stderr
+    m = re.search(r"(\d+) decode plans accepted, (\d+) refused, (\d+) prefill plans accepted", res.stdout)
+    assert m and int(m.group(1)) > 10000 and int(m.group(2)) > 10000 and int(m.group(3)) > 10000, res.stdout
+
+
 def test_null_pointers_refused():
     d = K.make_desc(**global_desc())
     p = K.AttnDecodePlan()
