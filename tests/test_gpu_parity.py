@@ -150,6 +150,15 @@ def test_global_lengths_auto_chunks(L):
     check(got, oracle.decode_attention(wl), f"L={L}")
 
 
+@pytest.mark.parametrize("L", [8191, 8192, 8193, 65536, 131072])
+def test_boundary_lengths(L):
+    """The five live lengths of the gem design note's audit (opening status section): one
+    below, at and one above 8192, and 65536 and 131072; automatic chunks."""
+    wl = synth.global_decode(L, seed=17)
+    _, got = run_case(wl, f"boundary length L={L}")
+    check(got, oracle.decode_attention(wl), f"L={L}")
+
+
 @pytest.mark.parametrize("fmt", ["split", "folded"])
 def test_four_streams_9k(fmt):
     """Four concurrent requests of a 9k-token prompt plus some decoded tokens (ragged
