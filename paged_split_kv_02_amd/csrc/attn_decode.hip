@@ -1149,6 +1149,7 @@ int split_launch(const attn_decode_plan_t* plan, const float* q, const void* kv_
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!q || !kv_pool || !page_table || !seq_lens) return ATTN_E_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pool)) return ATTN_E_INVALID_ARG;
   rc = check_workspace(plan, workspace, workspace_bytes);
   if (rc != ATTN_OK) return rc;
   const attn_decode_desc& d = plan->desc;
@@ -1225,7 +1226,7 @@ extern "C" int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace
   using namespace attn;
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
-  if (!out) return ATTN_E_INVALID_ARG;
+  if (!out || !aligned16(out)) return ATTN_E_INVALID_ARG;
   rc = check_workspace(plan, workspace, workspace_bytes);
   if (rc != ATTN_OK) return rc;
   if (!shape_supported(plan->desc)) return ATTN_E_UNSUPPORTED;
@@ -1245,6 +1246,7 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!k || !v || !start_pos || !kv_pool || !page_table || num_new < 1) return ATTN_E_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kv_pool)) return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
   if (d.kv_dtype != ATTN_KV_BF16) return ATTN_E_UNSUPPORTED;
   const int kcols = d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim;
@@ -1284,6 +1286,7 @@ extern "C" int attn_query_fold(const attn_decode_plan_t* plan, const float* q, c
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!q || !norm_w || !q_out) return ATTN_E_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(norm_w) || !aligned16(q_out)) return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
   if (d.format != ATTN_KV_FOLDED) return ATTN_E_UNSUPPORTED;
   const int64_t quads = int64_t(d.batch) * d.num_q_heads * d.head_dim / 4;

@@ -45,4 +45,7 @@ void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* 
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 
+// Device buffers the kernels move in 16-byte vectors (query, pool, output, K/V rows).
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 }  // namespace attn

@@ -310,6 +310,13 @@ def test_split_and_merge_refuse_before_any_launch():
     assert L.attn_kv_write(ctypes.byref(p), None, fake, 1, fake, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
     assert L.attn_query_fold(ctypes.byref(p), fake, fake, fake, None) == S["ATTN_E_UNSUPPORTED"]  # split plan
     assert L.attn_query_fold(ctypes.byref(bad), fake, fake, fake, None) == S["ATTN_E_PLAN"]
+    # buffers the kernels move in 16-byte vectors must be 16-byte aligned
+    mis = fake + 4
+    assert L.attn_decode_split(ctypes.byref(p), mis, fake, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_decode_split(ctypes.byref(p), fake, mis, fake, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_decode_merge(ctypes.byref(p), fake, ws, mis, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_kv_write(ctypes.byref(p), mis, fake, 1, fake, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_kv_write(ctypes.byref(p), fake, fake, 1, fake, mis, fake, None, None) == S["ATTN_E_INVALID_ARG"]
 
 
 def test_tree_split_refuses_before_any_launch():
@@ -467,6 +474,10 @@ def test_prefill_refuses_before_any_launch():
     for k in range(6):
         args = [fake] * 6
         args[k] = None
+        assert L.attn_prefill(ctypes.byref(p), *args, None) == S["ATTN_E_INVALID_ARG"], k
+    for k in (0, 1, 5):  # q, pool and out move in 16-byte vectors
+        args = [fake] * 6
+        args[k] = fake + 4
         assert L.attn_prefill(ctypes.byref(p), *args, None) == S["ATTN_E_INVALID_ARG"], k
     # a decode plan is not a prefill plan
     rc, dp = plan_status([1024], **global_desc())
