@@ -25,7 +25,8 @@
  * Ownership: the caller owns every buffer (query, pool, page table, lengths,
  * workspace, output).  Buffers of floats or pool rows (q, kv_pool, out, the K/V rows of
  * attn_kv_write, attn_query_fold's q, norm_w and q_out) must be 16-byte aligned (the
- * kernels move them in 16-byte vectors); the workspace 256-byte aligned.  The library allocates nothing, keeps no mutable global
+ * kernels move them in 16-byte vectors); the workspace 256-byte aligned; int32 and uint64
+ * arrays (page table, lengths, offsets, masks) to their element size.  The library allocates nothing, keeps no mutable global
  * state and is reentrant.  Launches are asynchronous; buffers must stay alive
  * until the stream has run them.  A plan is plain old data and may be copied.
  * The enqueuing calls neither synchronise nor allocate nor record memsets, and a

@@ -1149,7 +1149,9 @@ int split_launch(const attn_decode_plan_t* plan, const float* q, const void* kv_
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!q || !kv_pool || !page_table || !seq_lens) return ATTN_E_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kv_pool)) return ATTN_E_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned_to(page_table, 4) || !aligned_to(seq_lens, 4) ||
+      !aligned_to(row_masks, 8))
+    return ATTN_E_INVALID_ARG;
   rc = check_workspace(plan, workspace, workspace_bytes);
   if (rc != ATTN_OK) return rc;
   const attn_decode_desc& d = plan->desc;
@@ -1246,7 +1248,9 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
   int rc = check_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!k || !v || !start_pos || !kv_pool || !page_table || num_new < 1) return ATTN_E_INVALID_ARG;
-  if (!aligned16(k) || !aligned16(v) || !aligned16(kv_pool)) return ATTN_E_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kv_pool) || !aligned_to(start_pos, 4) ||
+      !aligned_to(page_table, 4) || !aligned_to(bad_rows, 4))
+    return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
   if (d.kv_dtype != ATTN_KV_BF16) return ATTN_E_UNSUPPORTED;
   const int kcols = d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim;

@@ -45,7 +45,9 @@ void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* 
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 
-// Device buffers the kernels move in 16-byte vectors (query, pool, output, K/V rows).
+// Device buffers the kernels move in 16-byte vectors (query, pool, output, K/V rows), and
+// the natural alignment of the 4- and 8-byte words they read (table, lengths, masks).
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
 }  // namespace attn

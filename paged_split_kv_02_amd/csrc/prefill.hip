@@ -777,7 +777,9 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
   int rc = check_prefill_plan(plan);
   if (rc != ATTN_OK) return rc;
   if (!q || !kv_pool || !page_table || !seq_lens || !q_starts || !out) return ATTN_E_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out)) return ATTN_E_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned_to(page_table, 4) ||
+      !aligned_to(seq_lens, 4) || !aligned_to(q_starts, 4))
+    return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
   if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
   if (plan->total_rows == 0) return ATTN_OK;

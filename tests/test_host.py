@@ -317,6 +317,10 @@ def test_split_and_merge_refuse_before_any_launch():
     assert L.attn_decode_merge(ctypes.byref(p), fake, ws, mis, None) == S["ATTN_E_INVALID_ARG"]
     assert L.attn_kv_write(ctypes.byref(p), mis, fake, 1, fake, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
     assert L.attn_kv_write(ctypes.byref(p), fake, fake, 1, fake, mis, fake, None, None) == S["ATTN_E_INVALID_ARG"]
+    odd = fake + 2  # int32 arrays at their element size
+    assert L.attn_decode_split(ctypes.byref(p), fake, fake, odd, fake, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_decode_split(ctypes.byref(p), fake, fake, fake, odd, fake, ws, None) == S["ATTN_E_INVALID_ARG"]
+    assert L.attn_kv_write(ctypes.byref(p), fake, fake, 1, odd, fake, fake, None, None) == S["ATTN_E_INVALID_ARG"]
 
 
 def test_tree_split_refuses_before_any_launch():
