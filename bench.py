@@ -242,15 +242,30 @@ def percentile(xs, p):
     return s[i] if i + 1 >= len(s) else s[i] + (s[i + 1] - s[i]) * (x - i)
 
 
-def cpu_baseline(wl, budget_s=10.0):
+def cpu_baseline(wl, budget_s=10.0, single_s=5.0):
     """Time the fp64 oracle on the host over the same step, repeated until the budget
-    is spent (KV heads one after another, at least one); GB/s of K/V rows consumed."""
+    is spent (KV heads one after another, at least one); GB/s of K/V rows consumed.
+    Then the same with the numeric library held to one thread (``single_thread``)."""
+    from threadpoolctl import threadpool_limits
+    out = _oracle_rate(wl, budget_s)
+    with threadpool_limits(limits=1):
+        one = _oracle_rate(wl, single_s)
+    out["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample", "seconds",
+                                                 "us_per_step_equiv")}
+    return out
+
+
+def _oracle_rate(wl, budget_s):
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
     G = wl.num_q_heads // wl.num_kv_heads
     done_heads = 0
     total_heads = wl.batch * wl.num_kv_heads
+    # one untimed pass first (first touches of the host arrays, library start-up)
+    lo, L = oracle.visible_range(int(wl.seq_lens[0]), wl.window)
+    Kx, Vx = oracle.keys_values(wl, oracle.bf16_bits_to_f64(oracle.gather_rows(wl, 0, 0, np.arange(lo, L))))
+    oracle.dense_attention(wl.q[0, 0:G], Kx, Vx, wl.scale)
     t0 = time.perf_counter()
     while True:
         for r in range(wl.batch):
