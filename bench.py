@@ -399,6 +399,9 @@ def main():
                  lambda: synth.set_tree(synth.make_workload([163336], **synth.GLOBAL, seed=6,
                                                             num_rows=4, spare_pages=1),
                                         np.array([[-1, 0, 0, 1]], dtype=np.int32)), 20),
+                ("global-decode-163336-split-fp8e4m3-4rows",
+                 lambda: synth.make_workload([163336], **synth.GLOBAL, seed=7, num_rows=4,
+                                             kv_dtype=synth.FP8, spare_pages=1), 20),
                 ("global-decode-163336-split-fp8e4m3",
                  lambda: synth.global_decode(163336, seed=7, kv_dtype=synth.FP8), 20),
                 ("global-decode-163336-folded-fp8e4m3",
