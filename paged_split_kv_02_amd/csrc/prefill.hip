@@ -218,6 +218,7 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char buf0[S::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char buf1[S::TILE_BYTES];
   __shared__ floatx4 xs[W][4][64];  // partial scores, one slot per wave
+  __shared__ floatx4 ys[SPLIT == 4 ? W : 1][64];  // four-way exchange: summed score groups
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 31;   // MFMA column: (row, head) of the block / key row of a K fragment
@@ -497,21 +498,23 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i)  // (IEEE addition commutes: the same sum in both waves)
           sc[4 * e4 + i] = sp[4 * e4 + i] + other[e4][i];
     } else if constexpr (SPLIT == 4) {
-      // Add the four quarters as (q0 + q1) + (q2 + q3), all read back from LDS: every wave
-      // of the block evaluates the same expression and holds the same scores bit for bit.
+      // Reduce-scatter, then all-gather, through LDS: wave `half` adds score group `half`
+      // of the four quarters as (q0 + q1) + (q2 + q3) and publishes it; every wave then
+      // reads the four sums, so all hold the same scores bit for bit (and each wave reads
+      // 8 KB per tile instead of all 16 KB of partials).
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         xs[wave][e][lane] = floatx4{sp[4 * e], sp[4 * e + 1], sp[4 * e + 2], sp[4 * e + 3]};
       __syncthreads();
       const int w0 = block * SPLIT;
-      floatx4 x[4][4];  // all reads issued before the first add
+      floatx4 x[4];  // all reads issued before the first add
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u][e4] = xs[w0 + u][e4][lane];
+      for (int u = 0; u < 4; ++u) x[u] = xs[w0 + u][half][lane];
+      ys[wave][lane] = (x[0] + x[1]) + (x[2] + x[3]);
+      __syncthreads();
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const floatx4 y = (x[0][e4] + x[1][e4]) + (x[2][e4] + x[3][e4]);
+        const floatx4 y = ys[w0 + e4][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[4 * e4 + i] = y[i];
       }
