@@ -570,15 +570,41 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
 // ---------------------------------------------------------------------------------------
 // FP32 pools (the KV type of the gem design note's "Fixed production shape"): products in
 // full fp32 on v_mfma_f32_16x16x4_f32, so nothing is split into parts.  A wave copies the
-// K half of a 16-key tile of whole rows into its own LDS region with 16-byte global->LDS
-// loads (no registers carry them), forms the scores, then copies the V half into the same
-// region.  Each wave works alone until the workgroup merge of the quarter states.
+// K half, then the V half, of a 16-key tile of whole rows into its own LDS region with
+// non-temporal 16-byte global->LDS loads (no registers carry them); at head dim 512
+// through a ring of eight slots, seven pieces in flight while it computes on the eighth.
+// Each wave works alone until the workgroup merge of the quarter states.
 //   A (16 x 4): lane l holds A[l % 16][l / 16];  B (4 x 16): B[l / 16][l % 16];
 //   C (16 x 16): element i of lane l is C[4(l / 16) + i][l % 16].
 typedef __attribute__((address_space(3))) void lds_void;
+// Cache policy of the rows' global->LDS loads: non-temporal, as for the streaming loads of
+// the other decode kernels (each row is read once per launch).  With the default policy
+// the f32 kernel streamed at ~5.1 TB/s at 163,336 tokens and ~3.1 TB/s on the sliding
+// batch; non-temporal, ~6.4 and ~5.4 TB/s.
+constexpr int kStreamLds = 2;
 
 __device__ __forceinline__ floatx4 mma_f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// A compile-time int for the loop bounds of the per-tile lambdas.
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_lt() {
+  static_assert(N >= 0 && N <= 28 && N % 4 == 0, "counts of whole 4-load pieces");
+  if constexpr (N == 28) asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int D>
@@ -590,6 +616,19 @@ struct F32Shape {
   static constexpr int QSTEPS = D / 16;           // 16-dim groups of QK (4 MFMA steps each)
   static constexpr int VBLOCKS = D / 64;          // 64-dim blocks of PV
   static_assert(HALF_BYTES % 1024 == 0, "whole kilobytes per row half");
+};
+
+// The head-dim-512 ring of the f32 kernel: each half (K or V) of a staged row streams in
+// NP pieces of PW bytes; one load instruction brings RPI rows of a piece.
+template <int D>
+struct F32Ring {
+  static constexpr int NP = 8;                                // pieces per row half
+  static constexpr int PW = F32Shape<D>::HALF_BYTES / NP;     // bytes of a row per piece
+  static constexpr int CH = PW / 16;                          // 16-byte chunks of a row per piece
+  static constexpr int RPI = 1024 / PW;                       // rows per load instruction
+  static constexpr int IPP = kTile / RPI;                     // load instructions per piece
+  static constexpr int SLOT = kTile * PW;                     // LDS bytes per slot
+  static constexpr int AHEAD = NP - 1;                        // pieces in flight behind the one in use
 };
 
 template <int D, int G>
@@ -635,20 +674,6 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
     }
   }
 
-  // Copy the K (part 0) or V (part 1) half of the tile's 16 rows: instruction (row, k)
-  // brings one kilobyte of the row, lane l its 16-byte chunk 64k + l.
-  auto stage = [&](int32_t pid, int tok0, int part) {
-    const char* base = head_base + int64_t(pid) * a.page_stride +
-                       int64_t(tok0 % a.page_size) * a.row_stride + (part ? a.v_offset : a.k_offset) +
-                       16 * lane;
-#pragma unroll
-    for (int row = 0; row < kTile; ++row)
-#pragma unroll
-      for (int k = 0; k < S::LOADS; ++k)
-        __builtin_amdgcn_global_load_lds(base + int64_t(row) * a.row_stride + 1024 * k,
-                                         (lds_void*)(lds + row * S::PITCH + 1024 * k), 16, 0, 0);
-  };
-
   float m_run = -INFINITY;
   float l_run = 0.0f;
   floatx4 acc[S::VBLOCKS][4];  // block b, step jj: lane (c, qg) element i <-> dim 64b + 4(4qg+i) + jj
@@ -656,30 +681,23 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   for (int b = 0; b < S::VBLOCKS; ++b)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 sj[4];  // score chains (step j) of the current tile
+  float p[4];     // probabilities of keys tok0 + 4qg + i for head c
 
-  if (c0 < end) pw.start(c0);
-  for (int tok0 = c0; tok0 < end; tok0 += kTile) {
-    const int32_t pid = pw.page_of(tok0);
-    if (pid < 0) {  // a table entry outside the pool poisons the quarter
-      poison = true;
-      break;
-    }
-    stage(pid, tok0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // Scores of keys tok0 + 4qg + i for head c: four independent chains (step j).
-    floatx4 sj[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                     {0.f, 0.f, 0.f, 0.f}};
+  // Scores of keys tok0 + 4qg + i for head c over 16-dim groups [S0, S1): four
+  // independent chains (step j), summed by the softmax.
+  auto qk = [&](auto s_begin, auto s_end) {
 #pragma unroll
-    for (int s = 0; s < S::QSTEPS; ++s) {
+    for (int s = decltype(s_begin)::value; s < decltype(s_end)::value; ++s) {
       const floatx4 kv = *reinterpret_cast<const floatx4*>(lds + c * S::PITCH + 64 * s + 16 * qg);
       const floatx4 qq = qv[s];
 #pragma unroll
       for (int j = 0; j < 4; ++j) sj[j] = mma_f32(kv[j], qq[j], sj[j]);
     }
+  };
+  // Online softmax (base 2), masked keys by select, lazy rescale as in the bf16 kernel.
+  auto softmax = [&](int tok0) {
     const floatx4 sc4 = (sj[0] + sj[1]) + (sj[2] + sj[3]);
-
-    // Online softmax (base 2), masked keys by select, lazy rescale as in the bf16 kernel.
     float sc[4];
     float mx = -INFINITY;
 #pragma unroll
@@ -701,21 +719,20 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
         for (int jj = 0; jj < 4; ++jj) acc[b][jj] *= alpha;
       m_run = m_new;
     }
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = 0.0f;
     if (m_run != -INFINITY) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
     }
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
-
-    // V half into the same region (the K reads above have all returned: they fed the
-    // scores), then PV.  MFMA t takes keys 4qg + t, so lane (c, qg) supplies its own p[t]
-    // as B; A = V^T: lane (m, qg) holds dims 64b + 4m + jj of key 4qg + t.
-    stage(pid, tok0, 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  // PV over 64-dim blocks [B0, B1).  MFMA t takes keys 4qg + t, so lane (c, qg) supplies
+  // its own p[t] as B; A = V^T: lane (m, qg) holds dims 64b + 4m + jj of key 4qg + t.
+  auto pv = [&](int tok0, auto b_begin, auto b_end) {
     const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
 #pragma unroll
-    for (int b = 0; b < S::VBLOCKS; ++b)
+    for (int b = decltype(b_begin)::value; b < decltype(b_end)::value; ++b)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kr = 4 * qg + t;
@@ -727,6 +744,154 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[b][jj] = mma_f32(vv[jj], p[t], acc[b][jj]);
       }
+  };
+  auto clear_scores = [&] {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sj[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  if constexpr (S::LOADS == 2) {
+    // Head dim 512: the tile's K half, then its V half, streams through a ring of eight
+    // 4 KB LDS slots in pieces of 256 bytes per row (64 dims of the 16 rows), seven pieces
+    // in flight while the wave computes on the eighth: piece j of a tile (K pieces 0-7,
+    // then V pieces 0-7) goes to slot j % 8, and phase j first requests piece j + 7 (of the
+    // next tile from phase 9 on) into the slot that phase j - 1 has finished reading, then
+    // waits only for piece j.  One load instruction brings four rows' 256 bytes; within a
+    // row, 16-byte chunk x sits at position x ^ row, so the score reads (16 rows, one chunk
+    // each) and the PV reads (one row, 16 chunks) both touch distinct banks, and each
+    // aligned group of eight lanes still fetches one whole 128-byte line.
+    using R = F32Ring<D>;
+    static_assert(R::PW == 256 && R::CH == kTile && R::NP * R::SLOT <= S::REGION, "ring of 4 KB slots");
+    static_assert(R::AHEAD * R::IPP <= 63, "outstanding loads fit the counter");
+    static_assert(S::QSTEPS == 4 * R::NP && S::VBLOCKS == R::NP, "one piece = 4 score steps = 1 PV block");
+
+    // Lane l of load instruction i fetches row R::RPI*i + l / R::CH, chunk (l % R::CH) ^ row.
+    auto issue = [&](int32_t pid, int tok0, int j) {  // piece j (0-15) of the tile at tok0
+      const char* base = head_base + int64_t(pid) * a.page_stride +
+                         int64_t(tok0 % a.page_size) * a.row_stride +
+                         (j >= R::NP ? a.v_offset : a.k_offset) + R::PW * (j % R::NP);
+      char* dst = lds + R::SLOT * (j % R::NP);
+#pragma unroll
+      for (int i = 0; i < R::IPP; ++i) {
+        const int row = R::RPI * i + lane / R::CH;
+        const int64_t off = int64_t(row) * a.row_stride + 16 * ((lane % R::CH) ^ row);
+        __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + 1024 * i), 16, 0, kStreamLds);
+      }
+    };
+    auto reads_done = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+
+    auto phase = [&](auto jc, int32_t pid, int tok0, int32_t npid, int next, bool more) {
+      constexpr int J = decltype(jc)::value;
+      reads_done();
+      if constexpr (J + R::AHEAD < 2 * R::NP) {
+        issue(pid, tok0, J + R::AHEAD);
+      } else {
+        if (more) issue(npid, next, J + R::AHEAD - 2 * R::NP);
+      }
+      // Wait for piece J: the loads issued after it may stay in flight.
+      if constexpr (J + R::AHEAD < 2 * R::NP) {
+        vm_wait_lt<R::AHEAD * R::IPP>();
+      } else {
+        if (more)
+          vm_wait_lt<R::AHEAD * R::IPP>();
+        else
+          vm_wait_lt<(2 * R::NP - 1 - J) * R::IPP>();
+      }
+      const char* slot = lds + R::SLOT * (J % R::NP);
+      if constexpr (J < R::NP) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int x = 4 * sl + qg;
+          const floatx4 kv = *reinterpret_cast<const floatx4*>(slot + R::PW * c + 16 * (x ^ c));
+          const floatx4 qq = qv[4 * J + sl];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) sj[jj] = mma_f32(kv[jj], qq[jj], sj[jj]);
+        }
+        if constexpr (J == R::NP - 1) softmax(tok0);
+      } else {
+        constexpr int B = J - R::NP;
+        const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kr = 4 * qg + t;
+          floatx4 vv = *reinterpret_cast<const floatx4*>(slot + R::PW * kr + 16 * (c ^ kr));
+          if (__builtin_expect(edge, 0)) {
+            const int key = tok0 + kr;
+            if (key < lo || key >= L) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[B][jj] = mma_f32(vv[jj], p[t], acc[B][jj]);
+        }
+      }
+    };
+    int32_t pid = -1;
+    if (c0 < end) {
+      pw.start(c0);
+      pid = pw.page_of(c0);
+      if (pid < 0) {  // a table entry outside the pool poisons the quarter
+        poison = true;
+      } else {
+#pragma unroll
+        for (int j = 0; j < R::AHEAD; ++j) issue(pid, c0, j);
+      }
+    }
+    for (int tok0 = c0; pid >= 0 && tok0 < end; tok0 += kTile) {
+      const int next = tok0 + kTile;
+      const int32_t npid = next < end ? pw.page_of(next) : -1;
+      const bool more = npid >= 0;  // uniform
+      if (next < end && !more) poison = true;
+      clear_scores();
+      phase(Int<0>{}, pid, tok0, npid, next, more);
+      phase(Int<1>{}, pid, tok0, npid, next, more);
+      phase(Int<2>{}, pid, tok0, npid, next, more);
+      phase(Int<3>{}, pid, tok0, npid, next, more);
+      phase(Int<4>{}, pid, tok0, npid, next, more);
+      phase(Int<5>{}, pid, tok0, npid, next, more);
+      phase(Int<6>{}, pid, tok0, npid, next, more);
+      phase(Int<7>{}, pid, tok0, npid, next, more);
+      phase(Int<8>{}, pid, tok0, npid, next, more);
+      phase(Int<9>{}, pid, tok0, npid, next, more);
+      phase(Int<10>{}, pid, tok0, npid, next, more);
+      phase(Int<11>{}, pid, tok0, npid, next, more);
+      phase(Int<12>{}, pid, tok0, npid, next, more);
+      phase(Int<13>{}, pid, tok0, npid, next, more);
+      phase(Int<14>{}, pid, tok0, npid, next, more);
+      phase(Int<15>{}, pid, tok0, npid, next, more);
+      pid = npid;
+    }
+  } else {
+    // Head dim 256: a row half is one kilobyte, so the K half is staged whole, then the V
+    // half into the same region: instruction (row, k) brings one kilobyte of the row, lane
+    // l its 16-byte chunk 64k + l.
+    auto stage = [&](int32_t pid, int tok0, int part) {
+      const char* base = head_base + int64_t(pid) * a.page_stride +
+                         int64_t(tok0 % a.page_size) * a.row_stride + (part ? a.v_offset : a.k_offset) +
+                         16 * lane;
+#pragma unroll
+      for (int row = 0; row < kTile; ++row)
+#pragma unroll
+        for (int k = 0; k < S::LOADS; ++k)
+          __builtin_amdgcn_global_load_lds(base + int64_t(row) * a.row_stride + 1024 * k,
+                                           (lds_void*)(lds + row * S::PITCH + 1024 * k), 16, 0, kStreamLds);
+    };
+    if (c0 < end) pw.start(c0);
+    for (int tok0 = c0; tok0 < end; tok0 += kTile) {
+      const int32_t pid = pw.page_of(tok0);
+      if (pid < 0) {  // a table entry outside the pool poisons the quarter
+        poison = true;
+        break;
+      }
+      stage(pid, tok0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      clear_scores();
+      qk(Int<0>{}, Int<S::QSTEPS>{});
+      softmax(tok0);
+      // V half into the same region (the K reads above have all returned: they fed the
+      // scores), then PV.
+      stage(pid, tok0, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      pv(tok0, Int<0>{}, Int<S::VBLOCKS>{});
+    }
   }
 
   // Quarter state: sum l over the lane groups; park (m, l, O) for the workgroup merge.
