@@ -291,7 +291,21 @@ def _oracle_rate(wl, budget_s):
                       f"same {wl.seq_lens[0]}-token step, fp64 numpy oracle, {dt:.1f} s wall",
             "seconds": round(dt, 2),
             "us_per_step_equiv": round(dt / done_heads * total_heads * 1e6, 1),
-            "host_cpu": platform.processor() or platform.machine(), "host_nproc": os.cpu_count()}
+            "cores_note": "threads of the numeric library (the score and output products); "
+                          "the row gather and the bf16 widening run on one thread",
+            "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
@@ -323,6 +337,12 @@ def main():
         del a, b
 
     t = time_steps(res, args.steps, args.warmup)
+    # the same step, each one after an untimed 1 GiB write that evicts the caches
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+
+    def flush():
+        flush_buf.zero_()  # 1 GiB of writes evicts the 256 MB infinity cache
+    tf = time_steps(res, args.steps, 2, flush=flush)
     # the plain streaming read over the step's own K/V bytes (the pool's leading pages)
     read_bytes = wl.kv_bytes() // 16 * 16
     read_ms = time_stream_read(res.pool, read_bytes)
@@ -345,6 +365,10 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "us_per_step_median": round(median(t["step_ms"]) * 1e3, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "flushed": {"us_per_step_median": round(median(tf["step_ms"]) * 1e3, 2),
+                    "partial_kernel_us_median": round(median(tf["split_ms"]) * 1e3, 2),
+                    "effective_gbs": round(kv / (median(tf["step_ms"]) * 1e-3) / 1e9, 1),
+                    "timing": f"median of {args.steps} steps, each after an untimed 1 GiB write"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -376,11 +400,6 @@ def main():
 
     if not args.no_variants:
         variants = {}
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
-
-        def flush():
-            flush_buf.zero_()  # 1 GiB of writes evicts the 256 MB infinity cache
-
         pick = [x for x in args.variants.split(",") if x]
 
         def wanted(name):
@@ -487,7 +506,7 @@ def main():
                   flush=True)
             del pwl
         line["variants"] = variants
-        del flush_buf
+    del flush_buf
 
     if not args.no_cpu_baseline:
         print("# timing the fp64 oracle on the host", file=sys.stderr, flush=True)

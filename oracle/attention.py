@@ -68,7 +68,7 @@ __all__ = [
     "f32_bits_to_f64", "stored_to_f64", "visible_range", "row_view", "gather_rows",
     "keys_values", "dense_attention", "decode_attention", "window_row_positions",
     "partial_state", "empty_state",
-    "merge", "finalize", "split_kv_attention", "paged_partials", "validate",
+    "merge", "finalize", "fold", "split_kv_attention", "paged_partials", "validate",
     "prefill_attention", "prefill_row_index",
 ]
 

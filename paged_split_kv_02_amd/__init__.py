@@ -77,7 +77,9 @@ class AttnDecodeError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+    # A library missing, or built from other sources than those in the tree, is rebuilt
+    # first: a stale library is never loaded.
+    if not _build.is_current():
         _build.build()
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
@@ -156,6 +158,8 @@ def attn_decode_plan(desc: AttnDecodeDesc, seq_lens_host) -> AttnDecodePlan:
     """Validate and plan; ``seq_lens_host`` is a host int32 array (numpy) of length batch."""
     import numpy as np
     lens = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+    if lens.ndim != 1 or lens.size != desc.batch:
+        raise ValueError("seq_lens needs batch entries")
     plan = AttnDecodePlan()
     rc = _lib.attn_decode_plan(ctypes.byref(desc), lens.ctypes.data, ctypes.byref(plan))
     if rc != 0:

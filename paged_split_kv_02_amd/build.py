@@ -21,6 +21,38 @@ UNITS = [("attn_decode.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
          ("stream_read.hip", []),
          ("plan.cpp", [])]
 SOURCES = [os.path.join(CSRC, name) for name, _ in UNITS]
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+# Digest of the sources a library was built from, written beside it by build().
+DIGEST = LIB + ".digest"
+
+
+def source_digest() -> str:
+    """SHA-256 over the library's sources, headers, build flags and this script."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)) + \
+        sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)) + [os.path.abspath(__file__)]
+    for path in files:
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode() + b"\0")
+            with open(path, "rb") as f:
+                h.update(f.read())
+    h.update(repr((COMMON, UNITS)).encode())
+    return h.hexdigest()
+
+
+def built_digest() -> str | None:
+    """Digest recorded for the library on disk (None if there is none)."""
+    try:
+        with open(DIGEST) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def is_current() -> bool:
+    """True if the library exists and was built from the sources as they are now."""
+    return os.path.exists(LIB) and built_digest() == source_digest()
 
 
 def hipcc() -> str:
@@ -33,6 +65,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile the library; always recompiles.  Returns the path of the .so."""
     cc = hipcc()
+    digest = source_digest()
     with tempfile.TemporaryDirectory(prefix="attn_build.") as tmpdir:
         objs = []
         for name, extra in UNITS:
@@ -47,6 +80,9 @@ def build(verbose: bool = False) -> str:
             os.unlink(tmp)
             raise
         os.replace(tmp, LIB)
+    with open(DIGEST + ".tmp", "w") as f:
+        f.write(digest + "\n")
+    os.replace(DIGEST + ".tmp", DIGEST)
     return LIB
 
 

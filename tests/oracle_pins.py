@@ -662,10 +662,99 @@ def pin_tree_brute_force():
     assert np.array_equal(np.delete(got, 2, axis=1), np.delete(ref, 2, axis=1))
 
 
+def brute_force_chunk_state(wl, r: int, g: int, h: int, row: int, a: int, b: int):
+    """(m, l, acc) of query head h (query row ``row`` of request r) over the keys of
+    positions [a, b) that the row sees, by pure Python; None when it sees none there.
+
+    Row i of an n-row window over L keys is the token at position p = L - n + i; it sees
+    every position j <= p, and with a window W only those with j > p - W.  Scores by
+    fsum of explicit products over flat pool indices; m is their maximum, l the fsum of
+    e^(s - m), acc the fsum of e^(s - m) v per dimension.
+    """
+    D = wl.head_dim
+    n = getattr(wl, "num_rows", 1)
+    elem = _ELEMENT[wl.kv_dtype]
+    ks, vs = wl.k_scale, wl.v_scale
+    p = int(wl.seq_lens[r]) - n + row
+    qh = [float(x) for x in (wl.q[r, row, h] if n > 1 else wl.q[r, h])]
+    scores, vals = [], []
+    for j in range(a, b):
+        if j < 0 or j > p or (wl.window and j <= p - wl.window):
+            continue
+        pg = int(wl.table[r][j // wl.page_size])
+        base = pg * wl.page_stride + g * wl.head_stride + (j % wl.page_size) * wl.row_stride
+        rowv = [elem(wl.pool[base + c]) for c in range(wl.row_cols)]
+        v = [x * vs for x in rowv[wl.v_offset:wl.v_offset + D]]
+        if wl.fmt == "split":
+            k = [x * ks for x in rowv[wl.k_offset:wl.k_offset + D]]
+        else:
+            k = [x * ks for x in rowv[wl.k_offset:wl.k_offset + wl.rot_cols]] + v[wl.rot_cols:]
+        scores.append(wl.scale * math.fsum(qh[d] * k[d] for d in range(D)))
+        vals.append(v)
+    if not scores:
+        return None
+    m = max(scores)
+    e = [math.exp(s - m) for s in scores]
+    return m, math.fsum(e), [math.fsum(e[t] * vals[t][d] for t in range(len(e))) for d in range(D)]
+
+
+# (seq_lens, Hq, Hkv, D, page_size, window, fmt, rows, kv_dtype)
+PARTIAL_CASES = [
+    ([37, 20, 5], 8, 2, 17, 4, 0, "split", 1, "bf16"),     # whole context, ragged
+    ([37, 9, 23], 4, 2, 17, 4, 6, "split", 1, "bf16"),      # window crossing chunks
+    ([30, 12], 4, 1, 17, 4, 0, "split", 4, "bf16"),         # each row of a 4-row window
+    ([30, 14], 4, 2, 17, 4, 5, "split", 3, "bf16"),         # rows and a window
+    ([21], 8, 1, 512, 4, 0, "folded", 2, "bf16"),           # folded row, two rows
+    ([26, 11], 4, 2, 33, 4, 7, "split", 2, "fp8_e4m3"),     # FP8 with its factors
+]
+
+
+def pin_paged_partials():
+    """Per-chunk states of the paged pool (the states every per-chunk GPU check compares
+    against) == a pure-Python state of the keys each chunk and row sees: random cut
+    points, chunks wholly before the window or past the length (empty), zero-width
+    chunks, every query row of a multi-row window, a window, folded rows, FP8 factors.
+    The states of a chunking that covers every key, folded in order, give the pinned
+    decode output (gem design note, opening status section: partitions with empty
+    members merge to the direct softmax)."""
+    rng = _rng(50)
+    for k, (lens, hq, hkv, D, ps, W, fmt, n, dt) in enumerate(PARTIAL_CASES):
+        wl = synth.make_workload(lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=ps,
+                                 window=W, fmt=fmt, seed=60 + k, num_rows=n, kv_dtype=dt,
+                                 pad="nan", spare_pages=2)
+        G = hq // hkv
+        dense = oracle.decode_attention(wl)
+        for r, L in enumerate(lens):
+            inner = sorted(int(x) for x in rng.integers(0, L + 1, size=4))
+            cuts = [-ps, 0] + inner + [L, L + 2 * ps]
+            ranges = list(zip(cuts[:-1], cuts[1:])) + [(L // 2, L // 2)]
+            for row in range(n):
+                for g in range(hkv):
+                    states = oracle.paged_partials(wl, r, g, ranges, row=row)
+                    assert len(states) == G and all(len(s) == len(ranges) for s in states)
+                    for i in range(G):
+                        h = g * G + i
+                        for c, (a, b) in enumerate(ranges):
+                            st = states[i][c]
+                            ref = brute_force_chunk_state(wl, r, g, h, row, a, b)
+                            what = f"partials case {k} r={r} row={row} h={h} chunk [{a},{b})"
+                            if ref is None:
+                                assert st.m == -math.inf and st.l == 0.0 and not np.any(st.acc), what
+                                continue
+                            m, l, acc = ref
+                            assert abs(st.m - m) <= 1e-13 * max(1.0, abs(m)), what
+                            assert abs(st.l - l) <= 1e-13 * l, what
+                            _assert_close(np.asarray(st.acc) / st.l, np.asarray(acc) / l, 1e-13, what)
+                        # a chunking that covers every key: folded in order == decode output
+                        got = oracle.finalize(oracle.fold(states[i][:-1]))
+                        want = dense[r, row, h] if n > 1 else dense[r, h]
+                        _assert_close(got, want, 1e-13, what + " (folded)")
+
+
 ALL_PINS = [pin_brute_force, pin_single_key, pin_uniform_scores, pin_two_keys, pin_needle,
             pin_gqa_grouping, pin_linearity_and_order, pin_partition_invariance,
             pin_empty_merge_identity, pin_merge_identity_values, pin_window,
             pin_permutation_invariance, pin_folded_equals_split, pin_fail_closed,
             pin_query_rows, pin_dtype_brute_force, pin_e4m3_codes, pin_f16_f32_codes,
             pin_dequant_factors, pin_prefill_brute_force, pin_prefill_rows_are_decode,
-            pin_prefill_causality, pin_tree_brute_force]
+            pin_prefill_causality, pin_tree_brute_force, pin_paged_partials]

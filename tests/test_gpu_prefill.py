@@ -1,7 +1,9 @@
 """GPU parity of paged prefill (attn_prefill through the C ABI) against the fp64 oracle.
 
 Bar: max |GPU - oracle| <= 2e-3 (the global prefill gate of pegainfer PR #1055,
-Verification, taken against fp64), NMSE <= 1e-4 and correlation >= 0.9999.  Cases follow
+Verification, taken against fp64), max |GPU - oracle| <= 1e-3 x max|o| (the decode
+tests' relative bar, which still bites where long rows make |o| small), NMSE <= 1e-4
+and correlation >= 0.9999.  Cases follow
 the windowed prefill gates of pegainfer PR #1057 (Verification): crossing the window,
 ragged prompts, a continuation and a tiny prompt; plus hostile padding, page-permutation
 and layout invariance, determinism, full-size sampled rows, the slow rescale path and
@@ -19,6 +21,7 @@ from tests.gpu_harness import SENTINEL, compare, fnv1a, note
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+REL = 1e-3
 GUARD_ROWS = 2
 
 
@@ -64,6 +67,7 @@ def check(got, ref, what, tol=TOL):
          f"nmse={st['nmse']:.3e} corr={st['corr']:.9f}")
     assert st["finite"], what
     assert st["max_abs"] <= tol, (what, st)
+    assert st["max_abs"] <= REL * st["max_ref"], (what, st)
     assert st["nmse"] <= 1e-4 and st["corr"] >= 0.9999, (what, st)
     return st
 
@@ -188,7 +192,7 @@ def test_full_size_global_sampled():
     rng = np.random.default_rng(7)
     n = 10602
     rows = sorted(set([0, 1, 7, 8, 9, 255, 256, 257, 4095, 4096, n - 9, n - 8, n - 2, n - 1]
-                      + rng.integers(0, n, 24).tolist()))
+                      + list(range(131, n, 128)) + rng.integers(0, n, 40).tolist()))
     for fmt in ("split", "folded"):
         note(f"[gpu] prefill {fmt} n=10602: generating")
         wl = synth.global_prefill(n, seed=205, fmt=fmt)
@@ -207,7 +211,8 @@ def test_full_size_sliding_sampled():
     rows = []
     for r in range(wl.batch):
         a, b = int(starts[r]), int(starts[r + 1])
-        rows += sorted(set([a, b - 1] + rng.integers(a, b, 3).tolist()))
+        rows += sorted(set([a, a + 1, b - 1] + list(range(a + 63, b, 64)) +
+                           rng.integers(a, b, 8).tolist()))
     check(got[rows], oracle.prefill_attention(wl, rows=rows), "sliding 16 sampled")
 
 

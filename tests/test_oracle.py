@@ -182,6 +182,26 @@ def _tree_masks_read_by_index(L, n, i, window, mask):
 _window_row_positions = OA.window_row_positions
 
 
+def _partials_variant(row_offset=True, window=True, clip=True):
+    """paged_partials with one of its visible-range steps left out."""
+    def f(wl, r, g, ranges, row=0):
+        G = wl.num_q_heads // wl.num_kv_heads
+        n = getattr(wl, "num_rows", 1)
+        q = wl.q if n > 1 else wl.q[:, None]
+        hi = int(wl.seq_lens[r]) - n + 1 + row if row_offset else int(wl.seq_lens[r])
+        lo, L = OA.visible_range(hi, wl.window if window else 0)
+        out = [[] for _ in range(G)]
+        for a, b in ranges:
+            pos = np.arange(max(a, lo), min(b, L)) if clip else np.arange(max(a, 0), b)
+            pos = pos[pos < int(wl.seq_lens[r])] if not clip else pos
+            K, V = OA.keys_values(wl, OA._stored_rows(wl, r, g, pos))
+            for i in range(G):
+                out[i].append(OA.partial_state(q[r, row, g * G + i], K, V, wl.scale))
+        return out
+    return f
+
+
+
 MUTANTS = {
     "rows_see_one_key_too_many": ("decode_attention", _rows_off_by_one),
     "k_v_swapped": ("keys_values", _kv_swapped),
@@ -201,6 +221,9 @@ MUTANTS = {
     "prefill_rows_from_zero": ("prefill_row_index", _prefill_rows_from_zero),
     "prefill_excludes_own_key": ("prefill_attention", _prefill_excludes_own_key),
     "tree_masks_read_by_index": ("window_row_positions", _tree_masks_read_by_index),
+    "partials_row_offset_dropped": ("paged_partials", _partials_variant(row_offset=False)),
+    "partials_window_dropped": ("paged_partials", _partials_variant(window=False)),
+    "partials_not_clipped_to_row": ("paged_partials", _partials_variant(clip=False)),
 }
 
 
