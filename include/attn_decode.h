@@ -27,7 +27,8 @@
  * attn_kv_write, attn_query_fold's q, norm_w and q_out) must be 16-byte aligned (the
  * kernels move them in 16-byte vectors); the workspace 256-byte aligned; int32 and uint64
  * arrays (page table, lengths, offsets, masks) to their element size.  The library allocates nothing, keeps no mutable global
- * state and is reentrant.  Launches are asynchronous; buffers must stay alive
+ * state and is reentrant (attn_decode_step_noalloc aside: it uses a static per-GPU array
+ * and remembers that array's address per device).  Launches are asynchronous; buffers must stay alive
  * until the stream has run them.  A plan is plain old data and may be copied.
  * The enqueuing calls neither synchronise nor allocate nor record memsets, and a
  * plan fixes their grids, so they can be captured into a HIP graph and replayed.
@@ -54,7 +55,9 @@ enum {
   ATTN_E_OVERFLOW = -4,     /* a size computation would overflow 64 bits / grid limits */
   ATTN_E_WORKSPACE = -5,    /* workspace smaller than the plan needs, or misaligned */
   ATTN_E_PLAN = -6,         /* plan not produced by attn_decode_plan (bad magic) */
-  ATTN_E_LAUNCH = -7        /* the HIP runtime refused a launch */
+  ATTN_E_LAUNCH = -7,       /* the HIP runtime refused a launch */
+  ATTN_E_SCRATCH = -8       /* attn_decode_step_noalloc: the plan needs more chunk-state
+                               memory than its static array holds */
 };
 
 /* Row formats of the pool, fixed for the pool's life (pegainfer PR #1055,
@@ -346,6 +349,30 @@ int attn_prefill_plan(const attn_decode_desc* desc, const int32_t* seq_lens_host
 int attn_prefill(const attn_prefill_plan_t* plan, const float* q, const void* kv_pool,
                  const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_starts,
                  float* out, void* stream);
+
+/*
+ * Allocation-free decode step, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  It enqueues
+ * exactly attn_decode_split (attn_decode_split_tree when row_masks is not NULL) followed
+ * by attn_decode_merge, but the chunk states live in a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs on until the
+ * process ends, instead of a caller's workspace.  Nothing is allocated: no hipMalloc, no
+ * hipFree, no allocating library routine.  The first call on a device, with that device
+ * current, looks up the array's device address (hipGetSymbolAddress) and keeps it.
+ *   q, kv_pool, page_table, seq_lens, row_masks  as attn_decode_split / _split_tree
+ *   out     device, float32 as attn_decode_merge
+ *   stream  hipStream_t of the current device (NULL = its default stream)
+ * Every call on one GPU shares that GPU's array and leaves the last call's states in it:
+ * calls that overlap on one GPU (other streams, other threads) race and must be ordered by
+ * the caller.  Returns ATTN_E_SCRATCH if plan->workspace_bytes exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES (e.g. 163,336 tokens with one query row needs 4.2 MB, four
+ * query rows 16.8 MB), ATTN_E_LAUNCH if the array's address cannot be obtained or HIP
+ * refuses a launch, else the errors of attn_decode_split and attn_decode_merge.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_decode_step_noalloc(const attn_decode_plan_t* plan, const float* q, const void* kv_pool,
+                             const int32_t* page_table, const int32_t* seq_lens,
+                             const uint64_t* row_masks, float* out, void* stream);
 
 /* Static, NUL-terminated text for a status code. */
 const char* attn_decode_status_string(int status);

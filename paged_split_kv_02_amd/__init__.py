@@ -18,6 +18,7 @@ __all__ = ["AttnDecodeDesc", "AttnDecodePlan", "AttnDecodeError", "attn_decode_p
            "attn_decode_status_string", "make_desc",
            "attn_kv_write", "attn_query_fold", "AttnPrefillPlan", "attn_prefill_plan",
            "attn_prefill", "attn_stream_read", "STREAM_READ_GROUPS",
+           "attn_decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
            "ATTN_KV_SPLIT", "ATTN_KV_FOLDED", "ATTN_KV_BF16", "ATTN_KV_F16", "ATTN_KV_FP8_E4M3",
            "ATTN_KV_F32", "STATUS", "LIB_PATH", "SYMBOLS"]
 
@@ -29,11 +30,12 @@ ATTN_KV_FP8_E4M3 = 2
 ATTN_KV_F32 = 3
 STATUS = {"ATTN_OK": 0, "ATTN_E_INVALID_ARG": -1, "ATTN_E_UNSUPPORTED": -2,
           "ATTN_E_PAST_PAGES": -3, "ATTN_E_OVERFLOW": -4, "ATTN_E_WORKSPACE": -5,
-          "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7}
+          "ATTN_E_PLAN": -6, "ATTN_E_LAUNCH": -7, "ATTN_E_SCRATCH": -8}
 SYMBOLS = ("attn_decode_plan", "attn_decode_split", "attn_decode_split_tree", "attn_decode_merge",
            "attn_decode_status_string", "attn_kv_write", "attn_query_fold",
-           "attn_prefill_plan", "attn_prefill", "attn_stream_read")
+           "attn_prefill_plan", "attn_prefill", "attn_stream_read", "attn_decode_step_noalloc")
 STREAM_READ_GROUPS = 2048  # ATTN_STREAM_READ_GROUPS
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 LIB_PATH = _build.LIB
 
 
@@ -103,6 +105,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.attn_stream_read.restype = ctypes.c_int
+    lib.attn_decode_step_noalloc.argtypes = [ctypes.POINTER(AttnDecodePlan), P, P, P, P, P, P, P]
+    lib.attn_decode_step_noalloc.restype = ctypes.c_int
     lib.attn_decode_status_string.argtypes = [ctypes.c_int]
     lib.attn_decode_status_string.restype = ctypes.c_char_p
     return lib
@@ -195,6 +199,18 @@ def attn_decode_merge(plan: AttnDecodePlan, workspace, out, workspace_bytes=None
                                 _stream(stream))
     if rc != 0:
         raise AttnDecodeError("attn_decode_merge", rc)
+
+
+def attn_decode_step_noalloc(plan: AttnDecodePlan, q, kv_pool, page_table, seq_lens, out,
+                             row_masks=None, stream=None) -> None:
+    """A whole decode step (split, or split_tree with row_masks, then merge) with the chunk
+    states in the library's static per-GPU array: no workspace argument, nothing
+    allocated.  Calls that overlap on one GPU race (they share the array)."""
+    rc = _lib.attn_decode_step_noalloc(ctypes.byref(plan), _ptr(q), _ptr(kv_pool),
+                                       _ptr(page_table), _ptr(seq_lens), _ptr(row_masks),
+                                       _ptr(out), _stream(stream))
+    if rc != 0:
+        raise AttnDecodeError("attn_decode_step_noalloc", rc)
 
 
 def attn_kv_write(plan: AttnDecodePlan, k, v, num_new: int, start_pos, kv_pool, page_table,

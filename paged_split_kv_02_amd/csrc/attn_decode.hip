@@ -31,6 +31,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "plan_internal.h"
 
@@ -1465,3 +1466,66 @@ extern "C" int attn_query_fold(const attn_decode_plan_t* plan, const float* q, c
   return launch_status();
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free decode step, for callers that cannot allocate device memory.  The chunk
+// states (the workspace of attn_decode_split / attn_decode_merge) live in one static device
+// array per GPU.  In host code `scratch` names a host-side stand-in, not device memory:
+// its device address is taken once per device with hipGetSymbolAddress and only that
+// address is ever handed to a kernel.
+namespace attn {
+
+__device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up on the first call
+// on that device, with it current).
+int scratch_of_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return ATTN_E_LAUNCH;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" int attn_decode_step_noalloc(const attn_decode_plan_t* plan, const float* q,
+                                        const void* kv_pool, const int32_t* page_table,
+                                        const int32_t* seq_lens, const uint64_t* row_masks,
+                                        float* out, void* stream) {
+  using namespace attn;
+  int rc = check_plan(plan);
+  if (rc != ATTN_OK) return rc;
+  if (row_masks && plan->num_rows < 2) return ATTN_E_INVALID_ARG;
+  if (!q || !kv_pool || !page_table || !seq_lens || !out) return ATTN_E_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned_to(page_table, 4) ||
+      !aligned_to(seq_lens, 4) || !aligned_to(row_masks, 8))
+    return ATTN_E_INVALID_ARG;
+  if (!shape_supported(plan->desc)) return ATTN_E_UNSUPPORTED;
+  if (plan->workspace_bytes > uint64_t(ATTN_NOALLOC_SCRATCH_BYTES)) return ATTN_E_SCRATCH;
+  char* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc != ATTN_OK) return rc;
+  // The same launches as attn_decode_split (or _split_tree) and attn_decode_merge, with
+  // the static array as their workspace; every state the merge reads is written first,
+  // so nothing needs clearing.
+  rc = split_launch(plan, q, kv_pool, page_table, seq_lens, row_masks, ws,
+                    ATTN_NOALLOC_SCRATCH_BYTES, stream);
+  if (rc != ATTN_OK) return rc;
+  return attn_decode_merge(plan, ws, ATTN_NOALLOC_SCRATCH_BYTES, out, stream);
+}

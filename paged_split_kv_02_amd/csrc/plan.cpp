@@ -339,6 +339,7 @@ extern "C" const char* attn_decode_status_string(int status) {
     case ATTN_E_WORKSPACE: return "workspace too small or misaligned";
     case ATTN_E_PLAN: return "not a plan made by attn_decode_plan";
     case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_SCRATCH: return "plan needs more chunk-state memory than the static scratch holds";
     default: return "unknown status";
   }
 }

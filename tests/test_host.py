@@ -507,3 +507,28 @@ def test_loaded_library_matches_the_sources():
     assert B.is_current(), "libattn_decode.so is older than its sources"
     assert B.built_digest() == B.source_digest()
 
+def test_noalloc_step_refuses_before_any_device_call():
+    """The allocation-free step refuses a bad plan, null or misaligned buffers, masks with a
+    one-row plan and a plan larger than its static array, all before touching a device."""
+    rc, p = plan_status([1024], **global_desc())
+    rc4, p4 = plan_status([1024], **global_desc(num_rows=4))
+    assert rc == 0 and rc4 == 0
+    # 16 requests of 163,336 tokens with 64-chunk states: more than the static array holds
+    big_lens = [163336] * 16
+    rcb, pb = plan_status(big_lens, **global_desc(163336, batch=16, num_chunks=64))
+    assert rcb == 0 and pb.workspace_bytes > K.NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    fake = 1 << 20  # never dereferenced
+    bad = K.AttnDecodePlan.from_buffer_copy(p)
+    bad.magic = 0
+    N = K._lib.attn_decode_step_noalloc
+    assert N(ctypes.byref(bad), fake, fake, fake, fake, None, fake, None) == S["ATTN_E_PLAN"]
+    assert N(None, fake, fake, fake, fake, None, fake, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(p), fake, fake, fake, fake, None, None, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(p), None, fake, fake, fake, None, fake, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(p), fake, fake, fake, fake, None, fake + 4, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(p4), fake, fake, fake, fake, fake + 4, fake, None) == S["ATTN_E_INVALID_ARG"]
+    assert N(ctypes.byref(pb), fake, fake, fake, fake, None, fake, None) == S["ATTN_E_SCRATCH"]
+
