@@ -122,7 +122,8 @@ def time_steps(res, steps, warmup, flush=None):
     step time); region B repeats the steps with events around each partial-kernel
     launch (its duration, for the roofline).  With ``flush`` (inputs that fit the
     256 MB infinity cache): every step is preceded by an untimed 1 GiB write and
-    timed on its own.
+    timed on its own (two events around split + merge), alternating with a partial-kernel
+    launch timed on its own after a flush of its own.
     """
     import torch
     stream = torch.cuda.current_stream()
@@ -154,17 +155,24 @@ def time_steps(res, steps, warmup, flush=None):
         each_step_ms = [a.elapsed_time(c) for a, _, c in ev]
         return dict(total_ms=total_ms, wall_s=wall, split_ms=split_ms,
                     step_ms=[total_ms / steps] * steps, each_step_ms=each_step_ms)
+    # Alternating: a step bracketed by two events only (split and merge back to back, as a
+    # caller runs them), then a partial-kernel launch bracketed on its own.
     step_ms, split_ms = [], []
     for _ in range(steps):
         flush()
-        a, b, c = E(), E(), E()
+        a, c = E(), E()
         a.record(stream)
         res.split()
-        b.record(stream)
         res.merge()
         c.record(stream)
         torch.cuda.synchronize()
         step_ms.append(a.elapsed_time(c))
+        flush()
+        a, b = E(), E()
+        a.record(stream)
+        res.split()
+        b.record(stream)
+        torch.cuda.synchronize()
         split_ms.append(a.elapsed_time(b))
     return dict(total_ms=sum(step_ms), wall_s=None, split_ms=split_ms, step_ms=step_ms)
 
@@ -430,7 +438,12 @@ def main():
                 ("sliding-hd256-16ragged-w1024-fp8e4m3",
                  lambda: synth.sliding_batch(seed=4, kv_dtype=synth.FP8), 20),
                 ("global-decode-163336-split-f32",
-                 lambda: synth.global_decode(163336, seed=10, kv_dtype=synth.F32), 20)):
+                 lambda: synth.global_decode(163336, seed=10, kv_dtype=synth.F32), 20),
+                ("global-decode-163336-folded-f32",
+                 lambda: synth.global_decode(163336, seed=10, fmt="folded", kv_dtype=synth.F32), 20),
+                ("global-decode-163336-split-f32-4rows",
+                 lambda: synth.make_workload([163336], **synth.GLOBAL, seed=10, num_rows=4,
+                                             kv_dtype=synth.F32, spare_pages=1), 20)):
             if not wanted(name):
                 continue
             vwl = maker()
@@ -488,6 +501,12 @@ def main():
                              lambda: synth.global_prefill(10602, seed=11, fmt="folded")),
                             ("global-prefill-10602-split-fp8",
                              lambda: synth.global_prefill(10602, seed=11, kv_dtype=synth.FP8)),
+                            ("global-prefill-10602-split-f16",
+                             lambda: synth.global_prefill(10602, seed=11, kv_dtype=synth.F16)),
+                            ("global-prefill-10602-split-f32",
+                             lambda: synth.global_prefill(10602, seed=11, kv_dtype=synth.F32)),
+                            ("sliding-prefill-16ragged-w1024-f32",
+                             lambda: synth.sliding_prefill(seed=12, kv_dtype=synth.F32)),
                             ("sliding-prefill-16ragged-w1024", lambda: synth.sliding_prefill(seed=12))):
             if not wanted(name):
                 continue

@@ -75,8 +75,7 @@ enum {
  * FP8 E4M3 as the OCP 8-bit floating point specification defines it (bias 7,
  * subnormals, no infinity, S.1111.111 = NaN), the FP8 encoding gfx950 converts
  * natively.  Every type is widened exactly to the MFMA operand type (bf16 for BF16
- * and FP8, f16 for F16); F32 rows are multiplied in full fp32 (split rows and one query
- * row only: folded F32 rows and F32 windows of several rows are ATTN_E_UNSUPPORTED). */
+ * and FP8, f16 for F16); F32 rows are multiplied in full fp32. */
 enum {
   ATTN_KV_BF16 = 0,
   ATTN_KV_F16 = 1,
@@ -255,14 +254,22 @@ int attn_decode_merge(const attn_decode_plan_t* plan, void* workspace, size_t wo
  * Write new tokens' K/V rows into the pool: the step that feeds decode.  Each
  * forward's k/v rows are copied into the pages through the table (TensorFold PR
  * #1619, body), in the pool's row format (pegainfer PR #1055, "Description": the
- * hd512 prep writes either form).  Values arrive as float32 and are stored as bf16,
- * rounded to nearest with ties to even.
+ * hd512 prep writes either form).  Values arrive as float32; each is divided by its
+ * tensor's factor (k_scale or v_scale: one float32 division rounded to nearest, skipped
+ * when the factor is 1) and stored as the pool's element type:
+ *   BF16, F16  rounded to nearest with ties to even (F16: overflow gives infinity)
+ *   F32        as is
+ *   FP8_E4M3   the nearest E4M3 value with ties to the even mantissa; magnitudes from 448
+ *              up (infinity included) saturate to 448, NaN gives S.1111.111, and a value
+ *              that rounds to zero keeps its sign (the decode path reads stored * factor;
+ *              the pages name quantised KV as an axis without fixing the encoding, gem
+ *              design note, "Fixed production shape").
  *   k          device float32 [batch][num_new][num_kv_heads][kc]; kc = head_dim for
  *              SPLIT (row columns k_offset..), rot_cols for FOLDED (the rotated part)
  *   v          device float32 [batch][num_new][num_kv_heads][head_dim] (columns v_offset..)
  *   start_pos  device int32 [batch]: logical position of each request's first new token;
  *              token i goes to position start_pos[r] + i (a decode step appends at L - 1)
- *   kv_pool    device bf16 pool, written in place
+ *   kv_pool    device pool of kv_dtype elements, written in place
  *   page_table device int32 [batch][max_pages_per_seq]
  *   bad_rows   device int32, may be NULL: set to 1 if any row was skipped because its
  *              position is past the table row or its page id is outside the pool (such
@@ -301,9 +308,11 @@ int attn_query_fold(const attn_decode_plan_t* plan, const float* q, const float*
  * window and max(0, p + 1 - window) with one: each row is a decode token at length
  * p + 1 (n_r < L_r is a continuation after L_r - n_r earlier keys).
  * The descriptor is the decode descriptor (num_chunks, merge_group and num_rows are not
- * used).  Supported: the decode shapes, bf16 and FP8 E4M3 pools (FP8 codes are widened
- * to bf16 on their way on chip and the dequantisation factors applied as in decode),
- * page_size a multiple of 32.
+ * used).  Supported: the decode shapes; bf16, f16 and FP8 E4M3 pools with page_size a
+ * multiple of 32 (FP8 codes are widened to bf16 on their way on chip, f16 rows are
+ * multiplied on the f16 MFMA, and the dequantisation factors are applied as in decode), and
+ * f32 pools (full fp32 products on the f32 decode kernel, 16 / G rows per workgroup, each
+ * wave a quarter of the keys).
  * The output is written directly (no workspace, no merge): one workgroup owns
  * row_tile consecutive rows of one (request, KV head) and walks their keys in
  * key_tile-key tiles, staged once in on-chip memory for all its rows and heads.
@@ -312,8 +321,9 @@ typedef struct attn_prefill_plan_t {
   uint64_t magic;
   attn_decode_desc desc;
   int32_t group_size;  /* query heads per KV head */
-  int32_t key_tile;    /* keys per tile (32) */
-  int32_t row_tile;    /* query rows per workgroup (8 at head dim 512 / GQA 8, 64 at head dim 256 / GQA 2) */
+  int32_t key_tile;    /* keys per tile (32; 16 for f32 pools) */
+  int32_t row_tile;    /* query rows per workgroup (8 at head dim 512 / GQA 8, 64 at head dim 256 / GQA 2;
+                          f32 pools: 2 and 8) */
   int32_t total_rows;  /* q_starts[batch] */
   int32_t max_rows;    /* largest n_r */
   int32_t grid_x;      /* row tiles per (request, KV head): ceil(max_rows / row_tile) */
@@ -323,8 +333,8 @@ typedef struct attn_prefill_plan_t {
  * Validate `desc`, the host lengths seq_lens_host[batch] and the host row offsets
  * q_starts_host[batch + 1], and fill `plan`.  No device call is made.
  * Refusals as attn_decode_plan for the descriptor (ATTN_E_INVALID_ARG,
- * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); an f16 or f32 pool or a page size not a
- * multiple of 32 (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
+ * ATTN_E_UNSUPPORTED, ATTN_E_OVERFLOW); a page size not a multiple of 32 for a 16-bit or
+ * FP8 pool (ATTN_E_UNSUPPORTED); q_starts[0] != 0, decreasing offsets, or
  * more rows than keys in a request (ATTN_E_INVALID_ARG); a length above
  * max_pages_per_seq * page_size (ATTN_E_PAST_PAGES); a length within 1024 of 2^31, or
  * more work items than one launch takes (ATTN_E_OVERFLOW).

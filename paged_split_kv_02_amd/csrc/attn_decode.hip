@@ -69,6 +69,11 @@ struct SplitArgs {
   float qscale_k;  // scale * log2(e) * k_scale: the query dims that meet K columns
   float qscale_v;  // scale * log2(e) * v_scale: folded query dims that meet V columns
   float vscale;    // v_scale, applied to the written numerators
+  // Prompt rows (the f32 kernel's prefill mode): request r's new rows are q_starts[r] ..
+  // q_starts[r + 1] of q and out; normalised rows are written to out.
+  const int32_t* q_starts;
+  float* out;
+  int32_t total_rows, max_rows;
 };
 
 // Keys covered by the first c chunks (even chunks chunk_len, odd ones chunk_len_odd).
@@ -632,45 +637,160 @@ struct F32Ring {
   static constexpr int AHEAD = NP - 1;                        // pieces in flight behind the one in use
 };
 
-template <int D, int G>
+// Merge of the four waves' quarter states of the f32 kernel (fixed order), 4 dims per
+// thread, for the 16 MFMA columns: column h is row row0 + h / G of the work item, head
+// h % G.  Decode: the chunk state of each active column (natural-log m, O times v_scale).
+// Prefill: the normalised row O * v_scale / S into out.
+template <int D, int G, bool PREFILL>
+__device__ __forceinline__ void write_f32_states(const SplitArgs& a,
+                                                 const QuarterState<D, 16>* const (&parked)[kWavesPerBlock],
+                                                 int g, int chunk, int64_t qs0, int row0, int rows) {
+  const float qnan = __builtin_nanf("");
+  for (int idx = threadIdx.x; idx < 16 * (D / 4); idx += 64 * kWavesPerBlock) {
+    const int h = idx / (D / 4);
+    const int d4 = idx % (D / 4);
+    const int row = row0 + h / G;
+    if (row >= rows) continue;
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const float x = parked[w]->m[h];
+      nan |= x != x;
+      M = fmaxf(M, x);
+    }
+    float S = 0.0f;
+    floatx4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float x = parked[w]->m[h];
+        const float wt = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - M);
+        S += wt * parked[w]->l[h];
+        O += wt * parked[w]->o[h][d4];
+      }
+    }
+    if (nan) {
+      M = S = qnan;
+      O = floatx4{qnan, qnan, qnan, qnan};
+    }
+    const int64_t hq = (qs0 + row) * a.num_q_heads + g * G + h % G;
+    if constexpr (PREFILL) {
+      *reinterpret_cast<floatx4*>(a.out + hq * D + 4 * d4) = O * (a.vscale / S);
+    } else {
+      const int64_t st = hq * a.num_chunks + chunk;
+      if (d4 == 0) {
+        a.part_m[st] = M == -INFINITY ? -INFINITY : M * kLn2;
+        a.part_l[st] = S;
+      }
+      *reinterpret_cast<floatx4*>(a.part_o + st * D + 4 * d4) = O * a.vscale;
+    }
+  }
+}
+
+// The f32 kernel.  Its 16 MFMA columns hold R = 16 / G query rows of the KV head's G heads
+// (column c: row c / G of the work item, head c % G): one decode row uses the first G
+// columns; a window of rows is cut into groups of R rows, each a workgroup per chunk; in
+// prefill mode (PREFILL) a workgroup is R consecutive prompt rows of one request, whose
+// keys (from the first row's window start to the last row's position) are cut into four
+// quarters, one per wave, and whose normalised rows are written directly.
+template <int D, int G, bool FOLDED, bool PREFILL>
 __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   using S = F32Shape<D>;
-  static_assert(G <= 16, "heads of a KV head fit the 16 MFMA columns");
-  static_assert(sizeof(QuarterState<D, G>) <= S::REGION, "parked state must fit the region");
+  constexpr int R = 16 / G;  // query rows per work item
+  static_assert(!FOLDED || D == 512, "folded rows: head dim 512");
+  static_assert(G <= 16 && 16 % G == 0, "whole rows of heads fill the 16 MFMA columns");
+  static_assert(sizeof(QuarterState<D, 16>) <= S::REGION, "parked state must fit the region");
   __shared__ __attribute__((aligned(16))) char region[kWavesPerBlock][S::REGION];
 
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15;   // MFMA column (head) / K row inside the tile
+  const int c = lane & 15;   // MFMA column ((row, head) pair) / K row inside the tile
   const int qg = lane >> 4;  // lane group: k index of the MFMA operands / output rows
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int chunk = blockIdx.x;
   const int g = blockIdx.y;
   const int r = blockIdx.z;
   char* lds = region[wave];
 
   const int L = a.seq_lens[r];
-  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
-  const int start = lo & ~(kTile - 1);
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
-  bool poison = L < 1 || int64_t(L) > cap ||
-                int64_t(L) - start > chunk_cover(a, a.num_chunks);
-  const int quarter = ((chunk & 1) ? a.chunk_len_odd : a.chunk_len) / kWavesPerBlock;
-  const int c0 = start + int(chunk_cover(a, chunk)) + wave * quarter;
-  const int c1 = min(c0 + quarter, L);
+  int chunk = 0, rows, row0;
+  int64_t qs0;
+  if constexpr (PREFILL) {
+    // Offsets the plan cannot serve are not followed: nothing is read or written.
+    qs0 = a.q_starts[r];
+    const int qs1 = a.q_starts[r + 1];
+    rows = qs1 - int(qs0);
+    if (qs0 < 0 || rows < 0 || rows > a.max_rows || qs1 > a.total_rows) return;
+    row0 = blockIdx.x * R;
+    if (row0 >= rows) return;
+  } else {
+    // Launch order of several row groups: the groups of a chunk 8 workgroups apart (one XCD).
+    const int lo8 = blockIdx.x % 8;
+    const int hi8 = blockIdx.x / 8;
+    chunk = (hi8 / a.row_groups) * 8 + lo8;
+    if (chunk >= a.num_chunks) return;  // padding of the launch order (whole workgroup)
+    rows = a.num_rows;
+    qs0 = int64_t(r) * rows;
+    row0 = (hi8 % a.row_groups) * R;
+  }
+  bool poison = L < max(rows, 1) || int64_t(L) > cap;
+
+  // This lane's column: row `row` of the request's rows (position L - rows + row), head
+  // c % G.  It sees keys lo_c <= t < hi_c, and with row masks (tree windows) of the window's
+  // own keys [wstart, L) only those whose bit t - wstart is set.  An idle column sees none.
+  const int row = row0 + c / G;
+  const bool active = row < rows;
+  const int hi_row = L - rows + row + 1;
+  int lo_c = a.window > 0 ? max(0, hi_row - a.window) : 0;
+  int hi_c = hi_row;
+  int wstart = INT32_MAX;
+  uint64_t mask_c = ~uint64_t(0);
+  if constexpr (!PREFILL) {
+    if (a.row_masks && active) {
+      hi_c = L;
+      wstart = L - rows;
+      mask_c = a.row_masks[qs0 + row];
+    }
+  }
+  if (!active) {
+    lo_c = INT32_MAX;
+    hi_c = 0;
+  }
+  // Keys some column of the work item may see: [kv_lo, kv_hi); V rows outside are zeroed.
+  // Decode chunks partition the keys from the request's first row's window start.
+  const int last = min(row0 + R, rows) - 1;
+  const int hi_first = L - rows + (PREFILL ? row0 : 0) + 1;
+  const int kv_lo = a.window > 0 ? max(0, hi_first - a.window) : 0;
+  const int kv_hi = (PREFILL || !a.row_masks) ? L - rows + last + 1 : L;
+  const int start = kv_lo & ~(kTile - 1);
+  int c0, c1;
+  if constexpr (PREFILL) {
+    const int quarter = (kv_hi - start + 4 * kTile - 1) / (4 * kTile) * kTile;
+    c0 = start + wave * quarter;
+    c1 = min(c0 + quarter, kv_hi);
+  } else {
+    poison = poison || int64_t(L) - start > chunk_cover(a, a.num_chunks);
+    const int quarter = ((chunk & 1) ? a.chunk_len_odd : a.chunk_len) / kWavesPerBlock;
+    c0 = start + int(chunk_cover(a, chunk)) + wave * quarter;
+    c1 = min(c0 + quarter, kv_hi);
+  }
   const int end = (!poison && c0 < c1) ? c1 : c0;
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
   PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
 
-  // Query operand: lane (c, qg), group s, step j holds q[head c][16s + 4qg + j] times
-  // scale * log2(e) * k_scale (zero for columns past the G heads).  Parked in the
-  // accumulation registers, so the vector registers hold the output accumulators.
+  // Query operand: lane (c, qg), group s, step j holds q[row][head][16s + 4qg + j] times
+  // scale * log2(e) * k_scale (folded rows: v_scale for the dims from 128 on, which meet V
+  // columns; zero for an idle column).  Parked in the accumulation registers, so the
+  // vector registers hold the output accumulators.
   floatx4 qv[S::QSTEPS];
   {
-    const float* qrow = a.q + (int64_t(r) * a.num_q_heads + g * G + (c < G ? c : 0)) * D + 4 * qg;
+    const float* qrow =
+        a.q + ((qs0 + (active ? row : 0)) * a.num_q_heads + g * G + c % G) * int64_t(D) + 4 * qg;
 #pragma unroll
     for (int s = 0; s < S::QSTEPS; ++s) {
-      qv[s] = c < G ? *reinterpret_cast<const floatx4*>(qrow + 16 * s) * a.qscale_k
-                    : floatx4{0.f, 0.f, 0.f, 0.f};
+      const float f = (FOLDED && 16 * s >= 128) ? a.qscale_v : a.qscale_k;
+      qv[s] = active ? *reinterpret_cast<const floatx4*>(qrow + 16 * s) * f
+                     : floatx4{0.f, 0.f, 0.f, 0.f};
       asm volatile("" : "+a"(qv[s]));
     }
   }
@@ -704,7 +824,8 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tok0 + 4 * qg + i;
-      sc[i] = (t >= lo && t < L) ? sc4[i] : -INFINITY;
+      const bool vis = t >= lo_c && t < hi_c && (t < wstart || ((mask_c >> ((t - wstart) & 63)) & 1));
+      sc[i] = vis ? sc4[i] : -INFINITY;
       mx = fmaxf(mx, sc[i]);
     }
     mx = fmaxf(mx, shfl_xor(mx, 16));
@@ -712,7 +833,9 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
     const bool grow = mx > m_run + kRescaleSlack;
     if (__builtin_expect(__any(grow), 0)) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+      // Columns see different keys (rows, windows): one that keeps its maximum keeps its
+      // sums (exp2(-inf - -inf) would be NaN for a column with no visible key yet).
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // 0 from -inf
       l_run *= alpha;
 #pragma unroll
       for (int b = 0; b < S::VBLOCKS; ++b)
@@ -731,7 +854,7 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   // PV over 64-dim blocks [B0, B1).  MFMA t takes keys 4qg + t, so lane (c, qg) supplies
   // its own p[t] as B; A = V^T: lane (m, qg) holds dims 64b + 4m + jj of key 4qg + t.
   auto pv = [&](int tok0, auto b_begin, auto b_end) {
-    const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
+    const bool edge = tok0 < kv_lo || tok0 + kTile > kv_hi;  // uniform
 #pragma unroll
     for (int b = decltype(b_begin)::value; b < decltype(b_end)::value; ++b)
 #pragma unroll
@@ -740,7 +863,7 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
         floatx4 vv = *reinterpret_cast<const floatx4*>(lds + kr * S::PITCH + 256 * b + 16 * c);
         if (__builtin_expect(edge, 0)) {
           const int key = tok0 + kr;
-          if (key < lo || key >= L) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
+          if (key < kv_lo || key >= kv_hi) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[b][jj] = mma_f32(vv[jj], p[t], acc[b][jj]);
@@ -766,12 +889,18 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
     static_assert(R::AHEAD * R::IPP <= 63, "outstanding loads fit the counter");
     static_assert(S::QSTEPS == 4 * R::NP && S::VBLOCKS == R::NP, "one piece = 4 score steps = 1 PV block");
 
+    // Folded rows (rotated K: 2 pieces, V: 8 pieces): the score takes K pieces 0-1 and V
+    // pieces 2-7, the output V pieces 0-7, so a tile loads 10 pieces into the same eight
+    // slots: K0, K1, V2 .. V7 for the score phases 0-7 (slots 0-7), and V0 / V1 into slots
+    // 0 / 1 once phases 0 / 1 have read K0 / K1; the output phases 8-15 read slots 0-7.  A
+    // slot is refilled with the next tile's piece after its last read (K0' after phase 8,
+    // K1' after 9, V2' .. V6' after 10 .. 14, V7' at the next tile's phase 0), so every
+    // piece is requested about seven phases before it is used.
     // Lane l of load instruction i fetches row R::RPI*i + l / R::CH, chunk (l % R::CH) ^ row.
-    auto issue = [&](int32_t pid, int tok0, int j) {  // piece j (0-15) of the tile at tok0
+    auto issue_at = [&](int32_t pid, int tok0, int64_t col, int slot) {  // 256 B per row at col
       const char* base = head_base + int64_t(pid) * a.page_stride +
-                         int64_t(tok0 % a.page_size) * a.row_stride +
-                         (j >= R::NP ? a.v_offset : a.k_offset) + R::PW * (j % R::NP);
-      char* dst = lds + R::SLOT * (j % R::NP);
+                         int64_t(tok0 % a.page_size) * a.row_stride + col;
+      char* dst = lds + R::SLOT * slot;
 #pragma unroll
       for (int i = 0; i < R::IPP; ++i) {
         const int row = R::RPI * i + lane / R::CH;
@@ -779,24 +908,56 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
         __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + 1024 * i), 16, 0, kStreamLds);
       }
     };
+    // Split rows: piece j (0-15) of the tile: K pieces 0-7, then V pieces 0-7, slot j % 8.
+    // Folded rows: piece j of the load order K0, K1, V2 .. V7, V0, V1 (slots 0-7, 0, 1).
+    auto issue = [&](int32_t pid, int tok0, int j) {
+      if constexpr (FOLDED) {
+        const int64_t col = j < 2 ? a.k_offset + R::PW * j
+                                  : a.v_offset + R::PW * (j < R::NP ? j : j - R::NP);
+        issue_at(pid, tok0, col, j % R::NP);
+      } else {
+        issue_at(pid, tok0, (j >= R::NP ? a.v_offset : a.k_offset) + R::PW * (j % R::NP), j % R::NP);
+      }
+    };
     auto reads_done = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
     auto phase = [&](auto jc, int32_t pid, int tok0, int32_t npid, int next, bool more) {
       constexpr int J = decltype(jc)::value;
       reads_done();
-      if constexpr (J + R::AHEAD < 2 * R::NP) {
-        issue(pid, tok0, J + R::AHEAD);
-      } else {
-        if (more) issue(npid, next, J + R::AHEAD - 2 * R::NP);
-      }
-      // Wait for piece J: the loads issued after it may stay in flight.
-      if constexpr (J + R::AHEAD < 2 * R::NP) {
-        vm_wait_lt<R::AHEAD * R::IPP>();
-      } else {
-        if (more)
+      if constexpr (FOLDED) {
+        // Requests: V7 at phase 0, V0 / V1 at 1 / 2, the next tile's K0, K1, V2 .. V6 at
+        // 9 .. 15.  Wait for the piece this phase reads (phases 10-15 read V pieces the
+        // score phases already waited for): pieces requested after it may stay in flight.
+        if constexpr (J == 0) issue(pid, tok0, 7);
+        if constexpr (J == 1 || J == 2) issue(pid, tok0, 7 + J);
+        if constexpr (J >= 9) {
+          if (more) issue(npid, next, J - 9);
+        }
+        if constexpr (J <= 2) {
           vm_wait_lt<R::AHEAD * R::IPP>();
-        else
-          vm_wait_lt<(2 * R::NP - 1 - J) * R::IPP>();
+        } else if constexpr (J <= 8) {
+          vm_wait_lt<(9 - J) * R::IPP>();
+        } else if constexpr (J == 9) {
+          if (more)
+            vm_wait_lt<R::IPP>();
+          else
+            vm_wait_lt<0>();
+        }
+      } else {
+        if constexpr (J + R::AHEAD < 2 * R::NP) {
+          issue(pid, tok0, J + R::AHEAD);
+        } else {
+          if (more) issue(npid, next, J + R::AHEAD - 2 * R::NP);
+        }
+        // Wait for piece J: the loads issued after it may stay in flight.
+        if constexpr (J + R::AHEAD < 2 * R::NP) {
+          vm_wait_lt<R::AHEAD * R::IPP>();
+        } else {
+          if (more)
+            vm_wait_lt<R::AHEAD * R::IPP>();
+          else
+            vm_wait_lt<(2 * R::NP - 1 - J) * R::IPP>();
+        }
       }
       const char* slot = lds + R::SLOT * (J % R::NP);
       if constexpr (J < R::NP) {
@@ -811,14 +972,14 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
         if constexpr (J == R::NP - 1) softmax(tok0);
       } else {
         constexpr int B = J - R::NP;
-        const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
+        const bool edge = tok0 < kv_lo || tok0 + kTile > kv_hi;  // uniform
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int kr = 4 * qg + t;
           floatx4 vv = *reinterpret_cast<const floatx4*>(slot + R::PW * kr + 16 * (c ^ kr));
           if (__builtin_expect(edge, 0)) {
             const int key = tok0 + kr;
-            if (key < lo || key >= L) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
+            if (key < kv_lo || key >= kv_hi) vv = floatx4{0.f, 0.f, 0.f, 0.f};  // padding never reaches O
           }
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) acc[B][jj] = mma_f32(vv[jj], p[t], acc[B][jj]);
@@ -895,28 +1056,28 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
     }
   }
 
-  // Quarter state: sum l over the lane groups; park (m, l, O) for the workgroup merge.
+  // Quarter state: sum l over the lane groups; park (m, l, O) of all 16 columns for the
+  // workgroup merge (an idle column parks the empty state).  Each wave parks in its own
+  // region, which only it has used.
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  using Parked = QuarterState<D, G>;
+  using Parked = QuarterState<D, 16>;
   Parked* mine = reinterpret_cast<Parked*>(lds);
-  if (c < G) {
-    if (qg == 0) {
-      mine->m[c] = poison ? __builtin_nanf("") : m_run;
-      mine->l[c] = l_run;
-    }
-#pragma unroll
-    for (int b = 0; b < S::VBLOCKS; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        mine->o[c][(64 * b + 16 * qg + 4 * i) / 4] =
-            floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+  if (qg == 0) {
+    mine->m[c] = poison ? __builtin_nanf("") : m_run;
+    mine->l[c] = l_run;
   }
+#pragma unroll
+  for (int b = 0; b < S::VBLOCKS; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mine->o[c][(64 * b + 16 * qg + 4 * i) / 4] =
+          floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
   __syncthreads();
   const Parked* parked[kWavesPerBlock];
 #pragma unroll
   for (int w = 0; w < kWavesPerBlock; ++w) parked[w] = reinterpret_cast<const Parked*>(region[w]);
-  write_chunk_state<D, G>(a, parked, r, g, chunk);
+  write_f32_states<D, G, PREFILL>(a, parked, g, chunk, qs0, row0, rows);
 }
 
 // Write one query row's chunk state: low columns added onto the high ones, maximum in
@@ -1199,18 +1360,98 @@ struct WriteArgs {
   const float* k;
   const float* v;
   const int32_t* start_pos;
-  uint16_t* pool;
+  char* pool;
   const int32_t* table;
   int32_t* bad_rows;
+  // Pool strides and column offsets in bytes.
   int64_t page_stride, head_stride, row_stride, k_offset, v_offset, num_pages;
   int32_t num_kv_heads, head_dim, kcols, num_new, page_size, max_pages;
+  float k_scale, v_scale;  // written value = x / factor (the decode multiplies back)
+};
+
+// One stored element type's encoding of 8 consecutive float32 values (16 bytes of bf16 or
+// f16, 8 of FP8, 32 of f32), stored at dst.
+template <int KV>
+struct Writer;
+
+template <>
+struct Writer<ATTN_KV_BF16> {  // nearest, ties to even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ void put(char* dst, floatx4 x0, floatx4 x1) {
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = (__bf16)x0[e];
+      y[e + 4] = (__bf16)x1[e];
+    }
+    *reinterpret_cast<bf16x8*>(dst) = y;
+  }
+};
+
+template <>
+struct Writer<ATTN_KV_F16> {  // IEEE binary16, nearest, ties to even; overflow to infinity
+  static __device__ __forceinline__ void put(char* dst, floatx4 x0, floatx4 x1) {
+    halfx8 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = (_Float16)x0[e];
+      y[e + 4] = (_Float16)x1[e];
+    }
+    *reinterpret_cast<halfx8*>(dst) = y;
+  }
+};
+
+template <>
+struct Writer<ATTN_KV_F32> {
+  static __device__ __forceinline__ void put(char* dst, floatx4 x0, floatx4 x1) {
+    *reinterpret_cast<floatx4*>(dst) = x0;
+    *reinterpret_cast<floatx4*>(dst + 16) = x1;
+  }
+};
+
+// OCP E4M3 code of a float32: nearest representable value, a tie to the even mantissa;
+// magnitudes from 448 up (infinity included) saturate to 448, NaN gives S.1111.111, and
+// the sign of a result that rounds to zero is kept.
+__device__ __forceinline__ unsigned e4m3_code(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const unsigned sgn = (u >> 24) & 0x80u;
+  const unsigned a = u & 0x7FFFFFFFu;
+  unsigned mag;
+  if (a > 0x7F800000u) {
+    mag = 0x7Fu;                                            // NaN
+  } else if (a >= 0x43E00000u) {
+    mag = 0x7Eu;                                            // >= 448: saturate
+  } else if (a < 0x3C800000u) {
+    // below the smallest normal 2^-6: subnormal steps of 2^-9 (exact scaling, then round
+    // half to even); 8 steps is the smallest normal, code 0x08
+    mag = unsigned(__builtin_rintf(__builtin_fabsf(x) * 512.0f));
+  } else {
+    // keep 3 of the 23 mantissa bits, rounding half to even (a carry moves the exponent);
+    // the exponent bias goes from 127 to 7
+    mag = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sgn | mag;
+}
+
+template <>
+struct Writer<ATTN_KV_FP8_E4M3> {
+  static __device__ __forceinline__ void put(char* dst, floatx4 x0, floatx4 x1) {
+    u32x2 y;
+    y[0] = e4m3_code(x0[0]) | (e4m3_code(x0[1]) << 8) | (e4m3_code(x0[2]) << 16) |
+           (e4m3_code(x0[3]) << 24);
+    y[1] = e4m3_code(x1[0]) | (e4m3_code(x1[1]) << 8) | (e4m3_code(x1[2]) << 16) |
+           (e4m3_code(x1[3]) << 24);
+    *reinterpret_cast<u32x2*>(dst) = y;
+  }
 };
 
 // New K/V rows into their pages: one workgroup per (request, token, KV head) row, one
-// thread per 16 output bytes (8 values, read as two 16-byte fp32 loads, rounded to bf16
-// with ties to even).  The row's position and page are workgroup-uniform.  Rows whose
-// position or page is outside the table / pool are skipped and flagged.
+// thread per 8 values (read as two 16-byte fp32 loads, divided by the tensor's factor
+// unless it is 1, encoded as the pool's element type).  The row's position and page are
+// workgroup-uniform.  Rows whose position or page is outside the table / pool are
+// skipped and flagged.
+template <int KV>
 __global__ __launch_bounds__(128) void kv_write_kernel(WriteArgs a) {
+  constexpr int EB = KV == ATTN_KV_FP8_E4M3 ? 1 : KV == ATTN_KV_F32 ? 4 : 2;  // bytes per element
   const int64_t row = blockIdx.x;  // ((r * num_new) + i) * num_kv_heads + g
   const int g = int(row % a.num_kv_heads);
   const int64_t ri = row / a.num_kv_heads;
@@ -1232,24 +1473,28 @@ __global__ __launch_bounds__(128) void kv_write_kernel(WriteArgs a) {
   }
   const float* src;
   int64_t col;
+  float fac;
   if (pc < kp) {
     src = a.k + row * a.kcols + 8 * pc;
-    col = a.k_offset + 8 * pc;
+    col = a.k_offset + 8 * EB * pc;
+    fac = a.k_scale;
   } else {
     src = a.v + row * a.head_dim + 8 * (pc - kp);
-    col = a.v_offset + 8 * (pc - kp);
+    col = a.v_offset + 8 * EB * (pc - kp);
+    fac = a.v_scale;
   }
-  const floatx4 x0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src));
-  const floatx4 x1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4));
-  bf16x8 y;
+  floatx4 x0 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src));
+  floatx4 x1 = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(src + 4));
+  if (fac != 1.0f) {  // x / factor, one correctly rounded division each (exact for 1)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    y[e] = (__bf16)x0[e];
-    y[e + 4] = (__bf16)x1[e];
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = __fdiv_rn(x0[e], fac);
+      x1[e] = __fdiv_rn(x1[e], fac);
+    }
   }
-  uint16_t* dst = a.pool + int64_t(pid) * a.page_stride + int64_t(g) * a.head_stride +
-                  (pos % a.page_size) * a.row_stride + col;
-  *reinterpret_cast<bf16x8*>(dst) = y;
+  char* dst = a.pool + int64_t(pid) * a.page_stride + int64_t(g) * a.head_stride +
+              (pos % a.page_size) * a.row_stride + col;
+  Writer<KV>::put(dst, x0, x1);
 }
 
 // q' = q with columns rot.. multiplied by the norm weight (one float32 product each).
@@ -1275,11 +1520,10 @@ void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
 
 template <int D, int G, bool FOLDED>
 void launch_split_kv(int kv_dtype, const SplitArgs& args, dim3 grid, hipStream_t s) {
-  if constexpr (!FOLDED) {
-    if (kv_dtype == ATTN_KV_F32) {  // split rows, one query row (checked by the plan)
-      hipLaunchKernelGGL((f32_partial_kernel<D, G>), grid, dim3(64 * kWavesPerBlock), 0, s, args);
-      return;
-    }
+  if (kv_dtype == ATTN_KV_F32) {  // any number of rows; folded rows at head dim 512
+    hipLaunchKernelGGL((f32_partial_kernel<D, G, FOLDED, false>), grid, dim3(64 * kWavesPerBlock),
+                       0, s, args);
+    return;
   }
   switch (kv_dtype) {
     case ATTN_KV_F16: launch_split<D, G, FOLDED, ATTN_KV_F16>(args, grid, s); break;
@@ -1296,6 +1540,52 @@ void launch_merge(const attn_decode_plan_t& p, char* ws, float* out, hipStream_t
               reinterpret_cast<const float*>(ws + p.off_part_o), out, p.num_chunks, p.merge_group};
   hipLaunchKernelGGL((merge_kernel<D>), dim3(D / 128, bh), dim3(256), 0, s, m);
 }
+
+}  // namespace
+
+// Prefill over an f32 pool: the f32 kernel in its prefill mode, one workgroup
+// per R = 16 / G consecutive prompt rows of one (request, KV head).
+void launch_f32_prefill(const attn_prefill_plan_t& p, const float* q, const void* kv_pool,
+                        const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_starts,
+                        float* out, void* stream) {
+  const attn_decode_desc& d = p.desc;
+  SplitArgs args{};
+  const int64_t eb = kv_elem_bytes(d.kv_dtype);
+  args.q = q;
+  args.pool = static_cast<const char*>(kv_pool);
+  args.table = page_table;
+  args.seq_lens = seq_lens;
+  args.page_stride = d.page_stride * eb;
+  args.head_stride = d.head_stride * eb;
+  args.row_stride = d.row_stride * eb;
+  args.k_offset = d.k_offset * eb;
+  args.v_offset = d.v_offset * eb;
+  args.num_pages = d.num_pages;
+  args.num_q_heads = d.num_q_heads;
+  args.page_size = d.page_size;
+  args.max_pages = d.max_pages_per_seq;
+  args.window = d.window;
+  args.qscale_k = d.scale * kLog2e * d.k_scale;
+  args.qscale_v = d.scale * kLog2e * d.v_scale;
+  args.vscale = d.v_scale;
+  args.q_starts = q_starts;
+  args.out = out;
+  args.total_rows = p.total_rows;
+  args.max_rows = p.max_rows;
+  const dim3 grid(p.grid_x, d.num_kv_heads, d.batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
+    hipLaunchKernelGGL((f32_partial_kernel<512, 8, true, true>), grid, dim3(64 * kWavesPerBlock), 0,
+                       s, args);
+  else if (d.head_dim == 512)
+    hipLaunchKernelGGL((f32_partial_kernel<512, 8, false, true>), grid, dim3(64 * kWavesPerBlock), 0,
+                       s, args);
+  else
+    hipLaunchKernelGGL((f32_partial_kernel<256, 2, false, true>), grid, dim3(64 * kWavesPerBlock), 0,
+                       s, args);
+}
+
+namespace {
 
 int launch_status() {
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
@@ -1418,7 +1708,8 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
       !aligned_to(page_table, 4) || !aligned_to(bad_rows, 4))
     return ATTN_E_INVALID_ARG;
   const attn_decode_desc& d = plan->desc;
-  if (d.kv_dtype != ATTN_KV_BF16) return ATTN_E_UNSUPPORTED;
+  if (!kv_dtype_served(d.kv_dtype)) return ATTN_E_UNSUPPORTED;
+  const int64_t eb = kv_elem_bytes(d.kv_dtype);
   const int kcols = d.format == ATTN_KV_FOLDED ? d.rot_cols : d.head_dim;
   const int row_pieces = (kcols + d.head_dim) / 8;  // at most 128 for the supported shapes
   int64_t rows;
@@ -1429,14 +1720,16 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
   a.k = k;
   a.v = v;
   a.start_pos = start_pos;
-  a.pool = static_cast<uint16_t*>(kv_pool);
+  a.pool = static_cast<char*>(kv_pool);
   a.table = page_table;
   a.bad_rows = bad_rows;
-  a.page_stride = d.page_stride;
-  a.head_stride = d.head_stride;
-  a.row_stride = d.row_stride;
-  a.k_offset = d.k_offset;
-  a.v_offset = d.v_offset;
+  a.page_stride = d.page_stride * eb;
+  a.head_stride = d.head_stride * eb;
+  a.row_stride = d.row_stride * eb;
+  a.k_offset = d.k_offset * eb;
+  a.v_offset = d.v_offset * eb;
+  a.k_scale = d.k_scale;
+  a.v_scale = d.v_scale;
   a.num_pages = d.num_pages;
   a.num_kv_heads = d.num_kv_heads;
   a.head_dim = d.head_dim;
@@ -1445,8 +1738,14 @@ extern "C" int attn_kv_write(const attn_decode_plan_t* plan, const float* k, con
   a.page_size = d.page_size;
   a.max_pages = d.max_pages_per_seq;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kv_write_kernel, dim3(unsigned(rows)), dim3(row_pieces), 0,
-                     static_cast<hipStream_t>(stream), a);
+  const dim3 grid{unsigned(rows)}, block{unsigned(row_pieces)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d.kv_dtype) {
+    case ATTN_KV_F16: hipLaunchKernelGGL(kv_write_kernel<ATTN_KV_F16>, grid, block, 0, s, a); break;
+    case ATTN_KV_FP8_E4M3: hipLaunchKernelGGL(kv_write_kernel<ATTN_KV_FP8_E4M3>, grid, block, 0, s, a); break;
+    case ATTN_KV_F32: hipLaunchKernelGGL(kv_write_kernel<ATTN_KV_F32>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(kv_write_kernel<ATTN_KV_BF16>, grid, block, 0, s, a); break;
+  }
   return launch_status();
 }
 

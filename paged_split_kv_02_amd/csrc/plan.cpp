@@ -54,7 +54,6 @@ bool kv_dtype_served(int kv_dtype) {
 
 bool shape_supported(const attn_decode_desc& d) {
   if (!kv_dtype_served(d.kv_dtype)) return false;
-  if (d.kv_dtype == ATTN_KV_F32 && d.format != ATTN_KV_SPLIT) return false;  // split rows only
   const int g = d.num_q_heads / d.num_kv_heads;
   if (d.head_dim == 512 && g == 8) {
     if (d.format == ATTN_KV_SPLIT) return d.rot_cols == 0;
@@ -118,8 +117,12 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   // Query rows: 1 = ordinary decode; a window of n rows uses groups of four rows.
   const int64_t rows = d.num_rows < 1 ? 1 : d.num_rows;
   if (rows > kMaxRows) return ATTN_E_INVALID_ARG;
-  if (rows > 1 && d.kv_dtype == ATTN_KV_F32) return ATTN_E_UNSUPPORTED;  // one query row
-  const int64_t groups = rows > 1 ? ceil_div(rows, kWavesPerBlock) : 1;
+  // Row groups: four rows per workgroup on the 16-bit kernels (one per wave, or a quarter of
+  // the dims each); f32 pools put 16 / G rows of the G heads in the 16 MFMA columns, and
+  // every wave streams a quarter of the chunk for all of them.
+  const bool f32 = d.kv_dtype == ATTN_KV_F32;
+  const int64_t per_group = f32 ? 16 / (d.num_q_heads / d.num_kv_heads) : kWavesPerBlock;
+  const int64_t groups = rows > 1 ? ceil_div(rows, per_group) : 1;
 
   // Keys per tile of the partial kernel the shape runs on.
   const int64_t T = rows_on_tiles(d, rows) ? kPrefillKeys : kTile;
@@ -144,12 +147,15 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   // tile.  Several rows: the four waves share each tile (one row each on the 16-key
   // kernel, a quarter of the dims each on the 32-key one), so a chunk is whole tiles.
   // An explicit count is honoured (trailing chunks may then be empty).
-  const int64_t split = rows > 1 ? 1 : kWavesPerBlock;  // waves a chunk is cut into
+  const int64_t split = (rows > 1 && !f32) ? 1 : kWavesPerBlock;  // waves a chunk is cut into
   const int64_t tiles = ceil_div(max_span, T);
   int64_t n = d.num_chunks;
   if (n == 0) {
     const int64_t units = int64_t(d.batch) * d.num_kv_heads * groups;
-    n = ceil_div(kTargetWaves / kWavesPerBlock, units);
+    // One row at head dim 256: the kernel's registers and LDS tiles allow two workgroups
+    // per CU (two waves per SIMD), so the chip takes twice as many chunks in one round.
+    const int64_t per_cu = (rows == 1 && d.head_dim == 256) ? 2 : 1;
+    n = ceil_div(per_cu * kTargetWaves / kWavesPerBlock, units);
     const int64_t most = ceil_div(tiles, split);
     if (n > most) n = most;
     if (n < 1) n = 1;
@@ -245,7 +251,9 @@ bool rows_on_tiles(const attn_decode_desc& d, int64_t rows) {
 }
 
 bool prefill_shape_supported(const attn_decode_desc& d) {
-  return shape_supported(d) && tile_dtype(d) && d.page_size % kPrefillKeys == 0;
+  if (!shape_supported(d)) return false;
+  if (d.kv_dtype == ATTN_KV_F32) return true;  // the f32 kernel's 16-key tiles
+  return (tile_dtype(d) || d.kv_dtype == ATTN_KV_F16) && d.page_size % kPrefillKeys == 0;
 }
 
 int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const int32_t* q_starts,
@@ -255,8 +263,10 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
   const int rc0 = check_desc(d);
   if (rc0 != ATTN_OK) return rc0;
   if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
-  // A tile's rows are addressed with 32-bit byte offsets from its first row.
-  if (!tile_offsets_fit(d)) return ATTN_E_OVERFLOW;
+  const bool f32 = d.kv_dtype == ATTN_KV_F32;
+  // A tile's rows are addressed with 32-bit byte offsets from its first row (the 32-key
+  // tile kernel; the f32 kernel addresses in 64 bits).
+  if (!f32 && !tile_offsets_fit(d)) return ATTN_E_OVERFLOW;
 
   // Rows of request r are q_starts[r] .. q_starts[r + 1] (0 allowed); they are its last
   // positions, so there are at most L_r of them, and L_r fits the table row.
@@ -272,7 +282,11 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
     if (n > max_rows) max_rows = n;
   }
   const int64_t total = q_starts[d.batch];
-  const int64_t row_tile = (d.head_dim == 256 ? 2 : 1) * kPrefillColumns / (d.num_q_heads / d.num_kv_heads);
+  // Rows per workgroup: the 32-key tile kernel's 64 (x2 at head dim 256) columns, or the f32
+  // kernel's 16 MFMA columns, of (row, head) pairs.
+  const int64_t row_tile = f32 ? 16 / (d.num_q_heads / d.num_kv_heads)
+                               : (d.head_dim == 256 ? 2 : 1) * kPrefillColumns /
+                                     (d.num_q_heads / d.num_kv_heads);
   const int64_t tiles = ceil_div(max_rows, row_tile);
   uint64_t elems;
   if (!mul_ok(uint64_t(total), uint64_t(d.num_q_heads) * uint64_t(d.head_dim), &elems) ||
@@ -280,6 +294,7 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
     return ATTN_E_OVERFLOW;
   // One workgroup per (row tile, KV head, request), launched in whole rounds of 256.
   uint64_t heads, items;
+  if (f32 && (d.batch > 65535 || d.num_kv_heads > 65535)) return ATTN_E_OVERFLOW;  // grid y, z
   if (!mul_ok(uint64_t(d.num_kv_heads), uint64_t(d.batch), &heads) ||
       !mul_ok(uint64_t(tiles), heads, &items) || items > uint64_t(INT32_MAX - 255))
     return ATTN_E_OVERFLOW;
@@ -289,7 +304,7 @@ int make_prefill_plan(const attn_decode_desc* desc, const int32_t* lens, const i
   p.magic = kPrefillMagic;
   p.desc = d;
   p.group_size = d.num_q_heads / d.num_kv_heads;
-  p.key_tile = kPrefillKeys;
+  p.key_tile = f32 ? kTile : kPrefillKeys;
   p.row_tile = int32_t(row_tile);
   p.total_rows = int32_t(total);
   p.max_rows = int32_t(max_rows);

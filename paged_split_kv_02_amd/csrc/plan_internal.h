@@ -42,6 +42,10 @@ void launch_rows_tiles(const attn_decode_plan_t& p, const float* q, const void* 
                        const int32_t* page_table, const int32_t* seq_lens,
                        const uint64_t* row_masks, float* part_m, float* part_l, float* part_o,
                        void* stream);
+// Prefill over an f32 pool on the f32 decode kernel's prefill mode.
+void launch_f32_prefill(const attn_prefill_plan_t& p, const float* q, const void* kv_pool,
+                        const int32_t* page_table, const int32_t* seq_lens, const int32_t* q_starts,
+                        float* out, void* stream);
 int check_plan(const attn_decode_plan_t* plan);
 int check_workspace(const attn_decode_plan_t* plan, const void* ws, size_t bytes);
 

@@ -39,7 +39,7 @@
 // The hot loop never rescales the accumulators (that would move them through the vector
 // registers every tile): a column's reference maximum is fixed by its first tile with a
 // visible key, when nothing has been accumulated yet, and probabilities may then grow to
-// 2^kHeadroom.  A larger score only raises a flag, and the workgroup recomputes its rows in
+// 2^kHeadroom (64 for bf16 operands, 15 for f16).  A larger score only raises a flag, and the workgroup recomputes its rows in
 // a second loop that does rescale.
 #include <hip/hip_runtime.h>
 
@@ -52,6 +52,7 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -62,9 +63,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // slow path: log2 units a tile may exceed the reference
 constexpr int kKeys = kPrefillKeys;    // keys per tile: the 32 rows of one MFMA block
-// Without rescaling, probabilities may reach 2^kHeadroom (log2 units above a column's
-// reference): far inside fp32 and bf16 range, with room for any sum of them.
-constexpr float kHeadroom = 64.0f;
 constexpr int kCols = 32;              // MFMA columns of a column block
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts, and the
 // loads' cache policy: non-temporal (bit 1 on gfx94x / gfx950) for decode windows, whose
@@ -139,11 +137,34 @@ __device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// D = A B + C on the 32x32x16 bf16 MFMA.  Lane l holds A[l % 32][8(l / 32) + j] and
+// MFMA operand type of a pool element type: bf16 for bf16 and FP8 E4M3 rows (every E4M3
+// value is a bf16 value), f16 for f16 rows; fp32 accumulation either way.
+// D = A B + C on the 32x32x16 MFMA.  Lane l holds A[l % 32][8(l / 32) + j] and
 // B[8(l / 32) + j][l % 32] (j = 0..7); element r of D is D[8(r / 4) + 4(l / 32) + r % 4][l % 32].
-__device__ __forceinline__ floatx16 mma(u32x4 a, bf16x8 b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
-}
+template <bool F16>
+struct POps;
+
+template <>
+struct POps<false> {
+  typedef __bf16 T;
+  typedef bf16x8 T8;
+  // Largest log2 distance a probability may sit above its column's reference in the
+  // loop that never rescales (fp32 and bf16 reach 2^127).
+  static constexpr float kHeadroom = 64.0f;
+  static __device__ __forceinline__ floatx16 mma(u32x4 a, T8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(T8, a), b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct POps<true> {
+  typedef _Float16 T;
+  typedef halfx8 T8;
+  static constexpr float kHeadroom = 15.0f;  // f16 reaches 65504 < 2^16
+  static __device__ __forceinline__ floatx16 mma(u32x4 a, T8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(T8, a), b, c, 0, 0, 0);
+  }
+};
 
 // Two E4M3 codes (bytes 2HI, 2HI + 1 of w) to a packed bf16 pair: exact, since every E4M3
 // value is a bf16 value.
@@ -204,8 +225,12 @@ __device__ __forceinline__ int pv_key(int t, int hh, int j) {
 //     chunk of one group of four rows (32 columns = 4 rows x 8 heads, each of the four
 //     waves holding a quarter of the dims), and the chunk's unnormalised state (m in
 //     natural-log units, l, O) is written for the merge, as by the one-row decode kernels.
-template <int D, int G, bool FOLDED, bool CHUNKED, bool FP8>
+template <int D, int G, bool FOLDED, bool CHUNKED, int KV>
 __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
+  constexpr bool FP8 = KV == ATTN_KV_FP8_E4M3;
+  using O = POps<KV == ATTN_KV_F16>;
+  using T = typename O::T;
+  using T8 = typename O::T8;
   constexpr int SPLIT = CHUNKED ? 4 : (D == 512 ? 2 : 1);  // waves sharing a column block
   // Staged through registers: decode windows (to keep tiles in flight) and FP8 pools (to
   // widen the codes to bf16 on their way into LDS).  Prefill keeps one tile ahead.
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 
   // Query operand (B of the QK MFMA): lane (n, hh), step s holds dims
   // half * HALF + 16s + 8hh + [0, 8) of column n, as a high and a low bf16 part.
-  bf16x8 qhi[S::KSTEPS], qlo[S::KSTEPS];
+  T8 qhi[S::KSTEPS], qlo[S::KSTEPS];
   {
     // Inactive columns read row 0 (always present) and use zeros.
     const float* qp = a.q + (int64_t(qs0) + (active ? qrow : 0)) * a.num_q_heads * D +
@@ -436,9 +461,9 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = active ? xq[s][e >> 2][e & 3] * qs : 0.0f;
-        const __bf16 h = (__bf16)x;
+        const T h = (T)x;
         qhi[s][e] = h;
-        qlo[s][e] = (__bf16)(x - (float)h);
+        qlo[s][e] = (T)(x - (float)h);
       }
       // Park the query operand in the accumulation registers, leaving the vector registers
       // to the tile work (it is copied back next to each use).
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
   float m_run, l_run;
   float m_top;              // decode windows: the largest score seen (the state's final m)
   floatx16 acc[DPR];        // step jj: element r <-> dim half*HALF + DPR*(8(r/4) + 4hh + r%4) + jj
-  bool overflow = false;    // a score exceeded the reference by more than kHeadroom
+  bool overflow = false;    // a score exceeded the reference by more than O::kHeadroom
 
   // One staged tile (keys k0 .. k0 + 31) for this wave's dims of its block's 32 columns.
   auto compute = [&](const char* t, int k0, auto rescale) {
@@ -482,8 +507,8 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
       const u32x4 kf = kq[s % KA];
       if (s + KA < S::KSTEPS) kq[s % KA] = kfrag(s + KA);
       __builtin_amdgcn_sched_barrier(0);
-      sp = mma(kf, qhi[s], sp);
-      sq = mma(kf, qlo[s], sq);
+      sp = O::mma(kf, qhi[s], sp);
+      sq = O::mma(kf, qlo[s], sq);
       __builtin_amdgcn_sched_barrier(0);
     }
     sp += sq;
@@ -560,21 +585,21 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
       }
     } else {
       if (m_run == -INFINITY) m_run = mx;  // first visible tile: nothing accumulated yet
-      overflow |= mx > m_run + kHeadroom;
+      overflow |= mx > m_run + O::kHeadroom;
     }
     // Probabilities as the PV B operands: MFMA t takes elements 8t .. 8t + 7.
     // A reference still unset means every score of the column so far is -inf: any finite
     // stand-in gives the zero probabilities.
-    bf16x8 phi[2], plo[2];
+    T8 phi[2], plo[2];
     float psum = 0.0f;
     const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(sc[e] - m_ref);
       psum += p;
-      const __bf16 h = (__bf16)p;
+      const T h = (T)p;
       phi[e >> 3][e & 7] = h;
-      plo[e >> 3][e & 7] = (__bf16)(p - (float)h);
+      plo[e >> 3][e & 7] = (T)(p - (float)h);
     }
     l_run += psum;
 
@@ -617,10 +642,10 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
           ev[u] = perm(w[2 * u + 1][dd], w[2 * u][dd], 0x05040100u);
           od[u] = perm(w[2 * u + 1][dd], w[2 * u][dd], 0x07060302u);
         }
-        acc[2 * dd] = mma(ev, phi[tt], acc[2 * dd]);
-        acc[2 * dd + 1] = mma(od, phi[tt], acc[2 * dd + 1]);
-        acc[2 * dd] = mma(ev, plo[tt], acc[2 * dd]);
-        acc[2 * dd + 1] = mma(od, plo[tt], acc[2 * dd + 1]);
+        acc[2 * dd] = O::mma(ev, phi[tt], acc[2 * dd]);
+        acc[2 * dd + 1] = O::mma(od, phi[tt], acc[2 * dd + 1]);
+        acc[2 * dd] = O::mma(ev, plo[tt], acc[2 * dd]);
+        acc[2 * dd + 1] = O::mma(od, plo[tt], acc[2 * dd + 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -745,9 +770,16 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
 template <int D, int G, bool FOLDED, bool CHUNKED>
 void launch_rows_tile(const PrefillArgs& args, int kv_dtype, dim3 grid, hipStream_t s) {
   if (kv_dtype == ATTN_KV_FP8_E4M3)
-    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, true>), grid, dim3(256), 0, s, args);
-  else
-    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, false>), grid, dim3(256), 0, s, args);
+    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, ATTN_KV_FP8_E4M3>), grid, dim3(256),
+                       0, s, args);
+  else if (kv_dtype == ATTN_KV_F16) {
+    if constexpr (!CHUNKED)  // prompts only: decode windows over f16 rows run elsewhere
+      hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, ATTN_KV_F16>), grid, dim3(256),
+                         0, s, args);
+  } else {
+    hipLaunchKernelGGL((rows_tile_kernel<D, G, FOLDED, CHUNKED, ATTN_KV_BF16>), grid, dim3(256),
+                       0, s, args);
+  }
 }
 
 // Pool geometry and query scaling shared by both uses.
@@ -792,6 +824,11 @@ extern "C" int attn_prefill(const attn_prefill_plan_t* plan, const float* q, con
   if (!prefill_shape_supported(d)) return ATTN_E_UNSUPPORTED;
   if (plan->total_rows == 0) return ATTN_OK;
 
+  if (d.kv_dtype == ATTN_KV_F32) {
+    (void)hipGetLastError();
+    launch_f32_prefill(*plan, q, kv_pool, page_table, seq_lens, q_starts, out, stream);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+  }
   PrefillArgs args;
   fill_common(args, d, q, kv_pool, page_table, seq_lens);
   args.out = out;

@@ -159,7 +159,9 @@ int main() {
       ++p_accepted;
       for (int32_t L : lens)
         if (int64_t(L) > int64_t(I32MAX) - 1024) return fail("prefill length near 2^31", it);
-      if (pp.grid_x < 0 || pp.row_tile < 1 || pp.key_tile != 32) return fail("prefill plan fields", it);
+      const int32_t key_tile = d.kv_dtype == ATTN_KV_F32 ? 16 : 32;
+      if (pp.grid_x < 0 || pp.row_tile < 1 || pp.key_tile != key_tile)
+        return fail("prefill plan fields", it);
     }
   }
   for (int s = -10; s <= 2; ++s)

@@ -1,7 +1,8 @@
 """GPU parity for the pool element types other than bf16: f16 rows (multiplied on
 f16 MFMA), FP8 E4M3 rows with K and V dequantisation factors (widened to bf16
-on their way into LDS), and f32 rows (split rows, one query row; multiplied in full fp32
-on the fp32 MFMA), against the fp64 oracle at the same bar as bf16."""
+on their way into LDS), and f32 rows (split or folded; multiplied in full fp32 on the fp32
+MFMA, R = 16 / G query rows in its 16 columns), against the fp64 oracle at the same bar as
+bf16."""
 import numpy as np
 import pytest
 import torch
@@ -15,14 +16,12 @@ from tests.test_gpu_parity import check, check_partials, run_case
 pytestmark = pytest.mark.gpu
 
 DTYPES = [synth.F16, synth.FP8]
-ALL_DTYPES = DTYPES + [synth.F32]   # f32: split rows and one query row only
+ALL_DTYPES = DTYPES + [synth.F32]
 
 
 @pytest.mark.parametrize("fmt", ["split", "folded"])
 @pytest.mark.parametrize("dt", ALL_DTYPES)
 def test_global_ragged(dt, fmt):
-    if dt == synth.F32 and fmt == "folded":
-        pytest.skip("f32 pools hold split rows (the plan refuses folded f32)")
     wl = synth.make_workload([1000, 333, 17], **synth.GLOBAL, fmt=fmt, seed=70, kv_dtype=dt,
                              spare_pages=3, pad="nan")
     for n in (0, 9):
@@ -59,7 +58,7 @@ def test_sliding_batch(dt):
     check(got, oracle.decode_attention(wl), f"{dt} sliding")
 
 
-@pytest.mark.parametrize("dt", DTYPES)
+@pytest.mark.parametrize("dt", ALL_DTYPES)
 @pytest.mark.parametrize("rows", [3, 4])
 def test_rows(dt, rows):
     wl = synth.make_workload([2000, rows + 6], **synth.GLOBAL, seed=74 + rows, kv_dtype=dt,
@@ -98,7 +97,8 @@ def test_fp8_widening_is_exact(rows):
 
 
 @pytest.mark.parametrize("dt,fmt", [(synth.FP8, "split"), (synth.FP8, "folded"),
-                                    (synth.F16, "split"), (synth.F32, "split")])
+                                    (synth.F16, "split"), (synth.F32, "split"),
+                                    (synth.F32, "folded")])
 def test_full_length_163k(dt, fmt):
     note(f"[gpu] {dt} {fmt} L=163336: generating")
     wl = synth.global_decode(163336, seed=79, fmt=fmt, kv_dtype=dt)
@@ -109,11 +109,51 @@ def test_full_length_163k(dt, fmt):
     check(got, oracle.decode_attention(wl), f"{dt} {fmt} 163K")
 
 
-def test_f32_refusals():
-    """f32 pools: folded rows and several query rows are refused by the plan."""
-    wl = synth.make_workload([100], **synth.GLOBAL, fmt="folded", seed=80, kv_dtype=synth.F32)
-    with pytest.raises(K.AttnDecodeError):
-        K.attn_decode_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens)
-    wl = synth.make_workload([100], **synth.GLOBAL, seed=80, kv_dtype=synth.F32, num_rows=2)
-    with pytest.raises(K.AttnDecodeError):
-        K.attn_decode_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens)
+@pytest.mark.parametrize("shape,rows", [("global", 2), ("global", 7), ("sliding", 8),
+                                        ("sliding", 13), ("folded", 3), ("sliding-late", 5)])
+def test_f32_rows_groups_and_chunks(shape, rows):
+    """f32 windows of several rows: R = 16 / G rows share the 16 MFMA columns (2 at head dim
+    512, 8 at 256), more rows take further row groups; automatic and explicit chunk counts,
+    a window crossing pages, NaN padding."""
+    if shape in ("global", "folded"):
+        wl = synth.make_workload([2500, rows + 20, 700], **synth.GLOBAL, seed=81 + rows,
+                                 kv_dtype=synth.F32, num_rows=rows, pad="nan", spare_pages=2,
+                                 fmt="split" if shape == "global" else "folded")
+    elif shape == "sliding":
+        wl = synth.make_workload([1500, rows + 3, 1030], **synth.SLIDING, seed=81 + rows,
+                                 kv_dtype=synth.F32, num_rows=rows, pad="nan", max_pages=40)
+    else:
+        # the first tile holds keys only the first rows of the window see (their windows
+        # start 14 .. 18 keys into it): the later rows' columns have no visible key yet while
+        # the first rows' columns move their maximum, and must keep their empty sums
+        wl = synth.make_workload([2674, 2944, 1818], **synth.SLIDING, seed=81 + rows,
+                                 kv_dtype=synth.F32, num_rows=rows, pad="big")
+    ref = oracle.decode_attention(wl)
+    for n in (0, 5):
+        dev, got = run_case(wl, f"f32 {shape} rows={rows} n={n}", num_chunks=n)
+        check(got, ref, f"f32 {shape} rows={rows} n={n}")
+
+
+def test_f32_rows_partials_per_chunk():
+    """Each chunk state of a 3-row f32 window against the oracle's state of the keys that
+    row sees in that chunk."""
+    import math
+    wl = synth.make_workload([900], **synth.GLOBAL, seed=85, kv_dtype=synth.F32, num_rows=3)
+    dev, got = run_case(wl, "f32 rows=3 partials n=5", num_chunks=5)
+    m, l, o = dev.partials()
+    ranges = dev.chunk_ranges(0)
+    for row in range(3):
+        for g in range(4):
+            states = oracle.paged_partials(wl, 0, g, ranges, row=row)
+            for i in range(8):
+                h = g * 8 + i
+                for c, st in enumerate(states[i]):
+                    if st.m == -math.inf:
+                        assert m[row, h, c] == -np.inf and l[row, h, c] == 0
+                        continue
+                    mg = float(m[row, h, c])
+                    assert st.m - 8 * math.log(2) - 1e-5 <= mg <= st.m + 1e-5 * max(1, abs(st.m))
+                    k = math.exp(mg - st.m)
+                    assert abs(l[row, h, c] * k - st.l) <= 1e-5 * st.l
+                    assert np.max(np.abs(o[row, h, c] * k / st.l - st.acc / st.l)) <= 1e-4
+    check(got, oracle.decode_attention(wl), "f32 rows partial case")

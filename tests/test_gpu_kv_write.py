@@ -20,15 +20,18 @@ def _t(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
 
 
+_SIGNED = {np.dtype(np.uint16): np.int16, np.dtype(np.uint8): np.uint8, np.dtype(np.uint32): np.int32}
+
+
 def _write_on_gpu(wl, k, v, start, expect_bad=False):
     plan = K.attn_decode_plan(K.make_desc(**wl.desc_fields()), wl.seq_lens)
-    pool = _t(wl.pool.view(np.int16))
+    pool = _t(wl.pool.view(_SIGNED[wl.pool.dtype]))
     bad = torch.zeros(1, dtype=torch.int32, device=DEV)
     K.attn_kv_write(plan, _t(k), _t(v), k.shape[1], _t(np.asarray(start, dtype=np.int32)), pool,
                     _t(wl.table), bad)
     torch.cuda.synchronize()
     assert int(bad.item()) == int(expect_bad)
-    return pool.cpu().numpy().view(np.uint16)
+    return pool.cpu().numpy().view(wl.pool.dtype)
 
 
 @pytest.mark.parametrize("fmt,layout,n", [("split", synth.HEAD_MAJOR, 37), ("folded", synth.TOKEN_MAJOR, 37),
@@ -102,3 +105,73 @@ def test_append_then_decode(fmt):
     if fmt == "folded":
         ref_wl.q = oracle.fold_query(wl.q_unfolded, wl.fold_w, 128)
     check(got, oracle.decode_attention(ref_wl), f"append+decode {fmt}")
+
+
+def _hard_values(rng, shape, dt, factor):
+    """Random values with the encodings' hard cases planted: exact E4M3 midpoints (ties),
+    saturating and tiny magnitudes, f16 overflow and subnormals, signed zeros, and (FP8)
+    NaN, all scaled by the tensor's factor so that the quotient hits them."""
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(2.0)
+    flat = x.reshape(-1)
+    if dt == "fp8_e4m3":
+        g = oracle.e4m3_bits_to_f64(np.arange(0x7F, dtype=np.uint8))
+        special = np.concatenate([(g[:-1] + g[1:]) / 2, g, [449.0, 480.0, 1e6, np.inf, 2.0 ** -11,
+                                                            0.0, -0.0, np.nan]])
+    elif dt == "f16":
+        special = np.array([65504.0, 65520.0, 1e6, np.inf, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25,
+                            1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 0.0, -0.0])
+    else:
+        special = np.array([np.inf, 1e-40, 3.4e38, 0.0, -0.0])
+    special = np.concatenate([special, -special]).astype(np.float32) * np.float32(factor)
+    idx = rng.choice(flat.size, size=special.size, replace=False)
+    flat[idx] = special
+    return x
+
+
+@pytest.mark.parametrize("dt,fmt,factors", [("f16", "split", (1.0, 1.0)),
+                                            ("fp8_e4m3", "split", (1.0, 1.0)),
+                                            ("fp8_e4m3", "folded", (None, None)),
+                                            ("fp8_e4m3", "split", (None, None)),
+                                            ("f32", "split", (1.0, 1.0)),
+                                            ("f16", "folded", (0.5, 2.0))])
+def test_write_rows_other_types_bit_exact(dt, fmt, factors):
+    """f16, FP8 E4M3 and f32 pools: every written element equals the oracle's encoding of
+    value / factor (nearest with ties to even; FP8 saturating at 448, NaN kept), over the
+    whole pool; the pool's own factors (FP8: 0.0175 / 0.0225) or unit ones."""
+    note(f"[gpu] kv write {dt} {fmt} factors={factors}")
+    kw = {} if factors[0] is None else dict(k_scale=factors[0], v_scale=factors[1])
+    wl = synth.make_workload([700, 520], **synth.GLOBAL, fmt=fmt, seed=30, spare_pages=2,
+                             kv_dtype=dt, **kw)
+    rng = np.random.default_rng(31)
+    n = 64
+    kc = 512 if fmt == "split" else 128
+    k = _hard_values(rng, (2, n, 4, kc), dt, wl.k_scale)
+    v = _hard_values(rng, (2, n, 4, 512), dt, wl.v_scale)
+    start = [700 - n, 100]
+    got = _write_on_gpu(wl, k, v, start)
+    ref = oracle.write_rows(wl, k, v, np.array(start))
+    assert got.dtype == ref.dtype
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dt", ["f16", "fp8_e4m3", "f32"])
+def test_append_then_decode_other_types(dt):
+    """A decode step over an f16, FP8 or f32 pool after the library writes the new token's
+    row (FP8 with its factors): the step equals the oracle on the oracle-written pool."""
+    note(f"[gpu] append + decode {dt}")
+    lens = [3000, 640]
+    wl = synth.make_workload(lens, **synth.GLOBAL, seed=32, kv_dtype=dt)
+    rng = np.random.default_rng(33)
+    k = (rng.standard_normal((2, 1, 4, 512)) * 2).astype(np.float32)
+    v = (rng.standard_normal((2, 1, 4, 512)) * 2).astype(np.float32)
+    if dt == "fp8_e4m3":  # values the factors bring inside the FP8 range
+        k *= np.float32(wl.k_scale * 100)
+        v *= np.float32(wl.v_scale * 100)
+    start = np.array(lens, dtype=np.int32) - 1
+    dev = Device(wl)
+    K.attn_kv_write(dev.plan, _t(k), _t(v), 1, _t(start), dev.pool, dev.table)
+    got = dev.run()
+    assert dev.guards_intact()
+    ref_wl = copy.copy(wl)
+    ref_wl.pool = oracle.write_rows(wl, k, v, start)
+    check(got, oracle.decode_attention(ref_wl), f"append+decode {dt}")

@@ -292,3 +292,85 @@ def test_device_mismatches_fail_closed():
     got = PrefillDevice(wl, table=table).run()
     assert np.all(np.isnan(got[350:450]))
     assert np.array_equal(got[:350].view(np.uint32), good[:350].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_f16_global_ragged(fmt):
+    """f16 pools: rows multiplied on the f16 MFMA (query and probabilities as high and low
+    f16 parts); ragged prompts, a continuation, a one-row and a zero-row request."""
+    wl = synth.make_workload([300, 610, 1, 45, 257], **synth.GLOBAL, fmt=fmt, seed=220,
+                             q_lens=[300, 37, 1, 0, 257], spare_pages=3, pad="nan",
+                             kv_dtype=synth.F16)
+    _, got = run_case(wl, f"f16 global {fmt} ragged")
+    check(got, oracle.prefill_attention(wl), f"f16 global {fmt} ragged")
+
+
+def test_f16_sliding_window_cases():
+    wl = synth.make_workload([1300, 1500, 70, 1], **synth.SLIDING, seed=221, kv_dtype=synth.F16,
+                             q_lens=[1300, 150, 70, 1], max_pages=40, pad="nan")
+    _, got = run_case(wl, "f16 sliding window cases")
+    rows = list(range(0, 1300, 7)) + list(range(1300, 1521))
+    check(got[rows], oracle.prefill_attention(wl, rows=rows), "f16 sliding window cases")
+
+
+@pytest.mark.parametrize("shape", ["global", "sliding"])
+def test_f16_slow_path_on_a_dominant_key(shape):
+    """f16 operands hold probabilities only up to 65504, so the no-rescale loop allows 2^15
+    above a column's reference: a key planted at position 100 that scores ~23 nat (global) /
+    ~16 nat (sliding) above the rest sends the workgroups of later rows through the
+    rescaling loop (the fast loop would overflow to infinity)."""
+    if shape == "global":
+        wl = synth.make_workload([400], **synth.GLOBAL, seed=222, q_lens=[400], pad="nan",
+                                 kv_dtype=synth.F16)
+    else:
+        wl = synth.make_workload([400], **synth.SLIDING, seed=222, q_lens=[400], pad="nan",
+                                 max_pages=8, kv_dtype=synth.F16)
+    head = 3
+    u = np.ascontiguousarray(wl.q[150, head], dtype=np.float32)
+    wl.q[:, head, :] = u
+    j = 100
+    g = head // (wl.num_q_heads // wl.num_kv_heads)
+    pid = int(wl.table[0][j // wl.page_size])
+    base = (pid * wl.page_stride + g * wl.head_stride + (j % wl.page_size) * wl.row_stride
+            + wl.k_offset)
+    wl.pool[base:base + wl.head_dim] = u.astype(np.float16).view(np.uint16)
+    _, got = run_case(wl, f"f16 dominant key {shape}")
+    check(got, oracle.prefill_attention(wl), f"f16 dominant key {shape}")
+
+
+@pytest.mark.parametrize("fmt", ["split", "folded"])
+def test_f32_global_ragged(fmt):
+    """f32 pools: prompt rows on the f32 kernel's prefill mode, two rows of the eight heads
+    per workgroup, each wave a quarter of the keys; ragged prompts, a continuation, a
+    one-row and a zero-row request, rows crossing pages of 256."""
+    wl = synth.make_workload([300, 610, 1, 45, 257], **synth.GLOBAL, fmt=fmt, seed=230,
+                             q_lens=[300, 37, 1, 0, 257], spare_pages=3, pad="nan",
+                             kv_dtype=synth.F32)
+    dev, got = run_case(wl, f"f32 global {fmt} ragged")
+    assert dev.plan.row_tile == 2 and dev.plan.key_tile == 16
+    check(got, oracle.prefill_attention(wl), f"f32 global {fmt} ragged")
+
+
+def test_f32_sliding_window_cases():
+    """f32, window 1024 over pages of 64: eight rows of the two heads per workgroup; a
+    prompt crossing the window, a continuation, a short and a tiny prompt."""
+    wl = synth.make_workload([1300, 1500, 70, 1], **synth.SLIDING, seed=231, kv_dtype=synth.F32,
+                             q_lens=[1300, 150, 70, 1], max_pages=40, pad="nan")
+    dev, got = run_case(wl, "f32 sliding window cases")
+    assert dev.plan.row_tile == 8
+    rows = list(range(0, 1300, 7)) + list(range(1300, 1521))
+    check(got[rows], oracle.prefill_attention(wl, rows=rows), "f32 sliding window cases")
+
+
+def test_f32_hostile_padding_and_repeat():
+    """NaN or huge values in every slot no row sees leave the f32 prefill's bits unchanged;
+    a second launch gives the same bits."""
+    outs = []
+    for pad in ("nan", "big"):
+        wl = synth.make_workload([200, 700], **synth.GLOBAL, seed=232, q_lens=[200, 90], pad=pad,
+                                 kv_dtype=synth.F32, spare_pages=2)
+        dev, got = run_case(wl, f"f32 padding {pad}")
+        outs.append(got)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert fnv1a(dev.run()) == fnv1a(outs[1])
+    check(outs[0], oracle.prefill_attention(wl), "f32 padding")

@@ -95,8 +95,6 @@ S = K.STATUS
     ([1024], dict(window=-1), "ATTN_E_INVALID_ARG"),
     ([1024], dict(kv_dtype=4), "ATTN_E_INVALID_ARG"),              # unknown element type
     ([1024], dict(kv_dtype=-1), "ATTN_E_INVALID_ARG"),
-    ([1024], dict(kv_dtype=3, format=1, rot_cols=128, v_offset=128), "ATTN_E_UNSUPPORTED"),  # f32: split rows only
-    ([1024], dict(kv_dtype=3, num_rows=2), "ATTN_E_UNSUPPORTED"),  # f32: one query row
     ([1024], dict(k_scale=0.0), "ATTN_E_INVALID_ARG"),
     ([1024], dict(v_scale=-0.5), "ATTN_E_INVALID_ARG"),
     ([1024], dict(k_scale=float("inf")), "ATTN_E_INVALID_ARG"),
@@ -422,6 +420,11 @@ def test_prefill_plan_layout_matches_header(tmp_path):
     assert vals[1:] == [getattr(K.AttnPrefillPlan, f).offset for f in pfields]
 
 
+def test_prefill_plan_accepts_f16():
+    rc, p = prefill_status([1024], [0, 1000], **global_desc(kv_dtype=1))
+    assert rc == 0 and p.row_tile == 8 and p.desc.kv_dtype == 1
+
+
 def test_prefill_plan_accepts_fp8():
     rc, p = prefill_status([1024], [0, 1000], **global_desc(kv_dtype=2, k_scale=0.02, v_scale=0.03))
     assert rc == 0 and p.row_tile == 8 and p.desc.kv_dtype == 2
@@ -445,7 +448,6 @@ def test_prefill_plan_tiles():
     ([1024], [0, 1025], dict(), "ATTN_E_INVALID_ARG"),            # more rows than keys
     ([10, 10], [0, 5, 4], dict(batch=2), "ATTN_E_INVALID_ARG"),   # decreasing offsets
     ([1025], [0, 1], dict(), "ATTN_E_PAST_PAGES"),
-    ([1024], [0, 8], dict(kv_dtype=1), "ATTN_E_UNSUPPORTED"),     # f16: decode only
     ([1024], [0, 8], dict(page_size=16, max_pages_per_seq=64), "ATTN_E_UNSUPPORTED"),
     ([1024], [0, 8], dict(head_dim=128), "ATTN_E_UNSUPPORTED"),
     ([1024], [0, 8], dict(row_stride=1020), "ATTN_E_INVALID_ARG"),
@@ -507,6 +509,7 @@ def test_loaded_library_matches_the_sources():
     assert B.is_current(), "libattn_decode.so is older than its sources"
     assert B.built_digest() == B.source_digest()
 
+
 def test_noalloc_step_refuses_before_any_device_call():
     """The allocation-free step refuses a bad plan, null or misaligned buffers, masks with a
     one-row plan and a plan larger than its static array, all before touching a device."""
@@ -532,3 +535,45 @@ def test_noalloc_step_refuses_before_any_device_call():
     assert N(ctypes.byref(p4), fake, fake, fake, fake, fake + 4, fake, None) == S["ATTN_E_INVALID_ARG"]
     assert N(ctypes.byref(pb), fake, fake, fake, fake, None, fake, None) == S["ATTN_E_SCRATCH"]
 
+
+def test_sliding_plan_fills_two_workgroups_per_cu():
+    """One query row at head dim 256: the kernels fit two workgroups per CU, so the 16-request
+    sliding batch (16 x 16 KV heads) is cut into two chunks per (request, KV head): 512
+    workgroups, two per CU; a shorter request's second chunk is empty."""
+    rng = np.random.default_rng(4)
+    lens = rng.integers(1, 4097, size=16)
+    f = dict(batch=16, num_q_heads=32, num_kv_heads=16, head_dim=256, format=0, rot_cols=0,
+             page_size=64, max_pages_per_seq=64, window=1024, num_chunks=0, merge_group=0,
+             scale=1 / 16, num_pages=300, page_stride=16 * 64 * 512, head_stride=64 * 512,
+             row_stride=512, k_offset=0, v_offset=256)
+    rc, p = plan_status(lens, **f)
+    assert rc == 0 and p.num_chunks == 2 and p.grid_x == 2
+    assert p.num_chunks * 16 * 16 == 512
+
+
+def test_f32_rows_plan():
+    """f32 windows of several rows: 16 / G rows per row group (2 at head dim 512), each wave
+    a quarter of a chunk, 16-key tiles; the row groups of a chunk 8 workgroups apart."""
+    rc, p = plan_status([5000], **global_desc(5000, kv_dtype=3, num_rows=5))
+    assert rc == 0 and p.num_rows == 5 and p.row_groups == 3 and p.tile == 16
+    assert p.chunk_len % (4 * 16) == 0
+    assert p.grid_x == -(-p.num_chunks // 8) * 8 * 3
+
+
+def test_f32_prefill_plan():
+    rc, p = prefill_status([1024], [0, 1000], **global_desc(kv_dtype=3))
+    assert rc == 0 and p.row_tile == 2 and p.key_tile == 16 and p.grid_x == 500
+
+
+def test_f32_folded_plans_accepted():
+    """f32 pools hold split or folded rows, for decode (one or several rows) and prefill."""
+    f = global_desc(kv_dtype=3, format=1, rot_cols=128, v_offset=128, row_stride=640,
+                    head_stride=256 * 640, page_stride=4 * 256 * 640)
+    rc, p = plan_status([1024], **f)
+    assert rc == 0 and p.tile == 16
+    f["num_rows"] = 3
+    rc, p = plan_status([1024], **f)
+    assert rc == 0 and p.row_groups == 2
+    f["num_rows"] = 0
+    rc, p = prefill_status([1024], [0, 100], **f)
+    assert rc == 0 and p.row_tile == 2
