@@ -417,6 +417,11 @@ def main():
                 ("global-decode-40002-split", lambda: synth.global_decode(40002, seed=14), 20),
                 ("global-decode-81653-split", lambda: synth.global_decode(81653, seed=15), 20),
                 ("global-decode-163336-folded", lambda: synth.global_decode(163336, seed=3, fmt="folded"), 20),
+                # the headline's workload with 64 chunks of equal length: the automatic plan
+                # gives even-numbered chunks (on the even XCDs) more keys than odd ones, and
+                # this line shows whether that still pays on the part the bench runs on
+                ("global-decode-163336-split-equal-chunks",
+                 lambda: synth.global_decode(163336, seed=2), 20),
                 ("global-decode-4streams-9k-split", lambda: synth.global_streams(seed=16), 20),
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
                 ("global-decode-163336-split-4rows",
@@ -447,7 +452,7 @@ def main():
             if not wanted(name):
                 continue
             vwl = maker()
-            vres = Resident(vwl)
+            vres = Resident(vwl, 64 if name.endswith("equal-chunks") else 0)
             vt = time_steps(vres, n_steps, 3, flush=flush)
             vms = median(vt["step_ms"])
             vsplit = median(vt["split_ms"])
@@ -460,7 +465,9 @@ def main():
                               "pct_hbm_peak": round(100 * vwl.kv_bytes() / (vms * 1e-3) / 1e9
                                                     / HBM_PEAK_GBS, 2),
                               "partial_kernel_gbs": round(vres.kernel_bytes() / (vsplit * 1e-3) / 1e9, 1),
-                              "num_chunks": vres.plan.num_chunks, "timing": "median, cache flushed"}
+                              "num_chunks": vres.plan.num_chunks,
+                              "chunk_len_even_odd": [vres.plan.chunk_len, vres.plan.chunk_len_odd],
+                              "timing": "median, cache flushed"}
             print(f"# {name}: {vms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
             del vres
         # the step that feeds decode: a 10,602-token prompt's K/V rows written into pages
