@@ -613,6 +613,373 @@ __device__ __forceinline__ void vm_wait_lt() {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Wait until at most N vector memory operations of this wave are outstanding (any N the
+// counter holds).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "the counter holds 0 .. 63");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// FP8 E4M3 rows, one query row per request.  The stored codes are staged in LDS as they
+// are, with 16-byte global->LDS loads (half the LDS bytes of a widened tile and no
+// registers in flight), and widened to bf16 as each lane reads its MFMA operands; the
+// math is the bf16 kernel's (QK^T on the 16x16x32 MFMA, base-2 online softmax with the
+// lazy rescale, PV on the 16x16x16 MFMA with V^T from byte permutes), so the results are
+// those of a bf16 pool holding the same values.  A tile's 16 rows stream in pieces of 128
+// codes per row (2 KB; one load instruction brings 8 rows, whose 16-byte chunk x lands at
+// position x ^ (row % 8); the two 8-row blocks of a piece sit 1,088 bytes apart), so the
+// score reads (16 rows, 8 bytes each) and the PV reads (one row per 16 lanes) spread over
+// the banks.
+//   * split rows: a tile is D / 128 K pieces, then D / 128 V pieces, each read once; the
+//     slots of two tiles form a ring, and each phase first requests the piece 2 * NPT - 1
+//     ahead of its own into the slot the previous phase finished reading;
+//   * folded rows: a tile is the rotated-K piece and the four V pieces (load order K0, V1,
+//     V2, V3, V0); the score reads K0, V1, V2, V3 and the output V0 .. V3, so slots free a
+//     tile at a time: three sets of five slots, the tile two ahead requested as a tile
+//     starts.
+template <int D, bool FOLDED>
+struct Fp8Ring {
+  static constexpr int PW = 128;                   // codes (bytes) of a row per piece
+  static constexpr int KP = FOLDED ? 1 : D / 128;  // K pieces of a tile
+  static constexpr int VP = D / 128;               // V pieces of a tile
+  static constexpr int NPT = KP + VP;              // pieces per tile
+  static constexpr int RPI = 1024 / PW;            // rows per load instruction
+  static constexpr int IPP = kTile / RPI;          // load instructions per piece
+  static constexpr int BLOCK = 1024 + 64;          // LDS bytes per 8-row block (padded)
+  static constexpr int SLOT = IPP * BLOCK;
+  static constexpr int SETS = FOLDED ? 3 : 2;      // tiles of slots
+  static constexpr int SLOTS = SETS * NPT;
+  static constexpr int REGION = SLOTS * SLOT;      // one wave's LDS
+  static constexpr int AHEAD = SLOTS - 1;          // split rows: pieces in flight behind the one in use
+  static_assert(AHEAD * IPP <= 63, "outstanding loads fit the counter");
+};
+
+// LDS offset of staged row kr inside a slot.
+template <class R>
+__device__ __forceinline__ int ring_row(int kr) {
+  return (kr / R::RPI) * R::BLOCK + (kr % R::RPI) * R::PW;
+}
+
+template <int D, int G, bool FOLDED>
+__global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
+  using S = Shape<D, FOLDED>;
+  using R = Fp8Ring<D, FOLDED>;
+  using O = Ops<false>;
+  using E = Elem<ATTN_KV_FP8_E4M3>;
+  constexpr int KSTEPS = S::KSTEPS;
+  static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
+  static_assert(!FOLDED || D == 512, "folded rows: head dim 512");
+  static_assert(R::PW == 8 * 16 && R::RPI == 8, "eight 16-byte chunks per row piece");
+  static_assert(sizeof(QuarterState<D, G>) <= R::REGION, "parked state must fit the region");
+  __shared__ __attribute__((aligned(16))) char region[kWavesPerBlock][R::REGION];
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;   // MFMA row/column index inside a 16-block
+  const int qg = lane >> 4;  // lane group: selects k sub-range / output rows
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int chunk = blockIdx.x;  // one chunk per workgroup, one quarter per wave
+  const int g = blockIdx.y;
+  const int r = blockIdx.z;
+  char* lds = region[wave];
+
+  const int64_t cap = int64_t(a.max_pages) * a.page_size;
+  const int quarter = ((chunk & 1) ? a.chunk_len_odd : a.chunk_len) / kWavesPerBlock;
+  PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
+  const int c0_nw = int(chunk_cover(a, chunk)) + wave * quarter;
+  const bool early = a.window == 0 && c0_nw < cap;
+  pw.start(early ? c0_nw : 0);
+
+  const int L = a.seq_lens[r];
+  const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+  const int start = lo & ~(kTile - 1);
+  bool poison = L < 1 || int64_t(L) > cap ||
+                int64_t(L) - start > chunk_cover(a, a.num_chunks);
+  const int c0 = start + int(chunk_cover(a, chunk)) + wave * quarter;
+  const int c1 = min(c0 + quarter, L);
+  int ntiles = (!poison && c0 < c1) ? (c1 - c0 + kTile - 1) / kTile : 0;
+  const char* head_base = a.pool + int64_t(g) * a.head_stride;
+
+  // Pool address of tile t's first row, or null (and the quarter poisoned and cut there)
+  // if its page id is outside the pool.  Called for t = 0, 1, 2, ... in order.
+  auto tile_base = [&](int t) -> const char* {
+    const int tok0 = c0 + t * kTile;
+    const int32_t pid = pw.page_of(tok0);
+    if (pid < 0) {
+      poison = true;
+      ntiles = t;
+      return nullptr;
+    }
+    return head_base + int64_t(pid) * a.page_stride + int64_t(tok0 % a.page_size) * a.row_stride;
+  };
+  // Byte offset in the stored row of load-order piece j of a tile.
+  auto piece_col = [&](int j) -> int64_t {
+    if constexpr (FOLDED) return j == 0 ? a.k_offset : a.v_offset + R::PW * (j < 4 ? j : 0);
+    return j < R::KP ? a.k_offset + R::PW * j : a.v_offset + R::PW * (j - R::KP);
+  };
+  // Request piece j of the tile at `tb` into `slot`: lane l of instruction i fetches row
+  // 8i + l / 8, chunk (l % 8) ^ (row % 8), landing at 16 l of the instruction's block.
+  auto issue = [&](const char* tb, int j, int slot) {
+    const char* base = tb + piece_col(j);
+    char* dst = lds + R::SLOT * slot;
+#pragma unroll
+    for (int i = 0; i < R::IPP; ++i) {
+      const int row = R::RPI * i + (lane >> 3);
+      const int64_t off = int64_t(row) * a.row_stride + 16 * ((lane & 7) ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + R::BLOCK * i), 16, 0, kStreamLds);
+    }
+  };
+  auto reads_done = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+
+  // The first two tiles stream while the query operand is prepared.
+  const char* tb1 = nullptr;  // base of the next tile whose pieces are still being requested
+  const char* tb2 = nullptr;
+  if (ntiles > 0) {
+    if (!early) pw.start(c0);
+    const char* tb0 = tile_base(0);
+    if (tb0) {
+#pragma unroll
+      for (int j = 0; j < R::NPT; ++j) issue(tb0, j, j);
+      if (ntiles > 1) tb1 = tile_base(1);
+      if (tb1) {
+        // split: tile 1 but its last piece; folded: all of tile 1
+#pragma unroll
+        for (int j = 0; j < (FOLDED ? R::NPT : R::NPT - 1); ++j) issue(tb1, j, R::NPT + j);
+      }
+    }
+  }
+
+  typename O::T8 qop[KSTEPS];
+  make_query_operand<D, G, false>(a.q + int64_t(r) * a.num_q_heads * D, g, c, qg, a.qscale_k,
+                                  a.qscale_v, FOLDED ? S::ROT : D, qop);
+
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  floatx4 acc[D / 128][8];  // slab b, step jj: lane (c, qg) rows 4qg + i <-> dims 128b + 8(4qg+i) + jj
+#pragma unroll
+  for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[b][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 sacc;             // scores of the tile in progress
+  typename O::T4 pop;       // its probabilities (high or low part per column)
+  const int part = c / G;
+
+  // Score steps 4p .. 4p + 3 (dims 128p .. 128p + 127) from the piece in `slot`: lane
+  // (c, qg), step u reads row c, codes 32u + 8qg .. + 8.
+  auto qk_piece = [&](const char* slot, auto pc) {
+    constexpr int P0 = 4 * decltype(pc)::value;
+    const char* rowp = slot + ring_row<R>(c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = 2 * u + (qg >> 1);
+      const u32x2 raw = *reinterpret_cast<const u32x2*>(rowp + 16 * (x ^ (c & 7)) + 8 * (qg & 1));
+      sacc = O::mma32(__builtin_bit_cast(typename O::T8, E::widen(raw)), qop[P0 + u], sacc);
+    }
+  };
+  // Online softmax over keys tok0 + 4qg + i (as the bf16 kernel's tile math).
+  auto softmax = [&](int tok0) {
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float full = sacc[i] + partner<G>(sacc[i]);
+      const int t = tok0 + 4 * qg + i;
+      sc[i] = (t >= lo && t < L) ? full : -INFINITY;
+      mx = fmaxf(mx, sc[i]);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_expect(__any(grow), 0)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 from -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[b][jj] *= alpha;
+      m_run = m_new;
+    }
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_run != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_run);
+    }
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h = (__bf16)p[i];
+      const __bf16 l = (__bf16)(p[i] - (float)h);
+      pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
+    }
+  };
+  // PV for slab b (dims 128b ..) from the V piece in `slot`: lane (c, qg) reads rows 4qg + e,
+  // codes 8c .. + 8; rows of keys outside [lo, L) are zeroed after widening.
+  auto pv_piece = [&](const char* slot, auto bc, int tok0) {
+    constexpr int B = decltype(bc)::value;
+    const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
+    u32x2 raw[4];  // all four reads issued before any is used
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kr = 4 * qg + e;
+      raw[e] = *reinterpret_cast<const u32x2*>(slot + ring_row<R>(kr) + 16 * ((c >> 1) ^ (kr & 7)) +
+                                               8 * (c & 1));
+    }
+    u32x4 w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = E::widen(raw[e]);
+    if (__builtin_expect(edge, 0)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = tok0 + 4 * qg + e;
+        const unsigned keep = (key >= lo && key < L) ? ~0u : 0u;
+        w[e] &= u32x4{keep, keep, keep, keep};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x2 even = {perm(w[1][u], w[0][u], 0x05040100u), perm(w[3][u], w[2][u], 0x05040100u)};
+      const u32x2 odd = {perm(w[1][u], w[0][u], 0x07060302u), perm(w[3][u], w[2][u], 0x07060302u)};
+      acc[B][2 * u] = O::mma16(__builtin_bit_cast(typename O::T4, even), pop, acc[B][2 * u]);
+      acc[B][2 * u + 1] = O::mma16(__builtin_bit_cast(typename O::T4, odd), pop, acc[B][2 * u + 1]);
+    }
+  };
+
+  if constexpr (!FOLDED) {
+    // Phase j of tile t reads the piece in slot (t % 2) * NPT + j.  It first requests the
+    // piece AHEAD pieces later (tile t + 1's last piece at j = 0, tile t + 2's piece j - 1
+    // after) into the slot phase j - 1 has finished reading, then waits for its own piece:
+    // with every later piece requested, AHEAD pieces' loads may stay in flight.
+    for (int t = 0; t < ntiles; ++t) {
+      const int tok0 = c0 + t * kTile;
+      const int set = t & 1;
+      sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+      static_for<0, R::NPT>([&](auto jc) {
+        constexpr int J = decltype(jc)::value;
+        reads_done();
+        if constexpr (J == 0) {
+          if (t + 1 < ntiles) issue(tb1, R::NPT - 1, (set ^ 1) * R::NPT + R::NPT - 1);
+        } else {
+          if constexpr (J == 1) {
+            if (t + 2 < ntiles) tb2 = tile_base(t + 2);
+          }
+          if (t + 2 < ntiles) issue(tb2, J - 1, set * R::NPT + J - 1);
+        }
+        // Pieces requested after this one: AHEAD while tiles t + 1 and t + 2 exist, fewer
+        // at the end.
+        if constexpr (J == 0) {
+          if (t + 1 < ntiles)
+            vm_wait<R::AHEAD * R::IPP>();
+          else
+            vm_wait<(R::NPT - 1) * R::IPP>();
+        } else {
+          if (t + 2 < ntiles)
+            vm_wait<R::AHEAD * R::IPP>();
+          else if (t + 1 < ntiles)
+            vm_wait<(2 * R::NPT - 1 - J) * R::IPP>();
+          else
+            vm_wait<(R::NPT - 1 - J) * R::IPP>();
+        }
+        const char* slot = lds + R::SLOT * (set * R::NPT + J);
+        if constexpr (J < R::KP) {
+          qk_piece(slot, Int<J>{});
+          if constexpr (J == R::KP - 1) softmax(tok0);
+        } else {
+          pv_piece(slot, Int<J - R::KP>{}, tok0);
+        }
+      });
+      tb1 = tb2;
+    }
+  } else {
+    // Tile t uses set t % 3 (slots: K0, V1, V2, V3, V0 in load order); as it starts, every
+    // read of tile t - 1 is done, and tile t + 2 is requested into that tile's set.
+    int set = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int tok0 = c0 + t * kTile;
+      reads_done();
+      if (t + 2 < ntiles) {
+        const char* tb = tile_base(t + 2);
+        const int nset = set == 0 ? 2 : set - 1;
+        if (tb) {
+#pragma unroll
+          for (int j = 0; j < R::NPT; ++j) issue(tb, j, nset * R::NPT + j);
+        }
+      }
+      // Tiles requested after this one: two, one (the last but one) or none.
+      const int later = min(ntiles - 1 - t, 2);
+      const char* sb = lds + R::SLOT * (set * R::NPT);
+      sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+      static_for<0, 4>([&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        if (later == 2)
+          vm_wait<(2 * R::NPT + 4 - K) * R::IPP>();
+        else if (later == 1)
+          vm_wait<(R::NPT + 4 - K) * R::IPP>();
+        else
+          vm_wait<(4 - K) * R::IPP>();
+        qk_piece(sb + R::SLOT * K, Int<K>{});
+      });
+      softmax(tok0);
+      if (later == 2)
+        vm_wait<2 * R::NPT * R::IPP>();
+      else if (later == 1)
+        vm_wait<R::NPT * R::IPP>();
+      else
+        vm_wait<0>();
+      pv_piece(sb + R::SLOT * 4, Int<0>{}, tok0);
+      pv_piece(sb + R::SLOT * 1, Int<1>{}, tok0);
+      pv_piece(sb + R::SLOT * 2, Int<2>{}, tok0);
+      pv_piece(sb + R::SLOT * 3, Int<3>{}, tok0);
+      set = set == 2 ? 0 : set + 1;
+    }
+  }
+  // Every load has landed and been read before the region is reused for the quarter state.
+  vm_wait<0>();
+  reads_done();
+
+  // Quarter state: sum l over the lane groups, add the low columns onto the high ones.
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+#pragma unroll
+  for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][jj][i] += partner<G>(acc[b][jj][i]);
+
+  using Parked = QuarterState<D, G>;
+  Parked* mine = reinterpret_cast<Parked*>(lds);
+  const float qnan = __builtin_nanf("");
+  if (c < G) {
+    if (qg == 0) {
+      mine->m[c] = poison ? qnan : m_run;  // log2 units, -inf when empty
+      mine->l[c] = l_run;
+    }
+#pragma unroll
+    for (int b = 0; b < D / 128; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 128 * b + 32 * qg + 8 * i;  // dims d .. d + 7
+        mine->o[c][d / 4] = floatx4{acc[b][0][i], acc[b][1][i], acc[b][2][i], acc[b][3][i]};
+        mine->o[c][d / 4 + 1] = floatx4{acc[b][4][i], acc[b][5][i], acc[b][6][i], acc[b][7][i]};
+      }
+  }
+  __syncthreads();
+  const Parked* parked[kWavesPerBlock];
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) parked[w] = reinterpret_cast<const Parked*>(region[w]);
+  write_chunk_state<D, G>(a, parked, r, g, chunk);
+}
+
 template <int D>
 struct F32Shape {
   static constexpr int HALF_BYTES = 4 * D;        // the K or the V half of a row
@@ -1513,6 +1880,8 @@ void launch_split(const SplitArgs& args, dim3 grid, hipStream_t s) {
   if (args.num_rows > 1)
     hipLaunchKernelGGL((rows_partial_kernel<D, G, FOLDED, KV>), grid, dim3(64 * kWavesPerBlock), 0,
                        s, args);
+  else if constexpr (KV == ATTN_KV_FP8_E4M3)
+    hipLaunchKernelGGL((fp8_ring_kernel<D, G, FOLDED>), grid, dim3(64 * kWavesPerBlock), 0, s, args);
   else
     hipLaunchKernelGGL((split_partial_kernel<D, G, FOLDED, KV>), grid, dim3(64 * kWavesPerBlock), 0,
                        s, args);
