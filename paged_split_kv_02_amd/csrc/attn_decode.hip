@@ -635,33 +635,41 @@ __device__ __forceinline__ void static_for(F&& f) {
 // registers in flight), and widened to bf16 as each lane reads its MFMA operands; the
 // math is the bf16 kernel's (QK^T on the 16x16x32 MFMA, base-2 online softmax with the
 // lazy rescale, PV on the 16x16x16 MFMA with V^T from byte permutes), so the results are
-// those of a bf16 pool holding the same values.  A tile's 16 rows stream in pieces of 128
-// codes per row (2 KB; one load instruction brings 8 rows, whose 16-byte chunk x lands at
-// position x ^ (row % 8); the two 8-row blocks of a piece sit 1,088 bytes apart), so the
-// score reads (16 rows, 8 bytes each) and the PV reads (one row per 16 lanes) spread over
-// the banks.
-//   * split rows: a tile is D / 128 K pieces, then D / 128 V pieces, each read once; the
-//     slots of two tiles form a ring, and each phase first requests the piece 2 * NPT - 1
-//     ahead of its own into the slot the previous phase finished reading;
-//   * folded rows: a tile is the rotated-K piece and the four V pieces (load order K0, V1,
-//     V2, V3, V0); the score reads K0, V1, V2, V3 and the output V0 .. V3, so slots free a
-//     tile at a time: three sets of five slots, the tile two ahead requested as a tile
-//     starts.
+// those of a bf16 pool holding the same values.  A tile's 16 rows stream in pieces: a
+// piece is the same span of codes (PW per row) of all 16 rows, one load instruction
+// brings 1024 / PW rows of it, and within a row 16-byte chunk x lands at position
+// x ^ (row % (PW / 16)), so the score reads (16 rows, 8 bytes each) and the PV reads (one
+// row per 16 lanes) spread over the banks.  The score of tile s is interleaved with the
+// output (PV) of tile s - 1, piece by piece (see the step loop), so each wave has two
+// independent MFMA streams and its LDS reads of one overlap the other's products.
+//   * split rows: pieces of 256 codes (whole 256-byte segments per row, as the bf16
+//     kernel's loads), K pieces then V pieces, slots of two tiles;
+//   * folded rows: pieces of 128 codes: the rotated-K piece and the four V pieces (load
+//     order K0, V1, V2, V3, V0); the score reads K0, V1, V2, V3 and the output V0 .. V3,
+//     so slots free a tile at a time: three sets of five slots.
 template <int D, bool FOLDED>
 struct Fp8Ring {
-  static constexpr int PW = 128;                   // codes (bytes) of a row per piece
-  static constexpr int KP = FOLDED ? 1 : D / 128;  // K pieces of a tile
-  static constexpr int VP = D / 128;               // V pieces of a tile
+  // Codes (bytes) of a row per piece: 256 for split rows (whole 256-byte row segments per
+  // load, as the bf16 kernel's); 128 for folded rows, whose rotated K part is 128 codes.
+  static constexpr int PW = FOLDED ? 128 : 256;
+  static constexpr int CH = PW / 16;               // 16-byte chunks of a row piece
+  static constexpr int KP = FOLDED ? 1 : D / PW;   // K pieces of a tile
+  static constexpr int VP = D / PW;                // V pieces of a tile
+  static constexpr int SPP = PW / 128;             // PV slabs (128 dims) per V piece
   static constexpr int NPT = KP + VP;              // pieces per tile
   static constexpr int RPI = 1024 / PW;            // rows per load instruction
   static constexpr int IPP = kTile / RPI;          // load instructions per piece
-  static constexpr int BLOCK = 1024 + 64;          // LDS bytes per 8-row block (padded)
+  // LDS bytes per load block: 128-code pieces pad 64 bytes, so rows 8 apart (same chunk
+  // positions) fall in other banks.
+  static constexpr int BLOCK = PW == 128 ? 1024 + 64 : 1024;
   static constexpr int SLOT = IPP * BLOCK;
   static constexpr int SETS = FOLDED ? 3 : 2;      // tiles of slots
   static constexpr int SLOTS = SETS * NPT;
   static constexpr int REGION = SLOTS * SLOT;      // one wave's LDS
-  static constexpr int AHEAD = SLOTS - 1;          // split rows: pieces in flight behind the one in use
-  static_assert(AHEAD * IPP <= 63, "outstanding loads fit the counter");
+  // Most load instructions a wave has outstanding (less the awaited piece's).
+  static constexpr int MAXOUT = FOLDED ? (2 * NPT - 1) * IPP : (2 * KP + VP - 1) * IPP;
+  static_assert(MAXOUT <= 63, "outstanding loads fit the counter");
+  static_assert(REGION * kWavesPerBlock <= 160 * 1024, "four waves' slots fit the LDS");
 };
 
 // LDS offset of staged row kr inside a slot.
@@ -679,8 +687,9 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
   constexpr int KSTEPS = S::KSTEPS;
   static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
   static_assert(!FOLDED || D == 512, "folded rows: head dim 512");
-  static_assert(R::PW == 8 * 16 && R::RPI == 8, "eight 16-byte chunks per row piece");
+  static_assert(R::PW % 128 == 0 && R::CH * 16 == R::PW, "whole 16-byte chunks per row piece");
   static_assert(sizeof(QuarterState<D, G>) <= R::REGION, "parked state must fit the region");
+  static_assert(R::KP + (FOLDED ? 3 : 0) == R::VP, "score piece i pairs with PV slab i");
   __shared__ __attribute__((aligned(16))) char region[kWavesPerBlock][R::REGION];
 
   const int lane = threadIdx.x & 63;
@@ -733,31 +742,39 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
     char* dst = lds + R::SLOT * slot;
 #pragma unroll
     for (int i = 0; i < R::IPP; ++i) {
-      const int row = R::RPI * i + (lane >> 3);
-      const int64_t off = int64_t(row) * a.row_stride + 16 * ((lane & 7) ^ (row & 7));
+      const int row = R::RPI * i + lane / R::CH;
+      const int64_t off = int64_t(row) * a.row_stride + 16 * ((lane % R::CH) ^ (row % R::CH));
       __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + R::BLOCK * i), 16, 0, kStreamLds);
     }
   };
   auto reads_done = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
 
-  // The first two tiles stream while the query operand is prepared.
-  const char* tb1 = nullptr;  // base of the next tile whose pieces are still being requested
-  const char* tb2 = nullptr;
+  // Tile 0 and the first pieces of tile 1 stream while the query operand is prepared.
+  const char* tb1 = nullptr;  // base of tile 1
   if (ntiles > 0) {
     if (!early) pw.start(c0);
     const char* tb0 = tile_base(0);
     if (tb0) {
+      if constexpr (FOLDED) {
 #pragma unroll
-      for (int j = 0; j < R::NPT; ++j) issue(tb0, j, j);
-      if (ntiles > 1) tb1 = tile_base(1);
-      if (tb1) {
-        // split: tile 1 but its last piece; folded: all of tile 1
+        for (int j = 0; j < R::NPT; ++j) issue(tb0, j, j);
+        if (ntiles > 1) tb1 = tile_base(1);
+        if (tb1) {
 #pragma unroll
-        for (int j = 0; j < (FOLDED ? R::NPT : R::NPT - 1); ++j) issue(tb1, j, R::NPT + j);
+          for (int j = 0; j < R::NPT; ++j) issue(tb1, j, R::NPT + j);
+        }
+      } else {
+        // tile 0, then tile 1's K pieces (its V pieces follow during step 0)
+#pragma unroll
+        for (int j = 0; j < R::NPT; ++j) issue(tb0, j, j);
+        if (ntiles > 1) tb1 = tile_base(1);
+        if (tb1) {
+#pragma unroll
+          for (int j = 0; j < R::KP; ++j) issue(tb1, j, R::NPT + j);
+        }
       }
     }
   }
-
   typename O::T8 qop[KSTEPS];
   make_query_operand<D, G, false>(a.q + int64_t(r) * a.num_q_heads * D, g, c, qg, a.qscale_k,
                                   a.qscale_v, FOLDED ? S::ROT : D, qop);
@@ -773,15 +790,16 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
   typename O::T4 pop;       // its probabilities (high or low part per column)
   const int part = c / G;
 
-  // Score steps 4p .. 4p + 3 (dims 128p .. 128p + 127) from the piece in `slot`: lane
-  // (c, qg), step u reads row c, codes 32u + 8qg .. + 8.
+  // Score steps of piece p (dims PW p .. PW (p + 1)) from the piece in `slot`: lane (c, qg),
+  // step u of the piece reads row c, codes 32u + 8qg .. + 8.
   auto qk_piece = [&](const char* slot, auto pc) {
-    constexpr int P0 = 4 * decltype(pc)::value;
+    constexpr int SPIECE = R::PW / 32;  // score steps per piece
+    constexpr int P0 = SPIECE * decltype(pc)::value;
     const char* rowp = slot + ring_row<R>(c);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < SPIECE; ++u) {
       const int x = 2 * u + (qg >> 1);
-      const u32x2 raw = *reinterpret_cast<const u32x2*>(rowp + 16 * (x ^ (c & 7)) + 8 * (qg & 1));
+      const u32x2 raw = *reinterpret_cast<const u32x2*>(rowp + 16 * (x ^ (c % R::CH)) + 8 * (qg & 1));
       sacc = O::mma32(__builtin_bit_cast(typename O::T8, E::widen(raw)), qop[P0 + u], sacc);
     }
   };
@@ -822,17 +840,18 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
       pop[i] = part == 0 ? h : (part == 1 ? l : (__bf16)0.0f);
     }
   };
-  // PV for slab b (dims 128b ..) from the V piece in `slot`: lane (c, qg) reads rows 4qg + e,
-  // codes 8c .. + 8; rows of keys outside [lo, L) are zeroed after widening.
-  auto pv_piece = [&](const char* slot, auto bc, int tok0) {
+  // PV for slab b (dims 128b ..), part bb of the V piece in `slot`: lane (c, qg) reads rows
+  // 4qg + e, codes 128bb + 8c .. + 8; rows of keys outside [lo, L) are zeroed after widening.
+  auto pv_slab = [&](const char* slot, auto bc, auto bbc, int tok0) {
     constexpr int B = decltype(bc)::value;
+    constexpr int BB = decltype(bbc)::value;
     const bool edge = tok0 < lo || tok0 + kTile > L;  // uniform
     u32x2 raw[4];  // all four reads issued before any is used
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kr = 4 * qg + e;
-      raw[e] = *reinterpret_cast<const u32x2*>(slot + ring_row<R>(kr) + 16 * ((c >> 1) ^ (kr & 7)) +
-                                               8 * (c & 1));
+      raw[e] = *reinterpret_cast<const u32x2*>(slot + ring_row<R>(kr) +
+                                               16 * ((8 * BB + (c >> 1)) ^ (kr % R::CH)) + 8 * (c & 1));
     }
     u32x4 w[4];
 #pragma unroll
@@ -853,93 +872,111 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
       acc[B][2 * u + 1] = O::mma16(__builtin_bit_cast(typename O::T4, odd), pop, acc[B][2 * u + 1]);
     }
   };
+  // PV for V piece v (slabs SPP v .. SPP v + SPP - 1) from `slot`.
+  auto pv_piece = [&](const char* slot, auto vc, int tok0) {
+    constexpr int V = decltype(vc)::value;
+    static_for<0, R::SPP>([&](auto bbc) {
+      constexpr int BB = decltype(bbc)::value;
+      pv_slab(slot, Int<R::SPP * V + BB>{}, bbc, tok0);
+    });
+  };
 
+  // Step s interleaves the score of tile s with the output of tile s - 1: score piece i,
+  // then the PV of tile s - 1's V piece i (with the probabilities step s - 1 produced); then
+  // tile s's softmax (which may rescale the accumulators, after the PV of tile s - 1).  A
+  // last step does the PV of the last tile.  Every accumulator sees its terms in the same
+  // order as tile after tile.
   if constexpr (!FOLDED) {
-    // Phase j of tile t reads the piece in slot (t % 2) * NPT + j.  It first requests the
-    // piece AHEAD pieces later (tile t + 1's last piece at j = 0, tile t + 2's piece j - 1
-    // after) into the slot phase j - 1 has finished reading, then waits for its own piece:
-    // with every later piece requested, AHEAD pieces' loads may stay in flight.
-    for (int t = 0; t < ntiles; ++t) {
-      const int tok0 = c0 + t * kTile;
-      const int set = t & 1;
-      sacc = floatx4{0.f, 0.f, 0.f, 0.f};
-      static_for<0, R::NPT>([&](auto jc) {
-        constexpr int J = decltype(jc)::value;
+    // Split rows: the slots of tile t are set t % 2 (K pieces, then V pieces).  Step s
+    // first requests tile s + 1's K pieces (into the slots tile s - 1's K pieces left in
+    // step s - 1), and after the PV of tile s - 1's V piece i, tile s + 1's V piece i (into
+    // its slot).  Before score piece i, the pieces requested after it are tile s's later K
+    // pieces, its V pieces, and tile s + 1's K pieces and first i V pieces: 2 KP + VP - 1
+    // of them while a tile s + 1 exists.  Tile s - 1's V pieces were requested before.
+    if (ntiles > 0) {
+      const char* tbn = tb1;  // base of tile s + 1
+      for (int s = 0; s < ntiles; ++s) {
+        const int tok0 = c0 + s * kTile;
+        const int set = s & 1;
         reads_done();
-        if constexpr (J == 0) {
-          if (t + 1 < ntiles) issue(tb1, R::NPT - 1, (set ^ 1) * R::NPT + R::NPT - 1);
-        } else {
-          if constexpr (J == 1) {
-            if (t + 2 < ntiles) tb2 = tile_base(t + 2);
+        if (s >= 1 && s + 1 < ntiles) {
+          tbn = tile_base(s + 1);  // null (and ntiles cut) for a bad page
+          if (tbn) {
+#pragma unroll
+            for (int j = 0; j < R::KP; ++j) issue(tbn, j, (set ^ 1) * R::NPT + j);
           }
-          if (t + 2 < ntiles) issue(tb2, J - 1, set * R::NPT + J - 1);
         }
-        // Pieces requested after this one: AHEAD while tiles t + 1 and t + 2 exist, fewer
-        // at the end.
-        if constexpr (J == 0) {
-          if (t + 1 < ntiles)
-            vm_wait<R::AHEAD * R::IPP>();
+        const bool more = s + 1 < ntiles;
+        const char* ks = lds + R::SLOT * (set * R::NPT);
+        const char* vs = lds + R::SLOT * ((set ^ 1) * R::NPT + R::KP);  // tiles s - 1, s + 1
+        sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+        static_for<0, R::KP>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          if (more)
+            vm_wait<(2 * R::KP + R::VP - 1) * R::IPP>();
           else
-            vm_wait<(R::NPT - 1) * R::IPP>();
-        } else {
-          if (t + 2 < ntiles)
-            vm_wait<R::AHEAD * R::IPP>();
-          else if (t + 1 < ntiles)
-            vm_wait<(2 * R::NPT - 1 - J) * R::IPP>();
-          else
-            vm_wait<(R::NPT - 1 - J) * R::IPP>();
-        }
-        const char* slot = lds + R::SLOT * (set * R::NPT + J);
-        if constexpr (J < R::KP) {
-          qk_piece(slot, Int<J>{});
-          if constexpr (J == R::KP - 1) softmax(tok0);
-        } else {
-          pv_piece(slot, Int<J - R::KP>{}, tok0);
-        }
+            vm_wait<(R::KP - 1 - I + R::VP) * R::IPP>();
+          qk_piece(ks + R::SLOT * I, Int<I>{});
+          if (s >= 1) pv_piece(vs + R::SLOT * I, Int<I>{}, tok0 - kTile);
+          if (more && tbn) {
+            reads_done();
+            issue(tbn, R::KP + I, (set ^ 1) * R::NPT + R::KP + I);
+          }
+        });
+        softmax(tok0);
+      }
+      // The output of the last tile.
+      vm_wait<0>();
+      const char* vs = lds + R::SLOT * (((ntiles - 1) & 1) * R::NPT + R::KP);
+      const int ptok = c0 + (ntiles - 1) * kTile;
+      static_for<0, R::VP>([&](auto vc) {
+        constexpr int V = decltype(vc)::value;
+        pv_piece(vs + R::SLOT * V, vc, ptok);
       });
-      tb1 = tb2;
     }
   } else {
-    // Tile t uses set t % 3 (slots: K0, V1, V2, V3, V0 in load order); as it starts, every
-    // read of tile t - 1 is done, and tile t + 2 is requested into that tile's set.
-    int set = 0;
-    for (int t = 0; t < ntiles; ++t) {
-      const int tok0 = c0 + t * kTile;
-      reads_done();
-      if (t + 2 < ntiles) {
-        const char* tb = tile_base(t + 2);
-        const int nset = set == 0 ? 2 : set - 1;
-        if (tb) {
+    // Folded rows: tile t's five pieces (K0, V1, V2, V3, V0) are set t % 3, all requested
+    // as step t - 1 starts (tiles 0 and 1 first); the score of tile t reads its first four
+    // pieces, the output V0 .. V3.  Before score piece i of tile s, the loads of the rest of
+    // tile s and all of tile s + 1 (if any) may stay in flight.
+    if (ntiles > 0) {
+      int kset = 0;  // set of tile s
+      int pset = 0;  // set of tile s - 1
+      for (int s = 0; s < ntiles; ++s) {
+        const int tok0 = c0 + s * kTile;
+        reads_done();
+        if (s >= 1 && s + 1 < ntiles) {
+          const char* tbn = tile_base(s + 1);  // null (and ntiles cut) for a bad page
+          if (tbn) {
+            const int nset = kset == 2 ? 0 : kset + 1;
 #pragma unroll
-          for (int j = 0; j < R::NPT; ++j) issue(tb, j, nset * R::NPT + j);
+            for (int j = 0; j < R::NPT; ++j) issue(tbn, j, nset * R::NPT + j);
+          }
         }
+        const bool more = s + 1 < ntiles;
+        const char* ks = lds + R::SLOT * (kset * R::NPT);
+        const char* ps = lds + R::SLOT * (pset * R::NPT);
+        sacc = floatx4{0.f, 0.f, 0.f, 0.f};
+        static_for<0, 4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;  // score piece: K0, V1, V2, V3
+          if (more)
+            vm_wait<(2 * R::NPT - 1 - I) * R::IPP>();
+          else
+            vm_wait<(R::NPT - 1 - I) * R::IPP>();
+          qk_piece(ks + R::SLOT * I, Int<I>{});
+          if (s >= 1) pv_piece(ps + R::SLOT * (I == 0 ? 4 : I), Int<I>{}, tok0 - kTile);
+        });
+        softmax(tok0);
+        pset = kset;
+        kset = kset == 2 ? 0 : kset + 1;
       }
-      // Tiles requested after this one: two, one (the last but one) or none.
-      const int later = min(ntiles - 1 - t, 2);
-      const char* sb = lds + R::SLOT * (set * R::NPT);
-      sacc = floatx4{0.f, 0.f, 0.f, 0.f};
-      static_for<0, 4>([&](auto kc) {
-        constexpr int K = decltype(kc)::value;
-        if (later == 2)
-          vm_wait<(2 * R::NPT + 4 - K) * R::IPP>();
-        else if (later == 1)
-          vm_wait<(R::NPT + 4 - K) * R::IPP>();
-        else
-          vm_wait<(4 - K) * R::IPP>();
-        qk_piece(sb + R::SLOT * K, Int<K>{});
+      vm_wait<0>();
+      const char* ps = lds + R::SLOT * (pset * R::NPT);
+      const int ptok = c0 + (ntiles - 1) * kTile;
+      static_for<0, R::VP>([&](auto vc) {
+        constexpr int V = decltype(vc)::value;
+        pv_piece(ps + R::SLOT * (V == 0 ? 4 : V), vc, ptok);
       });
-      softmax(tok0);
-      if (later == 2)
-        vm_wait<2 * R::NPT * R::IPP>();
-      else if (later == 1)
-        vm_wait<R::NPT * R::IPP>();
-      else
-        vm_wait<0>();
-      pv_piece(sb + R::SLOT * 4, Int<0>{}, tok0);
-      pv_piece(sb + R::SLOT * 1, Int<1>{}, tok0);
-      pv_piece(sb + R::SLOT * 2, Int<2>{}, tok0);
-      pv_piece(sb + R::SLOT * 3, Int<3>{}, tok0);
-      set = set == 2 ? 0 : set + 1;
     }
   }
   // Every load has landed and been read before the region is reused for the quarter state.
