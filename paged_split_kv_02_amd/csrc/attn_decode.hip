@@ -21,8 +21,10 @@
 //     huge padding never reaches the sums;
 //   * pool element types: bf16 and f16 rows are staged as stored and multiplied on
 //     the MFMA of their own type; FP8 E4M3 rows are fetched at half the bytes and
-//     widened to bf16 (exactly) on their way into LDS.  The dequantisation factors
-//     fold into the query (K) and into the written state (V).
+//     widened to bf16 (exactly): for one query row by a kernel of their own that stages
+//     the codes in LDS as stored and widens them as it reads its operands, for several
+//     rows on their way into LDS.  The dequantisation factors fold into the query (K)
+//     and into the written state (V).
 // Merge (one launch): level 1 folds runs of consecutive chunk states into group
 // states held in LDS, out of place; level 2 folds the group states in order and
 // divides (pegainfer PR #1055, "Description": merge in two levels; gem design note,
@@ -114,7 +116,7 @@ __device__ __forceinline__ unsigned perm(unsigned hi, unsigned lo, unsigned sel)
 // (16 bytes of bf16/f16, 8 bytes of FP8) with a streaming load that does not keep the
 // line in the caches, and widens them to 8 MFMA operand elements (16 bytes) before
 // they are written to LDS.  kAhead = key tiles a wave of the single-row kernel keeps
-// in flight, so that about 32 KB per wave are requested ahead whatever the type.
+// in flight (32 KB per wave at head dim 512).
 template <int KV>
 struct Elem;
 
@@ -142,7 +144,6 @@ template <>
 struct Elem<ATTN_KV_FP8_E4M3> {
   static constexpr int kBytes = 1;
   static constexpr bool kF16 = false;
-  static constexpr int kAhead = 2;
   typedef u32x2 Raw;
   static __device__ __forceinline__ Raw load(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
@@ -438,10 +439,9 @@ __global__ __launch_bounds__(256, 1) void split_partial_kernel(SplitArgs a) {
   constexpr int SLABS = S::SLABS;
   constexpr int P = S::P;
   constexpr int EB = E::kBytes;
-  // Tiles staged ahead in registers.  FP8 rows at head dim 512 keep a third in flight (the
-  // extra registers live in the accumulation file; 6 % faster at 163,336 tokens); at head
-  // dim 256 a third would cost the second wave per SIMD.
-  constexpr int kAhead = (KV == ATTN_KV_FP8_E4M3 && D == 512) ? 3 : E::kAhead;
+  // Tiles staged ahead in registers (one query row over FP8 rows: fp8_ring_kernel).
+  constexpr int kAhead = E::kAhead;
+  static_assert(KV != ATTN_KV_FP8_E4M3, "FP8 rows take the ring kernel");
   static_assert(2 * G <= 16, "hi/lo columns must fit one 16-wide MFMA block");
   __shared__ RowTile<COLS> tiles[kWavesPerBlock];
 
