@@ -157,3 +157,43 @@ def test_f32_rows_partials_per_chunk():
                     assert abs(l[row, h, c] * k - st.l) <= 1e-5 * st.l
                     assert np.max(np.abs(o[row, h, c] * k / st.l - st.acc / st.l)) <= 1e-4
     check(got, oracle.decode_attention(wl), "f32 rows partial case")
+
+
+@pytest.mark.parametrize("shape", ["split", "folded", "sliding"])
+def test_fp8_one_row_quarter_lengths(shape):
+    """The one-row FP8 kernel's piece pipeline at quarters of 1, 2, 4, 8 and 16 tiles (and
+    empty ones): explicit chunk counts over ragged lengths, outputs and every chunk state."""
+    if shape == "sliding":
+        wl = synth.make_workload([1100, 333, 17], **synth.SLIDING, seed=90, kv_dtype=synth.FP8,
+                                 pad="nan", max_pages=64)
+        counts = (1, 2, 4, 5)
+    else:
+        wl = synth.make_workload([1000, 333, 17], **synth.GLOBAL, fmt=shape, seed=91,
+                                 kv_dtype=synth.FP8, spare_pages=2, pad="nan")
+        counts = (1, 2, 4, 8, 16)
+    ref = oracle.decode_attention(wl)
+    for n in counts:
+        dev, got = run_case(wl, f"fp8 {shape} one row n={n}", num_chunks=n)
+        check(got, ref, f"fp8 {shape} n={n}")
+        check_partials(dev, wl)
+
+
+@pytest.mark.parametrize("shape", ["split", "folded", "sliding"])
+def test_fp8_one_row_poisoning(shape):
+    """Forced from the host (every kernel exits normally): a table entry outside the pool, or
+    a device length past the plan, turns only that request's output into NaN."""
+    kw = dict(**synth.SLIDING, max_pages=64) if shape == "sliding" else \
+        dict(**synth.GLOBAL, fmt=shape, spare_pages=2)
+    wl = synth.make_workload([600, 600], seed=92, kv_dtype=synth.FP8, **kw)
+    good = wl.table[1][1]
+    wl.table[1][1] = wl.num_pages + 100
+    _, got = run_case(wl, f"fp8 {shape} bad page id")
+    assert np.all(np.isnan(got[1]))
+    wl.table[1][1] = good
+    check(got[:1], oracle.decode_attention(wl)[:1], f"fp8 {shape} healthy request")
+    note(f"[gpu] fp8 {shape} device length past the plan")
+    dev = Device(wl, seq_lens_dev=[600, 5000])
+    got = dev.run()
+    assert dev.guards_intact()
+    assert np.all(np.isnan(got[1]))
+    check(got[:1], oracle.decode_attention(wl)[:1], f"fp8 {shape} request 0")
