@@ -423,6 +423,12 @@ def main():
                 ("global-decode-163336-split-equal-chunks",
                  lambda: synth.global_decode(163336, seed=2), 20),
                 ("global-decode-4streams-9k-split", lambda: synth.global_streams(seed=16), 20),
+                # one GPU's share of the headline step if it were sharded over GPUs: by KV
+                # head (one of the four, its 8 query heads) or by sequence (1/8 of the keys)
+                ("shard-kvhead-163336-split-8q1kv",
+                 lambda: synth.make_workload([163336], num_q_heads=8, num_kv_heads=1, head_dim=512,
+                                             page_size=256, seed=17), 20),
+                ("shard-seq-20417-split", lambda: synth.global_decode(20417, seed=18), 20),
                 ("sliding-hd256-16ragged-w1024", lambda: synth.sliding_batch(seed=4), 20),
                 ("global-decode-163336-split-4rows",
                  lambda: synth.make_workload([163336], **synth.GLOBAL, seed=6, num_rows=4,
