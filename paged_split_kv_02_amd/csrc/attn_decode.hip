@@ -689,7 +689,7 @@ __global__ __launch_bounds__(256, 1) void fp8_ring_kernel(SplitArgs a) {
   static_assert(!FOLDED || D == 512, "folded rows: head dim 512");
   static_assert(R::PW % 128 == 0 && R::CH * 16 == R::PW, "whole 16-byte chunks per row piece");
   static_assert(sizeof(QuarterState<D, G>) <= R::REGION, "parked state must fit the region");
-  static_assert(R::KP + (FOLDED ? 3 : 0) == R::VP, "score piece i pairs with V piece i");
+  static_assert(R::KP + (FOLDED ? 3 : 0) == R::VP, "score piece i pairs with PV slab i");
   __shared__ __attribute__((aligned(16))) char region[kWavesPerBlock][R::REGION];
 
   const int lane = threadIdx.x & 63;
