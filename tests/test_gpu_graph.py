@@ -51,13 +51,17 @@ def _replay_matches_eager(q, run_eager, replay, read, what, seed):
     note(f"  {what}: 9 replays equal the eager runs")
 
 
-@pytest.mark.parametrize("rows", [1, 4])
-def test_decode_step_in_a_graph(rows):
-    wl = synth.make_workload([3000, 1200], **synth.GLOBAL, seed=90 + rows, num_rows=rows)
-    note(f"[gpu] graph capture of a decode step, rows={rows}")
+@pytest.mark.parametrize("rows,dt,fmt", [(1, synth.BF16, "split"), (4, synth.BF16, "split"),
+                                         (1, synth.FP8, "split"), (1, synth.FP8, "folded"),
+                                         (4, synth.FP8, "split"), (1, synth.F32, "split")])
+def test_decode_step_in_a_graph(rows, dt, fmt):
+    wl = synth.make_workload([3000, 1200], **synth.GLOBAL, fmt=fmt, seed=90 + rows,
+                             num_rows=rows, kv_dtype=dt)
+    what = f"decode rows={rows} {dt} {fmt}"
+    note(f"[gpu] graph capture of a {what}")
     dev = Device(wl)
     g = _capture(dev.step)
-    _replay_matches_eager(dev.q, dev.step, g.replay, dev.result, f"decode rows={rows}", 7)
+    _replay_matches_eager(dev.q, dev.step, g.replay, dev.result, what, 7)
 
 
 def test_prefill_in_a_graph():

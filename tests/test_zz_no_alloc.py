@@ -66,14 +66,17 @@ def test_noalloc_equals_split_merge_twice_smaller_second():
 
 
 def test_noalloc_other_shapes():
-    """The sliding batch (head dim 256, window), a folded row, a 3-row causal window and a
-    tree window, one after another on the same array (largest first)."""
+    """The sliding batch (head dim 256, window), a folded row, a 3-row causal window, a tree
+    window and FP8 / f32 pools, one after another on the same array."""
     _pair(synth.make_workload([5000, 333], **synth.GLOBAL, seed=303, num_rows=3), "rows=3")
     wl = synth.make_workload([900, 40], **synth.GLOBAL, seed=304, num_rows=4)
     synth.set_tree(wl, np.array([[-1, 0, 0, 1], [-1, 0, 1, 1]], dtype=np.int32))
     _pair(wl, "tree rows=4")
     _pair(synth.sliding_batch(seed=305), "sliding batch")
     _pair(synth.make_workload([3000], **synth.GLOBAL, fmt="folded", seed=306), "folded 3000")
+    _pair(synth.make_workload([3000, 700], **synth.GLOBAL, seed=307, kv_dtype=synth.FP8),
+          "fp8 split 3000,700")
+    _pair(synth.make_workload([2000], **synth.GLOBAL, seed=308, kv_dtype=synth.F32), "f32 2000")
 
 
 def test_noalloc_refuses_plan_beyond_the_array():
