@@ -249,3 +249,24 @@ def test_device_length_past_plan_poisons():
     assert dev.guards_intact()
     assert np.all(np.isnan(got[1]))
     check(got[:1], oracle.decode_attention(wl)[:1], "request 0")
+
+
+@pytest.mark.parametrize("n,gm", [(0, 0), (65, 0), (100, 0), (100, 25), (256, 37)])
+def test_merge_groups_longer_than_eight(n, gm):
+    """Level-1 merge groups of more than eight chunk states (the merge's looped fold, with
+    a remainder): one KV head with its 8 query heads (automatic chunking gives 128 chunks
+    for two requests), explicit counts and explicit group sizes; outputs and chunk states."""
+    wl = synth.make_workload([20000, 7000], num_q_heads=8, num_kv_heads=1, head_dim=512,
+                             page_size=256, seed=95, pad="nan")
+    dev, got = run_case(wl, f"merge groups n={n} gm={gm}", num_chunks=n, merge_group=gm)
+    assert dev.plan.merge_group > 8
+    check(got, oracle.decode_attention(wl), f"n={n} gm={gm}")
+    check_partials(dev, wl)
+
+
+def test_merge_groups_longer_than_eight_sliding():
+    """The same for head dim 256 (the sliding shape), where most of 100 chunks are empty."""
+    wl = synth.make_workload([1100, 300, 5], **synth.SLIDING, seed=96, pad="nan", max_pages=64)
+    dev, got = run_case(wl, "sliding merge groups n=100", num_chunks=100)
+    assert dev.plan.merge_group > 8
+    check(got, oracle.decode_attention(wl), "sliding n=100")
