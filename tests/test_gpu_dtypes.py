@@ -197,3 +197,15 @@ def test_fp8_one_row_poisoning(shape):
     assert dev.guards_intact()
     assert np.all(np.isnan(got[1]))
     check(got[:1], oracle.decode_attention(wl)[:1], f"fp8 {shape} request 0")
+
+
+@pytest.mark.parametrize("shape", ["split", "folded", "sliding"])
+def test_fp8_one_row_token_major(shape):
+    """Token-major pages (the KV heads of a slot side by side: a row stride of several rows)
+    through the one-row FP8 kernel."""
+    kw = dict(**synth.SLIDING, max_pages=64) if shape == "sliding" else \
+        dict(**synth.GLOBAL, fmt=shape, spare_pages=2)
+    wl = synth.make_workload([1500, 260, 33], seed=93, kv_dtype=synth.FP8, pad="nan",
+                             layout=synth.TOKEN_MAJOR, **kw)
+    _, got = run_case(wl, f"fp8 {shape} token-major")
+    check(got, oracle.decode_attention(wl), f"fp8 {shape} token-major")
