@@ -13,11 +13,13 @@ LIB = os.path.join(HERE, "libattn_decode.so")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
-# Decode kernels: MFMA accumulators are allocated as VGPRs (not AGPRs), so the softmax
-# rescale touches them in place instead of copying them across register files every
-# tile.  The prefill kernel keeps its larger accumulator set in the AGPRs.
+# MFMA accumulators are allocated as VGPRs (not AGPRs): the decode kernels' softmax
+# rescale then touches them in place instead of copying them across register files every
+# tile, and the 32-key tile kernels (prompt rows, windows of several rows) read their
+# scores without copies and stop moving output accumulators between the two files around
+# each tile's score products (the query operands stay parked in the AGPRs).
 UNITS = [("attn_decode.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
-         ("prefill.hip", []),
+         ("prefill.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
          ("stream_read.hip", []),
          ("plan.cpp", [])]
 SOURCES = [os.path.join(CSRC, name) for name, _ in UNITS]

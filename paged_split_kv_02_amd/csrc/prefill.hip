@@ -466,7 +466,8 @@ __global__ __launch_bounds__(256, 1) void rows_tile_kernel(PrefillArgs a) {
         qlo[s][e] = (T)(x - (float)h);
       }
       // Park the query operand in the accumulation registers, leaving the vector registers
-      // to the tile work (the QK products read most steps' operands from there).
+      // to the output accumulators and the tile work (the QK products take their B operands
+      // from there).
       asm volatile("" : "+a"(qhi[s]), "+a"(qlo[s]));
     }
   }
