@@ -76,6 +76,7 @@ struct SplitArgs {
   const int32_t* q_starts;
   float* out;
   int32_t total_rows, max_rows;
+  int32_t row_tiles, items, num_kv_heads;  // prompt rows: work items (row tiles x KV heads x requests)
 };
 
 // Keys covered by the first c chunks (even chunks chunk_len, odd ones chunk_len_odd).
@@ -1111,9 +1112,26 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   const int c = lane & 15;   // MFMA column ((row, head) pair) / K row inside the tile
   const int qg = lane >> 4;  // lane group: k index of the MFMA operands / output rows
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int g = blockIdx.y;
-  const int r = blockIdx.z;
   char* lds = region[wave];
+
+  // Prompt rows: a 1-D launch over the work items.  Workgroups go to the eight XCDs in
+  // turn (slot w on XCD w % 8), so runs of 32 consecutive items, i.e. neighbouring row
+  // tiles of one (request, KV head) whose key ranges nearly coincide, are given to one XCD
+  // and start together, longest rows first: they stream the same keys through that XCD's
+  // L2 at about the same time.  The launch is padded to whole rounds of 256.
+  int g, r, tile = 0;
+  if constexpr (PREFILL) {
+    const int w = blockIdx.x;
+    const int slot = w >> 3;
+    const int item = ((slot >> 5) * 8 + (w & 7)) * 32 + (slot & 31);
+    if (item >= a.items) return;
+    g = (item / a.row_tiles) % a.num_kv_heads;
+    r = item / a.row_tiles / a.num_kv_heads;
+    tile = a.row_tiles - 1 - item % a.row_tiles;
+  } else {
+    g = blockIdx.y;
+    r = blockIdx.z;
+  }
 
   const int L = a.seq_lens[r];
   const int64_t cap = int64_t(a.max_pages) * a.page_size;
@@ -1125,7 +1143,7 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
     const int qs1 = a.q_starts[r + 1];
     rows = qs1 - int(qs0);
     if (qs0 < 0 || rows < 0 || rows > a.max_rows || qs1 > a.total_rows) return;
-    row0 = blockIdx.x * R;
+    row0 = tile * R;
     if (row0 >= rows) return;
   } else {
     // Launch order of several row groups: the groups of a chunk 8 workgroups apart (one XCD).
@@ -1978,7 +1996,10 @@ void launch_f32_prefill(const attn_prefill_plan_t& p, const float* q, const void
   args.out = out;
   args.total_rows = p.total_rows;
   args.max_rows = p.max_rows;
-  const dim3 grid(p.grid_x, d.num_kv_heads, d.batch);
+  args.row_tiles = p.grid_x;
+  args.num_kv_heads = d.num_kv_heads;
+  args.items = p.grid_x * d.num_kv_heads * d.batch;  // bounded by the plan
+  const dim3 grid((args.items + 255) / 256 * 256);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.head_dim == 512 && d.format == ATTN_KV_FOLDED)
     hipLaunchKernelGGL((f32_partial_kernel<512, 8, true, true>), grid, dim3(64 * kWavesPerBlock), 0,
