@@ -152,9 +152,13 @@ int make_plan(const attn_decode_desc* desc, const int32_t* lens, attn_decode_pla
   int64_t n = d.num_chunks;
   if (n == 0) {
     const int64_t units = int64_t(d.batch) * d.num_kv_heads * groups;
-    // One row at head dim 256: the kernel's registers and LDS tiles allow two workgroups
-    // per CU (two waves per SIMD), so the chip takes twice as many chunks in one round.
-    const int64_t per_cu = (rows == 1 && d.head_dim == 256) ? 2 : 1;
+    // One workgroup per CU in one round.  At head dim 256 the kernels' registers and LDS
+    // allow two per CU; filling both slots pays only on the f32 kernel (16 sliding
+    // requests: 89 against 94 us).  The 16-bit and FP8 kernels run faster with one
+    // workgroup per CU and chunks twice as long (16 requests 47.3 against 48.9 us, 4
+    // requests 22.1 against 25.7), their fixed cost per workgroup (query operand, state
+    // write) weighing more than the second slot's overlap.
+    const int64_t per_cu = (rows == 1 && d.head_dim == 256 && f32) ? 2 : 1;
     n = ceil_div(per_cu * kTargetWaves / kWavesPerBlock, units);
     const int64_t most = ceil_div(tiles, split);
     if (n > most) n = most;

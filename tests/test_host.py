@@ -536,19 +536,27 @@ def test_noalloc_step_refuses_before_any_device_call():
     assert N(ctypes.byref(pb), fake, fake, fake, fake, None, fake, None) == S["ATTN_E_SCRATCH"]
 
 
-def test_sliding_plan_fills_two_workgroups_per_cu():
-    """One query row at head dim 256: the kernels fit two workgroups per CU, so the 16-request
-    sliding batch (16 x 16 KV heads) is cut into two chunks per (request, KV head): 512
-    workgroups, two per CU; a shorter request's second chunk is empty."""
+def test_sliding_plan_workgroups_per_cu():
+    """One query row at head dim 256: one workgroup per CU in one round for the 16-bit and
+    FP8 pools (the 16-request sliding batch, 16 x 16 KV heads, in one chunk per (request, KV
+    head): 256 workgroups), two per CU for f32 pools (two chunks: 512 workgroups; a shorter
+    request's second chunk is empty); a 4-request batch takes four chunks, and more over f32."""
     rng = np.random.default_rng(4)
     lens = rng.integers(1, 4097, size=16)
     f = dict(batch=16, num_q_heads=32, num_kv_heads=16, head_dim=256, format=0, rot_cols=0,
              page_size=64, max_pages_per_seq=64, window=1024, num_chunks=0, merge_group=0,
              scale=1 / 16, num_pages=300, page_stride=16 * 64 * 512, head_stride=64 * 512,
              row_stride=512, k_offset=0, v_offset=256)
-    rc, p = plan_status(lens, **f)
+    for kv_dtype in (0, 1, 2):  # bf16, f16, FP8 E4M3
+        rc, p = plan_status(lens, **f, kv_dtype=kv_dtype)
+        assert rc == 0 and p.num_chunks == 1 and p.grid_x == 1
+    rc, p = plan_status(lens, **f, kv_dtype=3)  # f32: strides are in elements, as for bf16
     assert rc == 0 and p.num_chunks == 2 and p.grid_x == 2
     assert p.num_chunks * 16 * 16 == 512
+    rc, p = plan_status(lens[:4], **dict(f, batch=4))
+    assert rc == 0 and p.num_chunks == 4
+    rc, p = plan_status(lens[:4], **dict(f, batch=4), kv_dtype=3)
+    assert rc == 0 and p.num_chunks > 4  # eight asked for, fewer after rounding to whole quarters
 
 
 def test_f32_rows_plan():
