@@ -1199,6 +1199,10 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
   const int end = (!poison && c0 < c1) ? c1 : c0;
   const char* head_base = a.pool + int64_t(g) * a.head_stride;
   PageWalker pw{a.table + int64_t(r) * a.max_pages, a.num_pages, a.page_size, a.max_pages, 0, -1, -1};
+  // Cache policy of the row loads: decode streams each row once (non-temporal); the row
+  // tiles of a prompt read their keys again from L2 (default policy: the 16 sliding f32
+  // prompts 13.1 -> 9.3 ms, the 10,602-row prompt 41.8 -> 41.7 ms).
+  constexpr int kPolicy = PREFILL ? 0 : kStreamLds;
 
   // Query operand: lane (c, qg), group s, step j holds q[row][head][16s + 4qg + j] times
   // scale * log2(e) * k_scale (folded rows: v_scale for the dims from 128 on, which meet V
@@ -1327,7 +1331,7 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
       for (int i = 0; i < R::IPP; ++i) {
         const int row = R::RPI * i + lane / R::CH;
         const int64_t off = int64_t(row) * a.row_stride + 16 * ((lane % R::CH) ^ row);
-        __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + 1024 * i), 16, 0, kStreamLds);
+        __builtin_amdgcn_global_load_lds(base + off, (lds_void*)(dst + 1024 * i), 16, 0, kPolicy);
       }
     };
     // Split rows: piece j (0-15) of the tile: K pieces 0-7, then V pieces 0-7, slot j % 8.
@@ -1456,7 +1460,7 @@ __global__ __launch_bounds__(256, 1) void f32_partial_kernel(SplitArgs a) {
 #pragma unroll
         for (int k = 0; k < S::LOADS; ++k)
           __builtin_amdgcn_global_load_lds(base + int64_t(row) * a.row_stride + 1024 * k,
-                                           (lds_void*)(lds + row * S::PITCH + 1024 * k), 16, 0, kStreamLds);
+                                           (lds_void*)(lds + row * S::PITCH + 1024 * k), 16, 0, kPolicy);
     };
     if (c0 < end) pw.start(c0);
     for (int tok0 = c0; tok0 < end; tok0 += kTile) {
