@@ -45,7 +45,7 @@ def decode_case(seed: int):
     return wl, tree, chunks, what
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(128))
 def test_random_decode(seed):
     wl, tree, chunks, what = decode_case(seed)
     note(f"[gpu] random decode {what}")
@@ -56,7 +56,7 @@ def test_random_decode(seed):
     check(got, oracle.decode_attention(wl), what)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_prefill(seed):
     rng = np.random.default_rng(8000 + seed)
     family = "global" if rng.random() < 0.6 else "sliding"
